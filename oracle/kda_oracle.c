@@ -1,0 +1,256 @@
+/*
+ * KDA oracle: the Kimi Delta Attention recurrence, token by token, in fp64.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library. The GPU library neither links nor
+ * includes anything from here, and this file includes nothing from it.
+ *
+ * What is computed, per sequence b and head h, for tokens t = 0 .. T-1:
+ *
+ *   1. Short causal convolution of width 4 on each raw projection channel
+ *      (q, k and v), followed by SiLU. The three previous raw tokens come
+ *      from a per-sequence ring (oldest first); the ring is session state.
+ *      Source: "KV缓存从11.25GB缩到0.21GB：WARP中Kimi Delta Attention线性注意力
+ *      原理剖析", section "KDA 递推公式先衰减再差分" (short conv, SiLU, 3-token
+ *      ring) and the table under "414MB 的 KDA 状态从哪来" (3 projections).
+ *   2. L2 normalisation of q and k over the head's d_k channels:
+ *      x / sqrt(sum x^2 + eps). Same section ("q、k 在内核内部 L2 归一化").
+ *      v is not normalised.
+ *   3. Decay along the key axis: S'[i][j] = exp(g[i]) * S[i][j]; g is a
+ *      log-space decay, exponentiated here. Same section, step (1).
+ *   4. Delta read: r[j] = sum_i S'[i][j] * k[i].
+ *   5. Rank-1 write: S[i][j] = S'[i][j] + beta * k[i] * (v[j] - r[j]).
+ *      Same section, step (2); also "为什么 Kimi K3 敢把 KV Cache 扔掉？一篇讲透
+ *      GPT-2 到 K3 的架构进化", section 7, the Kimi Linear update
+ *      S_t = (I - beta k k^T) Diag(alpha) S_{t-1} + beta k v^T, which is the
+ *      same algebra.
+ *   6. Readout from the updated state: o[j] = sum_i S[i][j] * q[i].
+ *      Section "KDA 递推公式先衰减再差分", step (3).
+ *   7. Ring <- the last three raw tokens.
+ *
+ * Layouts (all row-major, fp64):
+ *   q, k   [B][T][H][dk]      raw projections (or post-conv values, see flags)
+ *   v      [B][T][H][dv]
+ *   g      [B][T][H][dk]      natural-log decay per key channel
+ *   beta   [B][T][H]
+ *   conv_w [Ctot][4]          Ctot = H*(2*dk+dv); channels ordered q | k | v,
+ *                             head-major inside each projection; tap 3
+ *                             multiplies the current token, tap 0 the token
+ *                             three steps back
+ *   ring   [B][3][Ctot]       raw tokens t-3, t-2, t-1 (oldest first)
+ *   S      [B][H][dk][dv]
+ *   o      [B][T][H][dv]
+ *
+ * flags: 1 = inputs are already convolved and activated (steps 1 and 7 are
+ * skipped, the ring is not touched); 2 = q and k are already normalised
+ * (step 2 is skipped).
+ *
+ * Heads are independent, so (b, h) pairs run in parallel under OpenMP; each
+ * pair is a plain sequential loop over tokens. No blocking, no reordering.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define KDAO_SKIP_CONV 1
+#define KDAO_SKIP_L2 2
+
+/* Number of threads the oracle will use (1 without OpenMP). */
+int kdao_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+static double silu(double y) { return y / (1.0 + exp(-y)); }
+
+/* Step 1 for one channel c of sequence b at token t: the raw value of that
+ * channel j steps back, taken from the inputs when it lies inside this call
+ * and from the ring otherwise. */
+static double raw_at(const double *x, long x_stride_t, int t, int back,
+                     const double *ring_b, long Ctot, long c) {
+  int s = t - back;
+  if (s >= 0) return x[(long)s * x_stride_t];
+  /* s = -1 is ring tap 2, s = -2 is tap 1, s = -3 is tap 0 */
+  return ring_b[(long)(3 + s) * Ctot + c];
+}
+
+static double conv4_silu(const double *x, long x_stride_t, int t,
+                         const double *ring_b, long Ctot, long c,
+                         const double *w /* [4] for channel c */) {
+  double y = w[0] * raw_at(x, x_stride_t, t, 3, ring_b, Ctot, c) +
+             w[1] * raw_at(x, x_stride_t, t, 2, ring_b, Ctot, c) +
+             w[2] * raw_at(x, x_stride_t, t, 1, ring_b, Ctot, c) +
+             w[3] * raw_at(x, x_stride_t, t, 0, ring_b, Ctot, c);
+  return silu(y);
+}
+
+static void l2_normalise(double *x, int n, double eps) {
+  double ss = 0.0;
+  for (int i = 0; i < n; ++i) ss += x[i] * x[i];
+  double inv = 1.0 / sqrt(ss + eps);
+  for (int i = 0; i < n; ++i) x[i] *= inv;
+}
+
+/* Steps 1-2 for one (b, h) at token t: fills qh[dk], kh[dk], vh[dv]. */
+static void prologue_token(int T, int H, int dk, int dv, int b, int h, int t,
+                           const double *q, const double *k, const double *v,
+                           const double *conv_w, const double *ring,
+                           int flags, double eps,
+                           double *qh, double *kh, double *vh) {
+  const long Ctot = (long)H * (2 * dk + dv);
+  const long sq_t = (long)H * dk, sv_t = (long)H * dv; /* token strides */
+  const double *qb = q + ((long)b * T) * sq_t + (long)h * dk;
+  const double *kb = k + ((long)b * T) * sq_t + (long)h * dk;
+  const double *vb = v + ((long)b * T) * sv_t + (long)h * dv;
+  const double *ring_b = ring ? ring + (long)b * 3 * Ctot : NULL;
+  const long cq = (long)h * dk;                  /* channel of q[h][0] */
+  const long ck = (long)H * dk + (long)h * dk;   /* channel of k[h][0] */
+  const long cv = 2L * H * dk + (long)h * dv;    /* channel of v[h][0] */
+
+  if (flags & KDAO_SKIP_CONV) {
+    for (int i = 0; i < dk; ++i) qh[i] = qb[(long)t * sq_t + i];
+    for (int i = 0; i < dk; ++i) kh[i] = kb[(long)t * sq_t + i];
+    for (int j = 0; j < dv; ++j) vh[j] = vb[(long)t * sv_t + j];
+  } else {
+    for (int i = 0; i < dk; ++i)
+      qh[i] = conv4_silu(qb + i, sq_t, t, ring_b, Ctot, cq + i,
+                         conv_w + 4 * (cq + i));
+    for (int i = 0; i < dk; ++i)
+      kh[i] = conv4_silu(kb + i, sq_t, t, ring_b, Ctot, ck + i,
+                         conv_w + 4 * (ck + i));
+    for (int j = 0; j < dv; ++j)
+      vh[j] = conv4_silu(vb + j, sv_t, t, ring_b, Ctot, cv + j,
+                         conv_w + 4 * (cv + j));
+  }
+  if (!(flags & KDAO_SKIP_L2)) {
+    l2_normalise(qh, dk, eps);
+    l2_normalise(kh, dk, eps);
+  }
+}
+
+/* Step 7 for the channels of head h of sequence b: ring <- last 3 raw tokens
+ * of (old ring, x_0 .. x_{T-1}). */
+static void ring_update(int T, int H, int dk, int dv, int b, int h,
+                        const double *q, const double *k, const double *v,
+                        double *ring) {
+  const long Ctot = (long)H * (2 * dk + dv);
+  double *ring_b = ring + (long)b * 3 * Ctot;
+  const struct { const double *x; long stride_t; long c0; int n; } proj[3] = {
+      {q + ((long)b * T) * H * dk + (long)h * dk, (long)H * dk, (long)h * dk, dk},
+      {k + ((long)b * T) * H * dk + (long)h * dk, (long)H * dk,
+       (long)H * dk + (long)h * dk, dk},
+      {v + ((long)b * T) * H * dv + (long)h * dv, (long)H * dv,
+       2L * H * dk + (long)h * dv, dv},
+  };
+  for (int p = 0; p < 3; ++p) {
+    for (int i = 0; i < proj[p].n; ++i) {
+      long c = proj[p].c0 + i;
+      double nw[3];
+      for (int tap = 0; tap < 3; ++tap) {
+        /* new tap 0 holds x_{T-3}, tap 1 x_{T-2}, tap 2 x_{T-1} */
+        int s = T - 3 + tap;
+        nw[tap] = (s >= 0) ? proj[p].x[(long)s * proj[p].stride_t + i]
+                           : ring_b[(long)(3 + s) * Ctot + c];
+      }
+      for (int tap = 0; tap < 3; ++tap) ring_b[(long)tap * Ctot + c] = nw[tap];
+    }
+  }
+}
+
+/* Full forward over T tokens: steps 1-7. S and ring are updated in place;
+ * o receives every token's readout. Returns 0, or -1 on bad arguments. */
+int kdao_forward(int B, int T, int H, int dk, int dv,
+                 const double *q, const double *k, const double *v,
+                 const double *g, const double *beta, const double *conv_w,
+                 double *ring, double *S, double *o, int flags, double eps,
+                 int nthreads) {
+  if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (!(flags & KDAO_SKIP_CONV) && (!conv_w || !ring)) return -1;
+  if (nthreads <= 0) nthreads = kdao_max_threads();
+  const long BH = (long)B * H;
+  int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (long bh = 0; bh < BH; ++bh) {
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    double *qh = malloc(sizeof(double) * dk);
+    double *kh = malloc(sizeof(double) * dk);
+    double *vh = malloc(sizeof(double) * dv);
+    double *r = malloc(sizeof(double) * dv);
+    if (!qh || !kh || !vh || !r) {
+#pragma omp atomic write
+      bad = 1;
+      free(qh); free(kh); free(vh); free(r);
+      continue;
+    }
+    double *Sbh = S + bh * dk * dv;
+
+    for (int t = 0; t < T; ++t) {
+      prologue_token(T, H, dk, dv, b, h, t, q, k, v, conv_w, ring, flags, eps,
+                     qh, kh, vh);
+      const double *gt = g + (((long)b * T + t) * H + h) * dk;
+      const double bt = beta[((long)b * T + t) * H + h];
+
+      /* step 3: decay each key row i by exp(g[i]) */
+      for (int i = 0; i < dk; ++i) {
+        const double a = exp(gt[i]);
+        for (int j = 0; j < dv; ++j) Sbh[(long)i * dv + j] *= a;
+      }
+      /* step 4: r = S'^T k */
+      for (int j = 0; j < dv; ++j) r[j] = 0.0;
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) r[j] += Sbh[(long)i * dv + j] * kh[i];
+      /* step 5: S = S' + beta k (v - r)^T */
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j)
+          Sbh[(long)i * dv + j] += bt * kh[i] * (vh[j] - r[j]);
+      /* step 6: o = S^T q */
+      double *ot = o + (((long)b * T + t) * H + h) * dv;
+      for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += Sbh[(long)i * dv + j] * qh[i];
+        ot[j] = acc;
+      }
+    }
+    /* step 7 */
+    if (!(flags & KDAO_SKIP_CONV) && T > 0)
+      ring_update(T, H, dk, dv, b, h, q, k, v, ring);
+    free(qh); free(kh); free(vh); free(r);
+  }
+  return bad ? -1 : 0;
+}
+
+/* Steps 1, 2 and 7 only: the activations the recurrence consumes.
+ * qo, ko [B][T][H][dk] and vo [B][T][H][dv] receive q-hat, k-hat (normalised
+ * unless flags has bit 2) and v after conv and SiLU. The ring is advanced. */
+int kdao_prologue(int B, int T, int H, int dk, int dv,
+                  const double *q, const double *k, const double *v,
+                  const double *conv_w, double *ring,
+                  double *qo, double *ko, double *vo, int flags, double eps,
+                  int nthreads) {
+  if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (!(flags & KDAO_SKIP_CONV) && (!conv_w || !ring)) return -1;
+  if (nthreads <= 0) nthreads = kdao_max_threads();
+  const long BH = (long)B * H;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (long bh = 0; bh < BH; ++bh) {
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    for (int t = 0; t < T; ++t) {
+      double *qt = qo + (((long)b * T + t) * H + h) * dk;
+      double *kt = ko + (((long)b * T + t) * H + h) * dk;
+      double *vt = vo + (((long)b * T + t) * H + h) * dv;
+      prologue_token(T, H, dk, dv, b, h, t, q, k, v, conv_w, ring, flags, eps,
+                     qt, kt, vt);
+    }
+    if (!(flags & KDAO_SKIP_CONV) && T > 0)
+      ring_update(T, H, dk, dv, b, h, q, k, v, ring);
+  }
+  return 0;
+}

@@ -1,0 +1,97 @@
+"""Seeded synthetic inputs for the KDA workloads.
+
+This module only draws random numbers. It holds none of the recurrence's
+arithmetic, and both the GPU tests/benchmark and the CPU oracle take their
+inputs from it.
+
+Every workload is drawn on the CPU with one ``torch.Generator`` seeded per
+workload, in a fixed order:
+
+    q, k, v, g_raw, beta_raw, conv_w, S0 (if random), ring (if random)
+
+with q, k, v ~ N(0, 1) of shape [B, T, H, d]; g = logsigmoid(g_mu + N(0, 1))
+per key channel [B, T, H, dk]; beta = sigmoid(N(0, 1)) [B, T, H]; conv
+weights ~ 0.5 * N(0, 1) of shape [H*(2dk+dv), 4]; S0 ~ 0.02 * N(0, 1) of
+shape [B, H, dk, dv]; ring ~ N(0, 1) of shape [B, 3, H*(2dk+dv)]. For
+bf16 workloads q, k, v and the ring are rounded to bf16 (round to nearest
+even); g, beta, the conv weights and S0 stay fp32. "N(m, s)" means mean m,
+standard deviation s.
+
+For decode workloads T is the number of consecutive decode steps; step t
+reads q[:, t], ... .
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+# name -> shape and distribution parameters (sizes follow the K3 KDA layer:
+# 96 heads with a 128x128 state per head).
+WORKLOADS = {
+    # 1 layer, batch 1, 2 heads of 16x16, 64 tokens, fp32 throughout.
+    "tiny": dict(B=1, T=64, H=2, dk=16, dv=16, io="f32", seed=0,
+                 s0_random=False, ring_random=False, g_mu=0.0, chunk=64),
+    # One decode step at the K3 shape, fp32, random state and ring.
+    "k3_decode1": dict(B=1, T=1, H=96, dk=128, dv=128, io="f32", seed=1,
+                       s0_random=True, ring_random=True, g_mu=0.0, chunk=64),
+    # 64 independent sequences, 256 consecutive decode steps, bf16 I/O.
+    "batched_decode": dict(B=64, T=256, H=96, dk=128, dv=128, io="bf16", seed=2,
+                           s0_random=True, ring_random=True, g_mu=0.0, chunk=64),
+    # Chunked prefill of 4096 tokens, chunk 64, slow decay, bf16 I/O.
+    "prefill_4k": dict(B=1, T=4096, H=96, dk=128, dv=128, io="bf16", seed=3,
+                       s0_random=False, ring_random=False, g_mu=2.0, chunk=64),
+}
+
+
+@dataclass
+class Inputs:
+    """One workload's tensors, all on the CPU."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    conv_w: torch.Tensor
+    S0: torch.Tensor
+    ring0: torch.Tensor
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def dims(self):
+        B, T, H, dk = self.q.shape
+        return B, T, H, dk, self.v.shape[-1]
+
+
+def draw(B, T, H, dk, dv, io="f32", seed=0, s0_random=False, ring_random=False,
+         g_mu=0.0, **meta) -> Inputs:
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    ctot = H * (2 * dk + dv)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, dtype=torch.float32)
+
+    q = randn(B, T, H, dk)
+    k = randn(B, T, H, dk)
+    v = randn(B, T, H, dv)
+    g = torch.nn.functional.logsigmoid(randn(B, T, H, dk) + float(g_mu))
+    beta = torch.sigmoid(randn(B, T, H))
+    conv_w = 0.5 * randn(ctot, 4)
+    S0 = 0.02 * randn(B, H, dk, dv) if s0_random else torch.zeros(B, H, dk, dv)
+    ring0 = randn(B, 3, ctot) if ring_random else torch.zeros(B, 3, ctot)
+    if io == "bf16":
+        q, k, v, ring0 = (x.to(torch.bfloat16) for x in (q, k, v, ring0))
+    elif io != "f32":
+        raise ValueError(f"io must be 'f32' or 'bf16', not {io!r}")
+    info = dict(B=B, T=T, H=H, dk=dk, dv=dv, io=io, seed=seed, g_mu=g_mu, **meta)
+    return Inputs(q, k, v, g, beta, conv_w, S0, ring0, info)
+
+
+def make(name: str, **overrides) -> Inputs:
+    """Draw the named workload; keyword overrides replace its parameters
+    (e.g. a smaller T for a quick check)."""
+    params = dict(WORKLOADS[name])
+    params.update(overrides)
+    inp = draw(**params)
+    inp.meta["name"] = name
+    return inp
