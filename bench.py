@@ -1,0 +1,229 @@
+"""KDA benchmark on one MI355X: batched decode throughput (the headline), the
+4096-token chunked prefill alongside it, roofline fractions, and the fp64 CPU
+oracle timed on the host as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+A step is one decode token for each of 64 independent sequences of one KDA
+layer (96 heads, 128x128 fp32 state per head, bf16 q/k/v/o, fp32 g/beta):
+short conv + SiLU + L2, decay, delta, rank-1 write and readout, fused in one
+kernel launch. Inputs for 256 consecutive steps are staged in HBM before the
+timed region; step i uses staged step i % 256. The chunked prefill of 4096
+tokens (batch 1, 96 heads, chunk 64, bf16) is timed separately in the same
+run and reported under "prefill". One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_DENSE_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = ("KDA tokens/s: decode (B×96h×128²) + prefill T=4K; "
+          "HBM GB/s & MFMA % of peak")
+
+
+def decode_bytes(B, H, dk, dv, io_bytes=2):
+    """Algorithmic HBM bytes of one decode launch (all B sequences)."""
+    ctot = H * (2 * dk + dv)
+    state = 2 * B * H * dk * dv * 4                   # read + write of S
+    tok_in = B * H * (2 * dk + dv) * io_bytes          # raw q, k, v
+    gates = B * H * dk * 4 + B * H * 4                 # g, beta
+    ring = 2 * B * 3 * ctot * io_bytes                 # ring read + write
+    out = B * H * dv * io_bytes                        # o
+    weights = ctot * 4 * 4                             # conv weights, once
+    return state + tok_in + gates + ring + out + weights
+
+
+def decode_flops(B, H, dk, dv):
+    # decay (dk*dv), two column reductions (2*2*dk*dv), rank-1 write (2*dk*dv)
+    return B * H * 7 * dk * dv
+
+
+def prefill_bytes(B, T, H, dk, dv, io_bytes=2):
+    """Compulsory HBM bytes of a T-token prefill: inputs, outputs, S in/out."""
+    return (B * T * H * ((2 * dk + dv) * io_bytes + dk * 4 + 4 + dv * io_bytes)
+            + 2 * B * H * dk * dv * 4)
+
+
+def prefill_flops(B, T, H, dk, dv, C):
+    """Algorithmic FLOPs of the chunked form per token-head: the three state
+    contractions (W S, Q~ S, K^T U: 6 dk dv), the intra-chunk matrices
+    (A and P, each C dk on average: 2 C dk), the WY products (W, U': C (dk+dv))
+    and P U (C dv), plus the triangular solve (C^2/3 per column pair)."""
+    per = 6 * dk * dv + 2 * C * dk + C * (dk + dv) + C * dv + (C * C) // 3
+    return B * T * H * per
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--prefill-reps", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the KDA state of every (sequence, head) is "
+              "independent, so more GPUs would each run this same kernel on their own "
+              "share; multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_83_amd as kda
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------- decode: 64 sequences x 96 heads, bf16 I/O -------------
+    inp = workloads.make("batched_decode")
+    B, T, H, dk, dv = inp.dims
+    stg = {name: getattr(inp, name).transpose(0, 1).contiguous().to(dev)
+           for name in ("q", "k", "v", "g", "beta")}           # [T, B, ...] per step
+    conv_w = inp.conv_w.to(dev)
+    st = kda.KDAState(B, H, dk, dv, io=torch.bfloat16, device=dev)
+    st.S.copy_(inp.S0.to(dev))
+    st.ring.copy_(inp.ring0.to(dev))
+    o = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        j = i % T
+        st.decode_step(stg["q"][j], stg["k"][j], stg["v"][j], stg["g"][j], stg["beta"][j],
+                       conv_w, o)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    dec_ms = ev0.elapsed_time(ev1)                   # HIP events on the launch stream
+    per_launch_s = dec_ms / 1e3 / args.steps         # one kernel launch per step
+    tok_s = B * args.steps / (dec_ms / 1e3)
+    dbytes = decode_bytes(B, H, dk, dv)
+    achieved = dbytes / per_launch_s / 1e9
+    assert torch.isfinite(st.S).all().item() and torch.isfinite(o.float()).all().item()
+
+    # ---------------- prefill: T=4096, 96 heads, chunk 64, bf16 ------------
+    pin = workloads.make("prefill_4k")
+    pB, pT, pH, pdk, pdv = pin.dims
+    pd = {name: getattr(pin, name).contiguous().to(dev)
+          for name in ("q", "k", "v", "g", "beta")}
+    pw = pin.conv_w.to(dev)
+    pst = kda.KDAState(pB, pH, pdk, pdv, io=torch.bfloat16, device=dev)
+    pst.reset()
+    po = torch.empty(pB, pT, pH, pdv, dtype=torch.bfloat16, device=dev)
+
+    def prefill():
+        pst.prefill(pT, pd["q"], pd["k"], pd["v"], pd["g"], pd["beta"], pw, po, chunk=64)
+
+    for _ in range(2):
+        prefill()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.prefill_reps):
+        prefill()
+    ev1.record()
+    torch.cuda.synchronize()
+    pre_ms = ev0.elapsed_time(ev1) / args.prefill_reps
+    pbytes = prefill_bytes(pB, pT, pH, pdk, pdv)
+    pflops = prefill_flops(pB, pT, pH, pdk, pdv, 64)
+    assert torch.isfinite(pst.S).all().item()
+
+    copy_gbps = None
+    if args.calib_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        ev1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * n * 5 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
+        del src, dst
+
+    # ---------------- CPU baseline: the fp64 oracle on a bounded sample -----
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import kda_oracle
+
+        def run_oracle(nsteps):
+            sl = slice(0, nsteps)
+            t0 = time.perf_counter()
+            kda_oracle.forward(inp.q[:, sl], inp.k[:, sl], inp.v[:, sl], inp.g[:, sl],
+                               inp.beta[:, sl], inp.conv_w, inp.S0, inp.ring0)
+            return time.perf_counter() - t0
+
+        t1 = run_oracle(1)
+        n = int(max(1, min(T, args.cpu_seconds / max(t1, 1e-3))))
+        tn = run_oracle(n)
+        cpu = {"value": B * n / tn, "unit": "tokens/s", "cores": kda_oracle.max_threads(),
+               "kind": "oracle",
+               "sample": f"fp64 sequential oracle, first {n} of the 256 staged decode steps "
+                         f"for all {B} sequences x {H} heads ({tn:.1f} s); includes the "
+                         f"conversion of the inputs to float64"}
+
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes of the K3 KDA layer)",
+        "config": {"workload": "batched KDA decode: 64 sequences x 96 heads x 128x128 fp32 "
+                               "state, bf16 q/k/v/o, one token per sequence per step "
+                               "(inputs of 256 consecutive steps staged in HBM)",
+                   "batch": B, "heads": H, "d_k": dk, "d_v": dv, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "decode_step_kernel<128,128,256,bf16>",
+                     "bytes_per_launch": dbytes, "avg_launch_us": per_launch_s * 1e6},
+        "prefill": {"workload": "chunked prefill T=4096, batch 1, 96 heads, chunk 64, bf16",
+                    "tokens_per_s": pT * pB / (pre_ms / 1e3), "ms": pre_ms,
+                    "hbm_GBps": pbytes / (pre_ms / 1e3) / 1e9,
+                    "hbm_frac": pbytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                    "tflops": pflops / (pre_ms / 1e3) / 1e12,
+                    "mfma_frac": pflops / (pre_ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
+                    "compulsory_bytes": pbytes, "flops": pflops},
+        "decode_flops_per_step": decode_flops(B, H, dk, dv),
+        "wall_s_timed_region": wall,
+        "cpu_baseline": cpu,
+    }
+    if copy_gbps is not None:
+        line["copy_GBps"] = copy_gbps
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,310 @@
+// C ABI of the KDA library: argument validation, state handles, dispatch.
+// Every entry point validates fully before it enqueues anything, returns a
+// kda_status, and never lets a C++ exception escape.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "kda_common.h"
+
+struct kda_state {
+  kda_dims dims;
+  float* S;
+  void* ring;
+  bool own_S;
+  bool own_ring;
+  void* ws;         // prefill workspace owned by the handle (grown on demand)
+  size_t ws_bytes;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status fail(kda_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kda_status hip_fail(hipError_t e, const char* what) {
+  return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_width(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t io_size(kda_dtype io) { return io == KDA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks dims; on success fills the element counts used by the calls.
+kda_status check_dims(const kda_dims* d) {
+  if (!d) return fail(KDA_ERR_INVALID, "dims is NULL");
+  if (d->batch < 1 || d->heads < 1)
+    return fail(KDA_ERR_INVALID, "batch (%d) and heads (%d) must be >= 1", d->batch, d->heads);
+  if (d->batch > 65535 || d->heads > 65535)
+    return fail(KDA_ERR_UNSUPPORTED, "batch and heads are limited to 65535 each");
+  if (d->conv_width != 4)
+    return fail(KDA_ERR_INVALID, "conv_width must be 4 (got %d)", d->conv_width);
+  if (d->io != KDA_F32 && d->io != KDA_BF16)
+    return fail(KDA_ERR_INVALID, "io dtype %d is not KDA_F32 or KDA_BF16", (int)d->io);
+  if (!supported_width(d->d_k) || !supported_width(d->d_v))
+    return fail(KDA_ERR_UNSUPPORTED, "d_k=%d d_v=%d: supported widths are 16, 32, 64, 128",
+                d->d_k, d->d_v);
+  return KDA_OK;
+}
+
+size_t ctot_of(const kda_dims* d) {
+  return (size_t)d->heads * (size_t)(2 * d->d_k + d->d_v);
+}
+
+size_t s_bytes_of(const kda_dims* d) {
+  return (size_t)d->batch * d->heads * d->d_k * d->d_v * sizeof(float);
+}
+
+size_t ring_bytes_of(const kda_dims* d) {
+  return (size_t)d->batch * 3 * ctot_of(d) * io_size(d->io);
+}
+
+kda_status check_flags(uint32_t flags) {
+  if (flags & ~(KDA_F_SKIP_CONV | KDA_F_SKIP_L2))
+    return fail(KDA_ERR_INVALID, "unknown flag bits 0x%x", flags);
+  return KDA_OK;
+}
+
+#define KDA_REQUIRE_PTR(p, name)                                                  \
+  do {                                                                            \
+    if (!(p)) return fail(KDA_ERR_INVALID, "%s is NULL", name);                   \
+    if (!aligned16(p)) return fail(KDA_ERR_INVALID, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+constexpr size_t kDefaultWsCap = (size_t)2 << 30;  // 2 GiB
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_last_error(void) { return g_err; }
+
+const char* kda_version(void) { return "kda-gfx950 0.1"; }
+
+size_t kda_state_bytes(const kda_dims* dims, size_t* ring_bytes) {
+  if (check_dims(dims) != KDA_OK) {
+    if (ring_bytes) *ring_bytes = 0;
+    return 0;
+  }
+  if (ring_bytes) *ring_bytes = ring_bytes_of(dims);
+  return s_bytes_of(dims);
+}
+
+kda_status kda_state_alloc(const kda_dims* dims, void* s_mem, void* ring_mem,
+                           kda_state** out) {
+  g_err[0] = 0;
+  if (!out) return fail(KDA_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  kda_status st = check_dims(dims);
+  if (st != KDA_OK) return st;
+  if (s_mem && !aligned16(s_mem)) return fail(KDA_ERR_INVALID, "s_mem is not 16-byte aligned");
+  if (ring_mem && !aligned16(ring_mem))
+    return fail(KDA_ERR_INVALID, "ring_mem is not 16-byte aligned");
+  kda_state* h = new (std::nothrow) kda_state();
+  if (!h) return fail(KDA_ERR_OOM, "host allocation of the handle failed");
+  h->dims = *dims;
+  h->S = static_cast<float*>(s_mem);
+  h->ring = ring_mem;
+  if (!h->S) {
+    if (hipMalloc(reinterpret_cast<void**>(&h->S), s_bytes_of(dims)) != hipSuccess) {
+      delete h;
+      return fail(KDA_ERR_OOM, "hipMalloc of %zu state bytes failed", s_bytes_of(dims));
+    }
+    h->own_S = true;
+  }
+  if (!h->ring) {
+    if (hipMalloc(&h->ring, ring_bytes_of(dims)) != hipSuccess) {
+      if (h->own_S) (void)hipFree(h->S);
+      delete h;
+      return fail(KDA_ERR_OOM, "hipMalloc of %zu ring bytes failed", ring_bytes_of(dims));
+    }
+    h->own_ring = true;
+  }
+  *out = h;
+  return KDA_OK;
+}
+
+void kda_state_free(kda_state* st) {
+  if (!st) return;
+  if (st->own_S) (void)hipFree(st->S);
+  if (st->own_ring) (void)hipFree(st->ring);
+  if (st->ws) (void)hipFree(st->ws);
+  delete st;
+}
+
+float* kda_state_S(kda_state* st) { return st ? st->S : nullptr; }
+
+void* kda_state_ring(kda_state* st) { return st ? st->ring : nullptr; }
+
+kda_status kda_state_get_dims(const kda_state* st, kda_dims* out) {
+  if (!st || !out) return fail(KDA_ERR_INVALID, "NULL argument");
+  *out = st->dims;
+  return KDA_OK;
+}
+
+kda_status kda_state_reset(kda_state* st, const int32_t* seq_ids, int32_t n,
+                           hipStream_t stream) {
+  g_err[0] = 0;
+  if (!st) return fail(KDA_ERR_INVALID, "state is NULL");
+  const kda_dims* d = &st->dims;
+  if (seq_ids) {
+    if (n < 0) return fail(KDA_ERR_INVALID, "n = %d is negative", n);
+    for (int32_t i = 0; i < n; ++i)
+      if (seq_ids[i] < 0 || seq_ids[i] >= d->batch)
+        return fail(KDA_ERR_INVALID, "seq_ids[%d] = %d is outside [0, %d)", i, seq_ids[i],
+                    d->batch);
+  }
+  const size_t s_seq = s_bytes_of(d) / d->batch;
+  const size_t r_seq = ring_bytes_of(d) / d->batch;
+  hipError_t e;
+  if (!seq_ids) {
+    if ((e = kda::launch_fill_zero(st->S, s_bytes_of(d), stream)) != hipSuccess)
+      return hip_fail(e, "reset of S");
+    if ((e = kda::launch_fill_zero(st->ring, ring_bytes_of(d), stream)) != hipSuccess)
+      return hip_fail(e, "reset of the ring");
+    return KDA_OK;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    uint8_t* s = reinterpret_cast<uint8_t*>(st->S) + (size_t)seq_ids[i] * s_seq;
+    uint8_t* r = reinterpret_cast<uint8_t*>(st->ring) + (size_t)seq_ids[i] * r_seq;
+    if ((e = kda::launch_fill_zero(s, s_seq, stream)) != hipSuccess)
+      return hip_fail(e, "reset of S");
+    if ((e = kda::launch_fill_zero(r, r_seq, stream)) != hipSuccess)
+      return hip_fail(e, "reset of the ring");
+  }
+  return KDA_OK;
+}
+
+kda_status kda_conv_prologue(const kda_dims* dims, int32_t T, const void* q, const void* k,
+                             const void* v, const float* conv_w, void* ring, float* q_out,
+                             float* k_out, float* v_out, uint32_t flags, hipStream_t stream) {
+  g_err[0] = 0;
+  kda_status st = check_dims(dims);
+  if (st != KDA_OK) return st;
+  if ((st = check_flags(flags)) != KDA_OK) return st;
+  if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);
+  if (T == 0) return KDA_OK;
+  if ((long long)dims->batch * T * dims->heads > (1LL << 31) * 3)
+    return fail(KDA_ERR_UNSUPPORTED, "B*T*H too large for one launch");
+  KDA_REQUIRE_PTR(q, "q");
+  KDA_REQUIRE_PTR(k, "k");
+  KDA_REQUIRE_PTR(v, "v");
+  KDA_REQUIRE_PTR(q_out, "q_out");
+  KDA_REQUIRE_PTR(k_out, "k_out");
+  KDA_REQUIRE_PTR(v_out, "v_out");
+  if (!(flags & KDA_F_SKIP_CONV)) {
+    KDA_REQUIRE_PTR(conv_w, "conv_w");
+    KDA_REQUIRE_PTR(ring, "ring");
+  }
+  kda::PrologueArgs a{q, k, v, conv_w, ring, q_out, k_out, v_out,
+                      dims->batch, T, dims->heads, dims->d_k, dims->d_v, flags};
+  hipError_t e = kda::launch_prologue(a, dims->io, stream);
+  if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  if (!(flags & KDA_F_SKIP_CONV)) {
+    e = kda::launch_ring_advance(q, k, v, ring, dims->batch, T, dims->heads, dims->d_k,
+                                 dims->d_v, dims->io, stream);
+    if (e != hipSuccess) return hip_fail(e, "ring advance launch");
+  }
+  return KDA_OK;
+}
+
+kda_status kda_decode_step(kda_state* stt, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const float* conv_w, void* o,
+                           uint32_t flags, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!stt) return fail(KDA_ERR_INVALID, "state is NULL");
+  kda_status st = check_flags(flags);
+  if (st != KDA_OK) return st;
+  const kda_dims* d = &stt->dims;
+  KDA_REQUIRE_PTR(q, "q");
+  KDA_REQUIRE_PTR(k, "k");
+  KDA_REQUIRE_PTR(v, "v");
+  KDA_REQUIRE_PTR(g, "g");
+  KDA_REQUIRE_PTR(beta, "beta");
+  KDA_REQUIRE_PTR(o, "o");
+  if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w");
+  kda::DecodeArgs a{stt->S, stt->ring, q, k, v, g, beta, conv_w, o,
+                    d->batch, d->heads, d->d_k, d->d_v, flags};
+  hipError_t e = kda::launch_decode(a, d->io, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return KDA_OK;
+}
+
+size_t kda_prefill_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chunk) {
+  if (check_dims(dims) != KDA_OK) return 0;
+  if (T < 0 || (chunk != 16 && chunk != 32 && chunk != 64)) return 0;
+  const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
+  return nchunks *
+         kda::prefill_ws_bytes_per_chunk(dims->heads, dims->batch, dims->d_k, dims->d_v, chunk,
+                                         dims->io);
+}
+
+kda_status kda_chunk_prefill(kda_state* stt, int32_t T, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta,
+                             const float* conv_w, void* o, int32_t chunk, void* workspace,
+                             size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!stt) return fail(KDA_ERR_INVALID, "state is NULL");
+  kda_status st = check_flags(flags);
+  if (st != KDA_OK) return st;
+  const kda_dims* d = &stt->dims;
+  if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);
+  if (chunk != 16 && chunk != 32 && chunk != 64)
+    return fail(KDA_ERR_UNSUPPORTED, "chunk = %d: supported chunks are 16, 32, 64", chunk);
+  if (T == 0) return KDA_OK;
+  KDA_REQUIRE_PTR(q, "q");
+  KDA_REQUIRE_PTR(k, "k");
+  KDA_REQUIRE_PTR(v, "v");
+  KDA_REQUIRE_PTR(g, "g");
+  KDA_REQUIRE_PTR(beta, "beta");
+  KDA_REQUIRE_PTR(o, "o");
+  if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w");
+  const size_t per_chunk =
+      kda::prefill_ws_bytes_per_chunk(d->heads, d->batch, d->d_k, d->d_v, chunk, d->io);
+  const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
+  if (workspace) {
+    if (!aligned16(workspace)) return fail(KDA_ERR_INVALID, "workspace is not 16-byte aligned");
+    if (workspace_bytes < per_chunk)
+      return fail(KDA_ERR_INVALID, "workspace of %zu bytes is below the %zu bytes of one chunk",
+                  workspace_bytes, per_chunk);
+  } else {
+    size_t want = nchunks * per_chunk;
+    if (want > kDefaultWsCap) want = (kDefaultWsCap / per_chunk) * per_chunk;
+    if (want < per_chunk) want = per_chunk;
+    if (stt->ws_bytes < want) {
+      // The handle's workspace grows here. hipFree waits for work already
+      // queued that may still read the old buffer.
+      if (stt->ws) (void)hipFree(stt->ws);
+      stt->ws = nullptr;
+      stt->ws_bytes = 0;
+      if (hipMalloc(&stt->ws, want) != hipSuccess)
+        return fail(KDA_ERR_OOM, "hipMalloc of a %zu-byte prefill workspace failed", want);
+      stt->ws_bytes = want;
+    }
+    workspace = stt->ws;
+    workspace_bytes = stt->ws_bytes;
+  }
+  kda::PrefillArgs a{stt->S, stt->ring, q, k, v, g, beta, conv_w, o,
+                     d->batch, T, d->heads, d->d_k, d->d_v, chunk, flags};
+  hipError_t e = kda::launch_prefill(a, d->io, workspace, workspace_bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  if (!(flags & KDA_F_SKIP_CONV)) {
+    e = kda::launch_ring_advance(q, k, v, stt->ring, d->batch, T, d->heads, d->d_k, d->d_v,
+                                 d->io, stream);
+    if (e != hipSuccess) return hip_fail(e, "ring advance launch");
+  }
+  return KDA_OK;
+}
+
+}  // extern "C"

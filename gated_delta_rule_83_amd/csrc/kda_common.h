@@ -1,0 +1,93 @@
+// Shared device helpers and kernel launch declarations for the KDA kernels
+// (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+using bf16 = __bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kL2Eps = 1e-6f;
+
+// Element loads/stores of the token I/O type. __bf16 -> float is exact;
+// float -> __bf16 rounds to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float silu(float y) { return y / (1.0f + __expf(-y)); }
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// ---- launch helpers (defined in the .hip files) ---------------------------
+
+struct DecodeArgs {
+  float* S;              // [B][H][dk][dv]
+  void* ring;            // [B][3][Ctot] io dtype
+  const void* q;         // [B][H][dk]
+  const void* k;         // [B][H][dk]
+  const void* v;         // [B][H][dv]
+  const float* g;        // [B][H][dk]
+  const float* beta;     // [B][H]
+  const float* conv_w;   // [Ctot][4]
+  void* o;               // [B][H][dv]
+  int B, H, dk, dv;
+  uint32_t flags;
+};
+hipError_t launch_decode(const DecodeArgs& a, kda_dtype io, hipStream_t stream);
+
+struct PrologueArgs {
+  const void* q;  // [B][T][H][dk]
+  const void* k;
+  const void* v;  // [B][T][H][dv]
+  const float* conv_w;
+  void* ring;     // [B][3][Ctot]
+  float* q_out;
+  float* k_out;
+  float* v_out;
+  int B, T, H, dk, dv;
+  uint32_t flags;
+};
+hipError_t launch_prologue(const PrologueArgs& a, kda_dtype io, hipStream_t stream);
+
+// Ring advance after a T-token block: ring <- last 3 raw tokens of
+// (ring, x_0..x_{T-1}). Reads x from the raw inputs [B][T][H][d].
+hipError_t launch_ring_advance(const void* q, const void* k, const void* v, void* ring,
+                               int B, int T, int H, int dk, int dv, kda_dtype io,
+                               hipStream_t stream);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+struct PrefillArgs {
+  float* S;            // [B][H][dk][dv]
+  void* ring;          // [B][3][Ctot]
+  const void* q;       // [B][T][H][dk]
+  const void* k;
+  const void* v;       // [B][T][H][dv]
+  const float* g;      // [B][T][H][dk]
+  const float* beta;   // [B][T][H]
+  const float* conv_w; // [Ctot][4]
+  void* o;             // [B][T][H][dv]
+  int B, T, H, dk, dv, chunk;
+  uint32_t flags;
+};
+size_t prefill_ws_bytes_per_chunk(int H, int B, int dk, int dv, int chunk, kda_dtype io);
+hipError_t launch_prefill(const PrefillArgs& a, kda_dtype io, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,186 @@
+/*
+ * kda.h -- C ABI of the KDA (Kimi Delta Attention) library for MI355X (gfx950).
+ *
+ * The library runs the gated delta-rule recurrence of Kimi Delta Attention on
+ * one GPU. Per sequence b and head h it keeps a fixed-size fp32 state S
+ * (d_k x d_v) and, per token t:
+ *
+ *   short conv + SiLU:   x~ = SiLU(w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t)
+ *                        for every channel of q, k and v (width-4, causal,
+ *                        depthwise, no bias; a 3-token ring of raw inputs
+ *                        carries the history between calls)
+ *   L2 normalisation:    q^ = q~ / sqrt(|q~|^2 + 1e-6), same for k (per head,
+ *                        over d_k); v^ = v~
+ *   decay:               S' = Diag(exp(g_t)) S_{t-1}   (g: log decay per key channel)
+ *   delta + rank-1:      S_t = S' + beta_t k^ (v^ - S'^T k^)^T
+ *   readout:             o_t = S_t^T q^
+ *
+ * Sources: "KV缓存从11.25GB缩到0.21GB：WARP中Kimi Delta Attention线性注意力原理剖析",
+ * section "KDA 递推公式先衰减再差分" (the three update steps, in-kernel L2
+ * normalisation, the width-4 short convolution with its 3-token ring kept as
+ * session state) and section "414MB 的 KDA 状态从哪来" (state size independent
+ * of context length); "为什么 Kimi K3 敢把 KV Cache 扔掉？一篇讲透 GPT-2 到 K3 的架构
+ * 进化", section 7 (the Kimi Linear update with Diag(alpha)) and section 5
+ * (the chunkwise-parallel prefill).
+ *
+ * Conventions for every call:
+ *  - Pointers named as device buffers are HIP device pointers, 16-byte
+ *    aligned, densely packed in the layouts given. The caller owns them.
+ *  - Calls are asynchronous on the given stream (NULL = the default stream)
+ *    and never synchronise the host. A kernel fault surfaces at the caller's
+ *    next synchronisation.
+ *  - Arguments are validated before anything is enqueued. On any error the
+ *    call returns a negative kda_status, enqueues nothing and leaves the
+ *    state untouched; kda_last_error() then describes the problem.
+ *  - No C++ exception crosses this boundary.
+ *  - A state handle must not be used from two streams at once.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID = -1,     /* bad argument: NULL pointer, size, alignment, flag */
+  KDA_ERR_UNSUPPORTED = -2, /* valid but not built: e.g. d_k = 96 */
+  KDA_ERR_HIP = -3,         /* a HIP runtime call failed (message has the HIP error) */
+  KDA_ERR_OOM = -4          /* device allocation failed */
+} kda_status;
+
+/* Element type of the token inputs q, k, v, of the output o and of the conv
+ * ring. The state S, g, beta and the conv weights are always fp32. */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef struct {
+  int32_t batch;      /* B: independent sequences, >= 1 */
+  int32_t heads;      /* H, >= 1 */
+  int32_t d_k;        /* key width per head: 16, 32, 64 or 128 */
+  int32_t d_v;        /* value width per head: 16, 32, 64 or 128 */
+  int32_t conv_width; /* must be 4 */
+  kda_dtype io;       /* dtype of q, k, v, o and the ring */
+} kda_dims;
+
+/* Flags for kda_conv_prologue / kda_decode_step / kda_chunk_prefill. */
+#define KDA_F_SKIP_CONV 1u /* q, k, v are already convolved and activated:
+                              no conv, no SiLU, the ring is neither read nor written */
+#define KDA_F_SKIP_L2 2u   /* q, k are already unit-normalised: no L2 step */
+
+/* Opaque per-layer session state: S and the conv ring for B sequences. */
+typedef struct kda_state kda_state;
+
+/* Channel count of the conv ring / weights: Ctot = H * (2*d_k + d_v).
+ * Channel order is q | k | v, each head-major: q channel of (h, i) is
+ * h*d_k + i, k channel is H*d_k + h*d_k + i, v channel is 2*H*d_k + h*d_v + j. */
+
+/* Bytes of the recurrent state: B*H*d_k*d_v*4. If ring_bytes is not NULL it
+ * receives the ring size B*3*Ctot*sizeof(io). Neither depends on the number
+ * of tokens processed (the state has a fixed size whatever the context
+ * length: section "Kimi Delta Attention 把注意力状态压成固定大小").
+ * Returns 0 for invalid or unsupported dims. */
+size_t kda_state_bytes(const kda_dims* dims, size_t* ring_bytes);
+
+/* Creates a state handle for dims.
+ *  s_mem:    device buffer of kda_state_bytes() bytes, layout S[B][H][d_k][d_v]
+ *            fp32, or NULL to let the library allocate it (hipMalloc).
+ *  ring_mem: device buffer of ring_bytes, layout ring[B][3][Ctot] in the io
+ *            dtype (tap 0 = token t-3, tap 2 = token t-1), or NULL to allocate.
+ * Caller-provided buffers are never freed by the library. The contents start
+ * uninitialised: call kda_state_reset before the first token.
+ * Errors: KDA_ERR_INVALID (NULL out, misaligned buffer), KDA_ERR_UNSUPPORTED
+ * (dims), KDA_ERR_OOM. */
+kda_status kda_state_alloc(const kda_dims* dims, void* s_mem, void* ring_mem,
+                           kda_state** out);
+
+/* Zeroes S and the ring of the listed sequences (a sequence start).
+ * seq_ids is a HOST array of n sequence indices in [0, B); seq_ids = NULL
+ * resets all B sequences (n is then ignored). The zeroing is done by a fill
+ * kernel on the stream (no hipMemsetAsync), so it may be graph-captured.
+ * Errors: KDA_ERR_INVALID (NULL state, n < 0, index out of range). */
+kda_status kda_state_reset(kda_state* st, const int32_t* seq_ids, int32_t n,
+                           hipStream_t stream);
+
+/* Frees the handle, and the buffers the library allocated for it. NULL is a no-op. */
+void kda_state_free(kda_state* st);
+
+/* Device views of the state (for checkpointing: copy out to save, copy in
+ * to restore). NULL for a NULL handle. */
+float* kda_state_S(kda_state* st);
+void* kda_state_ring(kda_state* st);
+kda_status kda_state_get_dims(const kda_state* st, kda_dims* out);
+
+/* The activations the recurrence consumes, for T tokens of B sequences.
+ *  q, k:  [B][T][H][d_k] raw projections (io dtype); v: [B][T][H][d_v].
+ *  conv_w: [Ctot][4] fp32, tap 3 multiplies the current token.
+ *  ring:  [B][3][Ctot] io dtype, read as the history before token 0 and
+ *         advanced to the last three raw tokens (in place).
+ *  q_out, k_out: [B][T][H][d_k] fp32; v_out: [B][T][H][d_v] fp32.
+ * Writes q^, k^ (conv, SiLU, L2) and v^ (conv, SiLU). With KDA_F_SKIP_CONV
+ * the inputs are copied through (conv_w and ring may be NULL); with
+ * KDA_F_SKIP_L2 q and k are not normalised. T = 0 is a no-op.
+ * Source: section "KDA 递推公式先衰减再差分" (short conv, SiLU, L2). */
+kda_status kda_conv_prologue(const kda_dims* dims, int32_t T, const void* q,
+                             const void* k, const void* v, const float* conv_w,
+                             void* ring, float* q_out, float* k_out, float* v_out,
+                             uint32_t flags, hipStream_t stream);
+
+/* One decode token for all B sequences of the state, fused in one pass over S:
+ * conv + SiLU + L2 on this token, decay, delta read, rank-1 write, readout.
+ *  q, k: [B][H][d_k] raw projections (io dtype); v: [B][H][d_v].
+ *  g:    [B][H][d_k] fp32 natural-log decay (-inf allowed: clears the rows).
+ *  beta: [B][H] fp32.
+ *  conv_w: [Ctot][4] fp32 (NULL allowed with KDA_F_SKIP_CONV).
+ *  o:    [B][H][d_v] io dtype (written).
+ * S and the ring are updated in place.
+ * Source: section "KDA 递推公式先衰减再差分", steps (1)-(3). */
+kda_status kda_decode_step(kda_state* st, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta,
+                           const float* conv_w, void* o, uint32_t flags,
+                           hipStream_t stream);
+
+/* Device workspace that kda_chunk_prefill needs for `chunk` and T tokens of
+ * this state's dims, or 0 if the arguments are invalid. Passing a smaller
+ * (but non-zero) workspace makes the call process T in several segments. */
+size_t kda_prefill_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chunk);
+
+/* T tokens for all B sequences, chunkwise-parallel, continuing from the
+ * current S and ring and leaving them at token T (same result as T decode
+ * steps up to rounding).
+ *  q, k: [B][T][H][d_k] raw (io dtype); v: [B][T][H][d_v].
+ *  g:    [B][T][H][d_k] fp32; precondition: finite and <= 0, and on every key
+ *        channel the sum of g over any 16 consecutive tokens is >= -80
+ *        (the intra-chunk decay factors must stay inside the fp32 range).
+ *  beta: [B][T][H] fp32.  conv_w: [Ctot][4] fp32.
+ *  o:    [B][T][H][d_v] io dtype (written).
+ *  chunk: 16, 32 or 64 (64 recommended). T need not be a multiple of chunk.
+ *  workspace: device buffer of workspace_bytes, or NULL to use a buffer the
+ *        state handle allocates on first use (and keeps until kda_state_free).
+ * With io = bf16 the contractions run on bf16 MFMA with fp32 accumulation and
+ * an fp32 state; with io = fp32 they run on fp32 MFMA.
+ * Source: "为什么 Kimi K3 敢把 KV Cache 扔掉？…", section 5 (chunks with
+ * attention-like work inside, the state handed from chunk to chunk, the WY
+ * representation) and section 6 (cumulative in-chunk decay). */
+kda_status kda_chunk_prefill(kda_state* st, int32_t T, const void* q,
+                             const void* k, const void* v, const float* g,
+                             const float* beta, const float* conv_w, void* o,
+                             int32_t chunk, void* workspace, size_t workspace_bytes,
+                             uint32_t flags, hipStream_t stream);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Library version string. */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

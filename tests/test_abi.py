@@ -1,0 +1,145 @@
+"""The C ABI on the CPU: the library loads, exports what include/kda.h
+declares, sizes the state independently of context length, and rejects bad
+arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_83_amd as kda
+from gated_delta_rule_83_amd import kda as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # an aligned address that is never dereferenced on these paths
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[A-Za-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = kda.lib()
+    names = header_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(K.EXPORTED) == names
+
+
+def test_state_size_independent_of_context():
+    # 69 layers x 96 heads x 128 x 128 x 4 bytes = 414 MiB ("414MB 的 KDA 状态从哪来")
+    d = kda.make_dims(69, 96, 128, 128, kda.KDA_F32)
+    s, r = kda.kda_state_bytes(d)
+    assert s == 69 * 96 * 128 * 128 * 4 == 434_110_464
+    assert abs(s / 2**20 - 414) < 0.01
+    # ring: 3 projections x 3 taps x 96*128 channels x 4 bytes x 69 layers ~ 30 MiB
+    assert r == 69 * 3 * 96 * (3 * 128) * 4
+    assert 29 < r / 2**20 < 30
+    # the size query takes no token count; bf16 rings are half as large
+    s2, r2 = kda.kda_state_bytes(kda.make_dims(69, 96, 128, 128, kda.KDA_BF16))
+    assert s2 == s and r2 * 2 == r
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((1, 2, 96, 16, 0, 4), kda.KDAError),
+    ((0, 2, 16, 16, 0, 4), kda.KDAError),
+    ((1, 2, 16, 16, 0, 3), kda.KDAError),
+    ((1, 2, 16, 16, 7, 4), kda.KDAError),
+])
+def test_bad_dims_rejected(dims, code):
+    B, H, dk, dv, io, w = dims
+    d = kda.make_dims(B, H, dk, dv, io, conv_width=w)
+    assert kda.kda_state_bytes(d) == (0, 0)
+    with pytest.raises(code):
+        kda.kda_state_alloc(d, FAKE, FAKE)
+
+
+def test_unsupported_width_code():
+    d = kda.make_dims(1, 2, 96, 16, kda.KDA_F32)
+    h = ctypes.c_void_p()
+    st = kda.lib().kda_state_alloc(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                   ctypes.byref(h))
+    assert st == K.KDA_ERR_UNSUPPORTED
+    assert "d_k=96" in kda.last_error()
+
+
+@pytest.fixture
+def fake_state():
+    d = kda.make_dims(2, 3, 16, 32, kda.KDA_F32)
+    h = ctypes.c_void_p()
+    assert kda.lib().kda_state_alloc(ctypes.byref(d), ctypes.c_void_p(FAKE),
+                                     ctypes.c_void_p(2 * FAKE), ctypes.byref(h)) == 0
+    yield h
+    kda.kda_state_free(h)  # caller-owned buffers: nothing is freed on the device
+
+
+def test_views_and_dims(fake_state):
+    assert kda.kda_state_S(fake_state) == FAKE
+    assert kda.kda_state_ring(fake_state) == 2 * FAKE
+    d = kda.kda_state_get_dims(fake_state)
+    assert (d.batch, d.heads, d.d_k, d.d_v, d.conv_width) == (2, 3, 16, 32, 4)
+
+
+def _vp(x):
+    return ctypes.c_void_p(x) if x is not None else None
+
+
+def call_decode(h, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, w=FAKE, o=FAKE, flags=0):
+    return kda.lib().kda_decode_step(h, _vp(q), _vp(k), _vp(v), _vp(g), _vp(beta), _vp(w),
+                                     _vp(o), flags, None)
+
+
+def call_prefill(h, T=8, chunk=64, ws=None, ws_bytes=0, flags=0, q=FAKE, w=FAKE):
+    return kda.lib().kda_chunk_prefill(h, T, _vp(q), _vp(FAKE), _vp(FAKE), _vp(FAKE), _vp(FAKE),
+                                       _vp(w), _vp(FAKE), chunk, _vp(ws), ws_bytes, flags, None)
+
+
+def test_decode_validation(fake_state):
+    assert call_decode(None) == K.KDA_ERR_INVALID
+    assert call_decode(fake_state, q=None) == K.KDA_ERR_INVALID
+    assert "q is NULL" in kda.last_error()
+    assert call_decode(fake_state, beta=FAKE + 4) == K.KDA_ERR_INVALID
+    assert "aligned" in kda.last_error()
+    assert call_decode(fake_state, flags=8) == K.KDA_ERR_INVALID
+    assert call_decode(fake_state, w=None) == K.KDA_ERR_INVALID
+    assert "conv_w" in kda.last_error()
+
+
+def test_prefill_validation(fake_state):
+    assert call_prefill(fake_state, chunk=48) == K.KDA_ERR_UNSUPPORTED
+    assert call_prefill(fake_state, T=-1) == K.KDA_ERR_INVALID
+    assert call_prefill(fake_state, T=0) == K.KDA_OK          # nothing to do
+    assert call_prefill(fake_state, q=None) == K.KDA_ERR_INVALID
+    assert call_prefill(fake_state, ws=FAKE, ws_bytes=16) == K.KDA_ERR_INVALID
+    assert "below" in kda.last_error()
+
+
+def test_reset_validation(fake_state):
+    arr = (ctypes.c_int32 * 2)(0, 5)
+    assert kda.lib().kda_state_reset(fake_state, arr, 2, None) == K.KDA_ERR_INVALID
+    assert "outside" in kda.last_error()
+    assert kda.lib().kda_state_reset(None, None, 0, None) == K.KDA_ERR_INVALID
+    arr = (ctypes.c_int32 * 1)(0)
+    assert kda.lib().kda_state_reset(fake_state, arr, -1, None) == K.KDA_ERR_INVALID
+
+
+def test_prologue_validation():
+    d = kda.make_dims(1, 2, 16, 16, kda.KDA_F32)
+    L = kda.lib()
+    assert L.kda_conv_prologue(ctypes.byref(d), -1, *([_vp(FAKE)] * 8), 0, None) == K.KDA_ERR_INVALID
+    assert L.kda_conv_prologue(ctypes.byref(d), 0, *([None] * 8), 0, None) == K.KDA_OK
+    assert L.kda_conv_prologue(ctypes.byref(d), 4, None, *([_vp(FAKE)] * 7), 0, None) == \
+        K.KDA_ERR_INVALID
+
+
+def test_workspace_size():
+    d = kda.make_dims(1, 96, 128, 128, kda.KDA_BF16)
+    one = kda.kda_prefill_workspace_bytes(d, 64, 64)
+    # per chunk-head: -W, Q~ [64x128], K^T [128x64], P [64x64], U' [64x128] bf16 + 128 fp32
+    assert one == 96 * ((3 * 64 * 128 + 64 * 64 + 64 * 128) * 2 + 128 * 4)
+    assert kda.kda_prefill_workspace_bytes(d, 4096, 64) == 64 * one
+    assert kda.kda_prefill_workspace_bytes(d, 4097, 64) == 65 * one
+    assert kda.kda_prefill_workspace_bytes(d, 64, 48) == 0
