@@ -39,7 +39,8 @@ bool supported_width(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 1
 
 size_t io_size(kda_dtype io) { return io == KDA_BF16 ? 2 : 4; }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
 
 // Checks dims; on success fills the element counts used by the calls.
 kda_status check_dims(const kda_dims* d) {
@@ -76,10 +77,13 @@ kda_status check_flags(uint32_t flags) {
   return KDA_OK;
 }
 
-#define KDA_REQUIRE_PTR(p, name)                                                  \
-  do {                                                                            \
-    if (!(p)) return fail(KDA_ERR_INVALID, "%s is NULL", name);                   \
-    if (!aligned16(p)) return fail(KDA_ERR_INVALID, "%s is not 16-byte aligned", name); \
+// Token tensors, g, beta and o are accessed per element (natural alignment);
+// conv weights, S, the ring and the workspace are accessed 16 bytes at a time.
+#define KDA_REQUIRE_PTR(p, name, align)                                              \
+  do {                                                                               \
+    if (!(p)) return fail(KDA_ERR_INVALID, "%s is NULL", name);                      \
+    if (!aligned((p), (align)))                                                      \
+      return fail(KDA_ERR_INVALID, "%s is not %d-byte aligned", name, (int)(align)); \
   } while (0)
 
 constexpr size_t kDefaultWsCap = (size_t)2 << 30;  // 2 GiB
@@ -197,15 +201,16 @@ kda_status kda_conv_prologue(const kda_dims* dims, int32_t T, const void* q, con
   if (T == 0) return KDA_OK;
   if ((long long)dims->batch * T * dims->heads > (1LL << 31) * 3)
     return fail(KDA_ERR_UNSUPPORTED, "B*T*H too large for one launch");
-  KDA_REQUIRE_PTR(q, "q");
-  KDA_REQUIRE_PTR(k, "k");
-  KDA_REQUIRE_PTR(v, "v");
-  KDA_REQUIRE_PTR(q_out, "q_out");
-  KDA_REQUIRE_PTR(k_out, "k_out");
-  KDA_REQUIRE_PTR(v_out, "v_out");
+  const size_t esz = io_size(dims->io);
+  KDA_REQUIRE_PTR(q, "q", esz);
+  KDA_REQUIRE_PTR(k, "k", esz);
+  KDA_REQUIRE_PTR(v, "v", esz);
+  KDA_REQUIRE_PTR(q_out, "q_out", 4);
+  KDA_REQUIRE_PTR(k_out, "k_out", 4);
+  KDA_REQUIRE_PTR(v_out, "v_out", 4);
   if (!(flags & KDA_F_SKIP_CONV)) {
-    KDA_REQUIRE_PTR(conv_w, "conv_w");
-    KDA_REQUIRE_PTR(ring, "ring");
+    KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
+    KDA_REQUIRE_PTR(ring, "ring", esz);
   }
   kda::PrologueArgs a{q, k, v, conv_w, ring, q_out, k_out, v_out,
                       dims->batch, T, dims->heads, dims->d_k, dims->d_v, flags};
@@ -227,13 +232,14 @@ kda_status kda_decode_step(kda_state* stt, const void* q, const void* k, const v
   kda_status st = check_flags(flags);
   if (st != KDA_OK) return st;
   const kda_dims* d = &stt->dims;
-  KDA_REQUIRE_PTR(q, "q");
-  KDA_REQUIRE_PTR(k, "k");
-  KDA_REQUIRE_PTR(v, "v");
-  KDA_REQUIRE_PTR(g, "g");
-  KDA_REQUIRE_PTR(beta, "beta");
-  KDA_REQUIRE_PTR(o, "o");
-  if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w");
+  const size_t esz = io_size(d->io);
+  KDA_REQUIRE_PTR(q, "q", esz);
+  KDA_REQUIRE_PTR(k, "k", esz);
+  KDA_REQUIRE_PTR(v, "v", esz);
+  KDA_REQUIRE_PTR(g, "g", 4);
+  KDA_REQUIRE_PTR(beta, "beta", 4);
+  KDA_REQUIRE_PTR(o, "o", esz);
+  if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
   kda::DecodeArgs a{stt->S, stt->ring, q, k, v, g, beta, conv_w, o,
                     d->batch, d->heads, d->d_k, d->d_v, flags};
   hipError_t e = kda::launch_decode(a, d->io, stream);
@@ -263,13 +269,14 @@ kda_status kda_chunk_prefill(kda_state* stt, int32_t T, const void* q, const voi
   if (chunk != 16 && chunk != 32 && chunk != 64)
     return fail(KDA_ERR_UNSUPPORTED, "chunk = %d: supported chunks are 16, 32, 64", chunk);
   if (T == 0) return KDA_OK;
-  KDA_REQUIRE_PTR(q, "q");
-  KDA_REQUIRE_PTR(k, "k");
-  KDA_REQUIRE_PTR(v, "v");
-  KDA_REQUIRE_PTR(g, "g");
-  KDA_REQUIRE_PTR(beta, "beta");
-  KDA_REQUIRE_PTR(o, "o");
-  if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w");
+  const size_t esz = io_size(d->io);
+  KDA_REQUIRE_PTR(q, "q", esz);
+  KDA_REQUIRE_PTR(k, "k", esz);
+  KDA_REQUIRE_PTR(v, "v", esz);
+  KDA_REQUIRE_PTR(g, "g", 4);
+  KDA_REQUIRE_PTR(beta, "beta", 4);
+  KDA_REQUIRE_PTR(o, "o", esz);
+  if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
   const size_t per_chunk =
       kda::prefill_ws_bytes_per_chunk(d->heads, d->batch, d->d_k, d->d_v, chunk, d->io);
   const size_t nchunks = ((size_t)T + chunk - 1) / chunk;

@@ -36,6 +36,7 @@ struct MmaBf16 {
   using frag = bf16x8;
   static constexpr int KS = 32, KPL = 8;
   __device__ static frag ld(const T* p) { return *reinterpret_cast<const frag*>(p); }
+  __device__ static void st(T* p, frag f) { *reinterpret_cast<frag*>(p) = f; }
   __device__ static frag mk(const float* v) {
     frag f;
 #pragma unroll
@@ -53,6 +54,7 @@ struct MmaF32 {
   using frag = float;
   static constexpr int KS = 4, KPL = 1;
   __device__ static frag ld(const T* p) { return *p; }
+  __device__ static void st(T* p, frag f) { *p = f; }
   __device__ static frag mk(const float* v) { return v[0]; }
   __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -61,16 +63,25 @@ struct MmaF32 {
 
 constexpr int rup(int x, int m) { return (x + m - 1) / m * m; }
 
-// Workspace block of one (chunk, sequence, head). Offsets in elements of T.
+__device__ __forceinline__ f32x4 mma_f32x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Workspace block of one (chunk, sequence, head); offsets in elements of T.
+// "Fragment-major" arrays hold an MFMA A-operand as it sits in the lanes:
+// element ((rb * nks + ks) * 64 + lane) * KPL + e is row 16*rb + lane%16,
+// column ks*KS + (lane/16)*KPL + e, so one lane loads one contiguous piece.
+// U' is stored in the accumulator layout: element ((rb * DV/16 + cb) * 64 +
+// lane) * 4 + e is row 16*rb + 4*(lane/16) + e, column 16*cb + lane%16.
 template <int C, int DK, int DV, class M>
 struct Ws {
   static constexpr int DKP = rup(DK, M::KS);  // K-dims padded to the MFMA depth
   static constexpr int CP = rup(C, M::KS);
-  static constexpr size_t oW = 0;                          // -W    [C][DKP]
-  static constexpr size_t oQ = oW + (size_t)C * DKP;       // Q~    [C][DKP]
-  static constexpr size_t oK = oQ + (size_t)C * DKP;       // K^^T  [DK][CP]
-  static constexpr size_t oP = oK + (size_t)DK * CP;       // P     [C][CP]
-  static constexpr size_t oU = oP + (size_t)C * CP;        // U'    [C][DV]
+  static constexpr size_t oW = 0;                          // -W    [C x DKP] fragment-major
+  static constexpr size_t oQ = oW + (size_t)C * DKP;       // Q~    [C x DKP] fragment-major
+  static constexpr size_t oK = oQ + (size_t)C * DKP;       // K^^T  [DK x CP] fragment-major
+  static constexpr size_t oP = oK + (size_t)DK * CP;       // P     [C][CP] row-major
+  static constexpr size_t oU = oP + (size_t)C * CP;        // U'    [C x DV] accumulator layout
   static constexpr size_t nT = oU + (size_t)C * DV;
   static constexpr size_t bytes = nT * sizeof(typename M::T) + DK * sizeof(float);  // + e^{Gam_n}
 };
@@ -80,39 +91,54 @@ constexpr size_t ws_block_bytes(int C, int DK, int DV, int KS, size_t esz) {
           (size_t)C * DV) * esz + (size_t)DK * 4;
 }
 
-constexpr int kNT = 256;
-constexpr int kNW = kNT / kWave;
+// ---------------------------------------------------------------------------
+// prep: one workgroup of 512 threads per (chunk, head, sequence).
+constexpr int kPrepNT = 512;
+constexpr int kPrepNW = kPrepNT / kWave;
 
-template <typename IO>
-struct Raw {
-  const IO* x;      // [B][T][H][d]
-  const IO* ring;   // this sequence's ring [3][ctot]
-  long ctot;
-  int T, H, d, b, h;
-  // raw input of channel i (ring channel chan) at global token s
-  __device__ float at(int i, long chan, int s) const {
-    if (s >= 0) return to_f32(x[(((long)b * T + s) * H + h) * d + i]);
-    return to_f32(ring[(long)(3 + s) * ctot + chan]);
-  }
-  __device__ float act(int i, long chan, f32x4 w, int t, bool conv) const {
-    if (!conv) return at(i, chan, t);
-    return silu(w.x * at(i, chan, t - 3) + w.y * at(i, chan, t - 2) +
-                w.z * at(i, chan, t - 1) + w.w * at(i, chan, t));
-  }
+template <int C, int DK, int DV, typename IO, class M>
+struct PrepSmem {
+  using ST = IO;                                   // storage of v^ in LDS
+  static constexpr int LDK = DK + 4, LDC = C + 4;  // fp32 row strides
+  static constexpr int LDV = DV + 16 / (int)sizeof(ST);
+  static constexpr size_t oQ = 0;                                    // q^ (later -W staging)
+  static constexpr size_t oK = oQ + (size_t)C * LDK * 4;             // k^ (later beta e^Gam k^)
+  static constexpr size_t nGX = (size_t)C * (LDK > LDC ? LDK : LDC) * 4;
+  static constexpr size_t oGX = oK + (size_t)C * LDK * 4;            // Gam, later X
+  static constexpr size_t oL = oGX + nGX;                            // beta * strict_lower(A)
+  static constexpr size_t oV = oL + (size_t)C * LDC * 4;             // v^
+  static constexpr size_t oB = oV + (size_t)C * LDV * sizeof(ST);    // beta
+  static constexpr size_t bytes = oB + (size_t)C * 4;
+  static_assert(bytes <= 160 * 1024, "prep LDS exceeds 160 KiB");
+  static_assert((size_t)C * rup(DK, M::KS) * sizeof(typename M::T) <= (size_t)C * LDK * 4,
+                "-W staging does not fit in the q^ region");
 };
 
-// ---------------------------------------------------------------------------
-// prep: one workgroup per (chunk, head, sequence).
 template <int C, int DK, int DV, typename IO, class M>
-__global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillArgs a, int t0, uint8_t* ws) {
+__global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, int t0,
+                                                               uint8_t* ws) {
   using L = Ws<C, DK, DV, M>;
+  using SM = PrepSmem<C, DK, DV, IO, M>;
   using MT = typename M::T;
-  constexpr int LDX = DK + 4, LDL = C + 4;
+  using ST = typename SM::ST;
+  using frag = typename M::frag;
+  constexpr int LDK = SM::LDK, LDC = SM::LDC, LDV = SM::LDV;
   constexpr int DKP = L::DKP, CP = L::CP;
-  __shared__ float sQ[C][LDX], sK[C][LDX], sG[C][LDX], sL[C][LDL], sBeta[C];
+  constexpr int NRB = C / 16;
+  constexpr int KS = M::KS, KPL = M::KPL;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SM::bytes];
+  float (*sQ)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oQ);
+  float (*sK)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oK);
+  float (*sG)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oGX);
+  float (*sX)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oGX);
+  float (*sL)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oL);
+  ST (*sV)[LDV] = reinterpret_cast<ST (*)[LDV]>(smem + SM::oV);
+  float* sB = reinterpret_cast<float*>(smem + SM::oB);
+  MT (*sWst)[DKP] = reinterpret_cast<MT (*)[DKP]>(smem + SM::oQ);
 
   const int cl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l16 = lane % 16, g16 = lane / 16;
   const int H = a.H, T = a.T;
   const int tstart = t0 + cl * C;
   const int n = min(C, T - tstart);
@@ -121,204 +147,314 @@ __global__ __launch_bounds__(kNT) void prefill_prep_kernel(PrefillArgs a, int t0
   const long ctot = (long)H * (2 * DK + DV);
   const bool do_conv = !(a.flags & KDA_F_SKIP_CONV);
   const bool do_l2 = !(a.flags & KDA_F_SKIP_L2);
-  const IO* ring = static_cast<const IO*>(a.ring) + (long)b * 3 * ctot;
-  const Raw<IO> rq{static_cast<const IO*>(a.q), ring, ctot, T, H, DK, b, h};
-  const Raw<IO> rk{static_cast<const IO*>(a.k), ring, ctot, T, H, DK, b, h};
-  const Raw<IO> rv{static_cast<const IO*>(a.v), ring, ctot, T, H, DV, b, h};
 
-  // (1) q^, k^ of every token of the chunk (zero rows past n)
-  {
-    constexpr int U = (DK + kWave - 1) / kWave;
-    f32x4 wq[U], wk[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = lane + u * kWave;
-      wq[u] = wk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (do_conv && i < DK) {
-        wq[u] = *reinterpret_cast<const f32x4*>(a.conv_w + 4 * ((long)h * DK + i));
-        wk[u] = *reinterpret_cast<const f32x4*>(a.conv_w + 4 * ((long)H * DK + (long)h * DK + i));
-      }
+  // ---- 1. every global input of the chunk, loaded up front ---------------
+  // Threads [0, DK) own q channels, [DK, 2DK) k channels, [2DK, 2DK+DV) v
+  // channels: each loads its channel for the C tokens and the three before
+  // (ring or earlier tokens), convolves with a rolling window and writes the
+  // activation to LDS. Threads [2DK+DV, 2DK+DV+DK) own the g channels and
+  // form the in-chunk prefix sums. Loads use clamped, always-valid addresses
+  // and masks instead of branches so that they are all in flight together.
+  if (tid < C) sB[tid] = tid < n ? a.beta[((long)b * T + tstart + tid) * H + h] : 0.f;
+  if (tid < 2 * DK + DV) {
+    int p, c, d;
+    const IO* x;
+    long chan;
+    if (tid < DK) {
+      p = 0; c = tid; d = DK; x = static_cast<const IO*>(a.q); chan = (long)h * DK + c;
+    } else if (tid < 2 * DK) {
+      p = 1; c = tid - DK; d = DK; x = static_cast<const IO*>(a.k);
+      chan = (long)H * DK + (long)h * DK + c;
+    } else {
+      p = 2; c = tid - 2 * DK; d = DV; x = static_cast<const IO*>(a.v);
+      chan = 2L * H * DK + (long)h * DV + c;
     }
-    for (int r = wv; r < C; r += kNW) {
-      float qv[U], kv[U];
-      float ssq = 0.f, ssk = 0.f;
+    const IO* ring = static_cast<const IO*>(a.ring) + (long)b * 3 * ctot + chan;
+    const IO* xc = x + ((long)b * T * H + h) * d + c;   // token 0 of this channel
+    const long ts = (long)H * d;                        // token stride
+    float raw[C + 3];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = lane + u * kWave;
-        qv[u] = kv[u] = 0.f;
-        if (r < n && i < DK) {
-          qv[u] = rq.act(i, (long)h * DK + i, wq[u], tstart + r, do_conv);
-          kv[u] = rk.act(i, (long)H * DK + (long)h * DK + i, wk[u], tstart + r, do_conv);
-        }
-        ssq += qv[u] * qv[u];
-        ssk += kv[u] * kv[u];
-      }
-      float iq = 1.f, ik = 1.f;
-      if (do_l2) {
-        iq = 1.0f / sqrtf(wave_sum(ssq) + kL2Eps);
-        ik = 1.0f / sqrtf(wave_sum(ssk) + kL2Eps);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = lane + u * kWave;
-        if (i < DK) {
-          sQ[r][i] = qv[u] * iq;
-          sK[r][i] = kv[u] * ik;
-        }
-      }
+    for (int i = 0; i < C + 3; ++i) {
+      const int tok = tstart - 3 + i;
+      const int tcl = tok < T ? tok : T - 1;
+      const IO* src = tcl >= 0 ? xc + (long)tcl * ts
+                               : (do_conv ? ring + (long)(3 + tcl) * ctot : xc);
+      const float val = to_f32(*src);
+      raw[i] = ((i >= 3 || do_conv) && tok < T) ? val : 0.f;
     }
-  }
-  // (2) Gam = inclusive prefix sum of g inside the chunk; beta (0 past n)
-  if (tid < DK) {
-    const float* gp = a.g + (((long)b * T + tstart) * H + h) * DK + tid;
-    float acc = 0.f;
-#pragma unroll 8
+    f32x4 w = {0.f, 0.f, 0.f, 1.f};
+    if (do_conv) w = *reinterpret_cast<const f32x4*>(a.conv_w + 4 * chan);
+#pragma unroll
     for (int r = 0; r < C; ++r) {
-      if (r < n) acc += gp[(long)r * H * DK];
-      sG[r][tid] = acc;
+      float y = raw[r + 3];
+      if (do_conv) y = silu(w.x * raw[r] + w.y * raw[r + 1] + w.z * raw[r + 2] + w.w * raw[r + 3]);
+      y = r < n ? y : 0.f;
+      if (p == 0) sQ[r][c] = y;
+      else if (p == 1) sK[r][c] = y;
+      else sV[r][c] = (ST)y;
     }
-  }
-  if (tid >= kNT - C) {
-    const int r = tid - (kNT - C);
-    sBeta[r] = r < n ? a.beta[((long)b * T + tstart + r) * H + h] : 0.f;
+  } else if (tid < 2 * DK + DV + DK) {
+    const int c = tid - (2 * DK + DV);
+    const float* gc = a.g + ((long)b * T * H + h) * DK + c;
+    float gv[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      const int tcl = tstart + r < T ? tstart + r : T - 1;
+      gv[r] = gc[(long)tcl * H * DK];
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      acc += r < n ? gv[r] : 0.f;
+      sG[r][c] = acc;
+    }
   }
   __syncthreads();
 
-  // (3) A (scaled by beta, strictly lower) to LDS, P (lower) to the workspace
+  // ---- 2. L2 normalisation of q~ and k~, 8 threads per token -------------
+  if (do_l2 && tid < 8 * C) {
+    const int r = tid / 8, part = tid % 8;
+    float sq = 0.f, sk = 0.f;
+    for (int c = part; c < DK; c += 8) {
+      sq += sQ[r][c] * sQ[r][c];
+      sk += sK[r][c] * sK[r][c];
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      sq += __shfl_xor(sq, off, kWave);
+      sk += __shfl_xor(sk, off, kWave);
+    }
+    const float iq = 1.0f / sqrtf(sq + kL2Eps), ik = 1.0f / sqrtf(sk + kL2Eps);
+    for (int c = part; c < DK; c += 8) {
+      sQ[r][c] *= iq;
+      sK[r][c] *= ik;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. A (beta-scaled, strictly lower) to LDS and P (lower) to the
+  //         workspace, one 16x16 tile (a, bc <= a) per wave at a time --------
   {
-    constexpr int NRB = C / 16;
-    constexpr int NKS = DKP / M::KS;
-    const int l16 = lane % 16, koff = (lane / 16) * M::KPL;
-    for (int arb = wv; arb < NRB; arb += kNW) {
-      const int m = 16 * arb, r = m + l16;
-      typename M::frag fk[NKS], fq[NKS];
+    constexpr int NKS = DKP / KS;
+    constexpr int NTILE = NRB * (NRB + 1) / 2;
+    for (int tile = wv; tile < NTILE; tile += kPrepNW) {
+      int arb = 0, rem = tile;
+      while (rem > arb) { rem -= arb + 1; ++arb; }
+      const int bc = rem;
+      const int m = 16 * arb, r = m + l16, j = 16 * bc + l16;
+      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        float vk[M::KPL], vq[M::KPL];
+        float vk[KPL], vq[KPL], vc[KPL];
 #pragma unroll
-        for (int e = 0; e < M::KPL; ++e) {
-          const int c = ks * M::KS + koff + e;
-          vk[e] = vq[e] = 0.f;
+        for (int e = 0; e < KPL; ++e) {
+          const int c = ks * KS + g16 * KPL + e;
+          vk[e] = vq[e] = vc[e] = 0.f;
           if (c < DK) {
-            const float ex = __expf(sG[r][c] - sG[m][c]);
+            const float gm = sG[m][c];
+            const float ex = __expf(sG[r][c] - gm);
             vk[e] = sK[r][c] * ex;
             vq[e] = sQ[r][c] * ex;
+            vc[e] = sK[j][c] * __expf(gm - sG[j][c]);
           }
         }
-        fk[ks] = M::mk(vk);
-        fq[ks] = M::mk(vq);
+        const frag fc = M::mk(vc);
+        accA = M::mma(M::mk(vk), fc, accA);
+        accP = M::mma(M::mk(vq), fc, accP);
       }
-      for (int bc = 0; bc < NRB; ++bc) {
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-        if (bc <= arb) {
-          const int j = 16 * bc + l16;
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            float vc[M::KPL];
-#pragma unroll
-            for (int e = 0; e < M::KPL; ++e) {
-              const int c = ks * M::KS + koff + e;
-              vc[e] = c < DK ? sK[j][c] * __expf(sG[m][c] - sG[j][c]) : 0.f;
-            }
-            const typename M::frag fc = M::mk(vc);
-            accA = M::mma(fk[ks], fc, accA);
-            accP = M::mma(fq[ks], fc, accP);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = m + 4 * (lane / 16) + e, jj = 16 * bc + l16;
-          sL[rr][jj] = jj < rr ? sBeta[rr] * accA[e] : 0.f;
-          blk[L::oP + (size_t)rr * CP + jj] = (MT)(jj <= rr ? accP[e] : 0.f);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int rr = m + 4 * g16 + e, jj = 16 * bc + l16;
+        sL[rr][jj] = jj < rr ? sB[rr] * accA[e] : 0.f;
+        blk[L::oP + (size_t)rr * CP + jj] = (MT)(jj <= rr ? accP[e] : 0.f);
       }
     }
-    if constexpr (CP > C) {
-      for (int idx = tid; idx < C * (CP - C); idx += kNT)
-        blk[L::oP + (size_t)(idx / (CP - C)) * CP + C + idx % (CP - C)] = (MT)0.f;
+    // the upper tiles of L and P are zero; P's padding columns too
+    for (int idx = tid; idx < C * CP; idx += kPrepNT) {
+      const int rr = idx / CP, jj = idx % CP;
+      if (jj >= C || jj / 16 > rr / 16) {
+        blk[L::oP + idx] = (MT)0.f;
+        if (jj < C) sL[rr][jj] = 0.f;
+      }
     }
   }
   __syncthreads();
 
-  // (4) W and U' by forward substitution, one column per thread:
-  //     (I + L) x = beta * rhs,  L = diag(beta) strict_lower(A)
-  for (int col = tid; col < DK + DV; col += kNT) {
-    float x[C];
-    if (col < DK) {
+  // ---- 4. Q~ and K^^T (fragment-major) and e^{Gam_n} to the workspace ----
+  {
+    constexpr int NQ = C * DKP / KPL;   // lane pieces of Q~
+#pragma unroll 1
+    for (int pc = tid; pc < NQ; pc += kPrepNT) {
+      const int ln = pc % kWave, frg = pc / kWave;
+      const int rb = frg / (DKP / KS), ks = frg % (DKP / KS);
+      const int r = 16 * rb + ln % 16, c0 = ks * KS + (ln / 16) * KPL;
+      float v[KPL];
 #pragma unroll
-      for (int r = 0; r < C; ++r) x[r] = sBeta[r] * __expf(sG[r][col]) * sK[r][col];
-    } else {
-      const int jv = col - DK;
-      const long chan = 2L * H * DK + (long)h * DV + jv;
-      f32x4 w = {0.f, 0.f, 0.f, 1.f};
-      float p0 = 0.f, p1 = 0.f, p2 = 0.f;  // raw tokens t-3, t-2, t-1
-      if (do_conv) {
-        w = *reinterpret_cast<const f32x4*>(a.conv_w + 4 * chan);
-        p0 = rv.at(jv, chan, tstart - 3);
-        p1 = rv.at(jv, chan, tstart - 2);
-        p2 = rv.at(jv, chan, tstart - 1);
+      for (int e = 0; e < KPL; ++e) {
+        const int c = c0 + e;
+        v[e] = c < DK ? __expf(sG[r][c]) * sQ[r][c] : 0.f;
       }
-#pragma unroll
-      for (int r = 0; r < C; ++r) {
-        const float xr = r < n ? rv.at(jv, chan, tstart + r) : 0.f;
-        const float y = do_conv ? silu(w.x * p0 + w.y * p1 + w.z * p2 + w.w * xr) : xr;
-        p0 = p1;
-        p1 = p2;
-        p2 = xr;
-        x[r] = sBeta[r] * y;
-      }
+      M::st(blk + L::oQ + (size_t)pc * KPL, M::mk(v));
     }
+    constexpr int NKP = DK * CP / KPL;  // lane pieces of K^^T
+#pragma unroll 1
+    for (int pc = tid; pc < NKP; pc += kPrepNT) {
+      const int ln = pc % kWave, frg = pc / kWave;
+      const int rb = frg / (CP / KS), ks = frg % (CP / KS);
+      const int c = 16 * rb + ln % 16, j0 = ks * KS + (ln / 16) * KPL;
+      const float gn = sG[C - 1][c];
+      float v[KPL];
 #pragma unroll
-    for (int r = 1; r < C; ++r) {
-      float acc = x[r];
+      for (int e = 0; e < KPL; ++e) {
+        const int jj = j0 + e;
+        v[e] = jj < C ? __expf(gn - sG[jj][c]) * sK[jj][c] : 0.f;
+      }
+      M::st(blk + L::oK + (size_t)pc * KPL, M::mk(v));
+    }
+    if (tid < DK) Dn[tid] = __expf(sG[C - 1][tid]);
+  }
+  __syncthreads();
+  // k^ -> beta e^{Gam} k^ (the right-hand side of W); Gam is dead after this
+  for (int idx = tid; idx < C * DK; idx += kPrepNT) {
+    const int r = idx / DK, c = idx % DK;
+    sK[r][c] *= sB[r] * __expf(sG[r][c]);
+  }
+  __syncthreads();
+
+  // ---- 5. X = (I + L)^{-1}, L = beta * strict_lower(A), in 16x16 blocks --
+  //  diagonal blocks: forward substitution, one lane per column;
+  //  X_ab = -X_aa * sum_{c=b}^{a-1} L_ac X_cb, by block distance a - b,
+  //  on fp32 MFMA.
+  for (int idx = tid; idx < C * C; idx += kPrepNT) {
+    const int rr = idx / C, jj = idx % C;
+    if (jj / 16 > rr / 16) sX[rr][jj] = 0.f;
+  }
+  if (wv < NRB && lane < 16) {
+    const int m = 16 * wv, j = lane;
+    float x[16];
 #pragma unroll
-      for (int j = 0; j < r; ++j) acc -= sL[r][j] * x[j];
+    for (int r = 0; r < 16; ++r) {
+      float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc -= sL[m + r][m + i] * x[i];
       x[r] = acc;
     }
-    if (col < DK) {
 #pragma unroll
-      for (int r = 0; r < C; ++r) blk[L::oW + (size_t)r * DKP + col] = (MT)(-x[r]);
-    } else {
+    for (int r = 0; r < 16; ++r) sX[m + r][m + j] = x[r];
+  }
+  __syncthreads();
+  for (int dist = 1; dist < NRB; ++dist) {
+    if (wv < NRB - dist) {
+      const int ab = wv + dist, bb = wv;
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      for (int cb = bb; cb < ab; ++cb) {
 #pragma unroll
-      for (int r = 0; r < C; ++r) blk[L::oU + (size_t)r * DV + (col - DK)] = (MT)x[r];
+        for (int s = 0; s < 4; ++s)
+          y = mma_f32x4(sL[16 * ab + l16][16 * cb + 4 * s + g16],
+                        sX[16 * cb + 4 * s + g16][16 * bb + l16], y);
+      }
+      // X_aa * Y with the contraction index of step s taken as 4*(lane/16)+s:
+      // Y's rows are then exactly the accumulator elements each lane holds.
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) x = mma_f32x4(sX[16 * ab + l16][16 * ab + 4 * g16 + s], y[s], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sX[16 * ab + 4 * g16 + e][16 * bb + l16] = -x[e];
+    }
+    __syncthreads();
+  }
+
+  // ---- 6. W = X (beta e^Gam K) and U' = X (beta V) on MFMA ---------------
+  {
+    constexpr int NCBW = DK / 16, NCBU = DV / 16;
+    constexpr int NKC = CP / KS;
+    for (int cbk = wv; cbk < NCBW + NCBU; cbk += kPrepNW) {
+      const bool isw = cbk < NCBW;
+      const int col = (isw ? cbk : cbk - NCBW) * 16 + l16;
+      frag fb[NKC];
+#pragma unroll
+      for (int ks = 0; ks < NKC; ++ks) {
+        float v[KPL];
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          const int jj = ks * KS + g16 * KPL + e;
+          v[e] = jj < C ? (isw ? sK[jj][col] : sB[jj] * to_f32(sV[jj][col])) : 0.f;
+        }
+        fb[ks] = M::mk(v);
+      }
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKC; ++ks) {
+          float v[KPL];
+#pragma unroll
+          for (int e = 0; e < KPL; ++e) {
+            const int jj = ks * KS + g16 * KPL + e;
+            v[e] = jj < C ? sX[16 * rb + l16][jj] : 0.f;
+          }
+          acc = M::mma(M::mk(v), fb[ks], acc);
+        }
+        if (isw) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sWst[16 * rb + 4 * g16 + e][col] = (MT)(-acc[e]);
+        } else {
+          MT* dst = blk + L::oU + ((size_t)(rb * NCBU + (cbk - NCBW)) * kWave + lane) * 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e] = (MT)acc[e];
+        }
+      }
+    }
+    if constexpr (DKP > DK) {
+      for (int idx = tid; idx < C * (DKP - DK); idx += kPrepNT)
+        sWst[idx / (DKP - DK)][DK + idx % (DKP - DK)] = (MT)0.f;
     }
   }
-  // (5) Q~ = e^{Gam} q^, K^^T = (e^{Gam_n - Gam} k^)^T, e^{Gam_n}; K-pads zeroed
-  for (int idx = tid; idx < C * DKP; idx += kNT) {
-    const int r = idx / DKP, c = idx % DKP;
-    blk[L::oQ + idx] = (MT)(c < DK ? __expf(sG[r][c]) * sQ[r][c] : 0.f);
-    if (c >= DK) blk[L::oW + idx] = (MT)0.f;
+  __syncthreads();
+  // -W, fragment-major
+  {
+    constexpr int NQ = C * DKP / KPL;
+#pragma unroll 1
+    for (int pc = tid; pc < NQ; pc += kPrepNT) {
+      const int ln = pc % kWave, frg = pc / kWave;
+      const int rb = frg / (DKP / KS), ks = frg % (DKP / KS);
+      const int r = 16 * rb + ln % 16, c0 = ks * KS + (ln / 16) * KPL;
+      M::st(blk + L::oW + (size_t)pc * KPL, M::ld(&sWst[r][c0]));
+    }
   }
-  for (int idx = tid; idx < DK * CP; idx += kNT) {
-    const int c = idx / CP, j = idx % CP;
-    blk[L::oK + idx] = (MT)(j < C ? __expf(sG[C - 1][c] - sG[j][c]) * sK[j][c] : 0.f);
-  }
-  if (tid < DK) Dn[tid] = __expf(sG[C - 1][tid]);
 }
 
 // ---------------------------------------------------------------------------
-// chain: one workgroup per (dv-block, head, sequence); walks the chunks.
+// chain: one workgroup of 256 threads per (dv-block, head, sequence) walks the
+// chunks in order. Wave w owns the U/O row blocks w, w+4, ... and the S row
+// blocks w, w+4, ... (all column tiles of the dv-block). The next chunk's
+// workspace operands are loaded into registers while the current one runs.
+constexpr int kChainNT = 256;
+constexpr int kChainNW = kChainNT / kWave;
+
 template <int C, int DK, int DV, int DVB, typename IO, class M>
-__global__ __launch_bounds__(kNT) void prefill_chain_kernel(PrefillArgs a, int t0, int ncs,
-                                                            const uint8_t* ws) {
+__global__ __launch_bounds__(kChainNT) void prefill_chain_kernel(PrefillArgs a, int t0, int ncs,
+                                                                 const uint8_t* ws) {
   using L = Ws<C, DK, DV, M>;
   using MT = typename M::T;
+  using frag = typename M::frag;
   constexpr int DKP = L::DKP, CP = L::CP;
-  constexpr int NCB = DVB / 16;                 // 16-wide column tiles per block
-  constexpr int NU = (C / 16) * NCB;            // tiles of U and O
-  constexpr int NS = (DK / 16) * NCB;           // tiles of S
-  constexpr int UPW = (NU + kNW - 1) / kNW, SPW = (NS + kNW - 1) / kNW;
+  constexpr int KS = M::KS, KPL = M::KPL;
+  constexpr int NW = kChainNW;
+  constexpr int NCB = DVB / 16;                       // 16-wide column tiles per block
+  constexpr int NRU = C / 16, NRS = DK / 16;          // row blocks of U/O and of S
+  constexpr int RU = (NRU + NW - 1) / NW, RS = (NRS + NW - 1) / NW;
+  constexpr int NKS = DKP / KS, NKP = CP / KS;
   constexpr int PAD = 16 / (int)sizeof(MT);
   constexpr int LDST = DKP + PAD, LDUT = CP + PAD;
-  __shared__ __attribute__((aligned(16))) MT sST[DVB][LDST];  // S^T (bf16 or fp32)
+  __shared__ __attribute__((aligned(16))) MT sST[DVB][LDST];  // S^T
   __shared__ __attribute__((aligned(16))) MT sUT[DVB][LDUT];  // U^T
 
   const int H = a.H, T = a.T, B = a.B;
   constexpr int nblk = DV / DVB;
   // Workgroup -> (column block, head, sequence). Workgroups are dealt to the
-  // 8 XCDs round-robin; when the (h, b) count allows it, the nblk column
-  // blocks of one head land on the same XCD so they share its L2 copy of
-  // the head's workspace.
+  // 8 XCDs round-robin; when the (h, b) count allows it, the column blocks
+  // of one head land on the same XCD and share its L2 copy of the workspace.
   int cbk, hb;
   const int L1 = blockIdx.x;
   const int HB = H * B;
@@ -333,115 +469,160 @@ __global__ __launch_bounds__(kNT) void prefill_chain_kernel(PrefillArgs a, int t
   const int h = hb % H, b = hb / H;
   const int cb0 = cbk * DVB;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
-  const int l16 = lane % 16, koff = (lane / 16) * M::KPL, r4 = 4 * (lane / 16);
+  const int l16 = lane % 16, koff = (lane / 16) * KPL, r4 = 4 * (lane / 16);
 
-  for (int idx = tid; idx < DVB * LDST; idx += kNT) (&sST[0][0])[idx] = (MT)0.f;
-  for (int idx = tid; idx < DVB * LDUT; idx += kNT) (&sUT[0][0])[idx] = (MT)0.f;
+  for (int idx = tid; idx < DVB * LDST; idx += kChainNT) (&sST[0][0])[idx] = (MT)0.f;
+  for (int idx = tid; idx < DVB * LDUT; idx += kChainNT) (&sUT[0][0])[idx] = (MT)0.f;
+
+  struct Frags {
+    frag w[RU][NKS], q[RU][NKS], p[RU][NKP], k[RS][NKP];
+    f32x4 u[RU][NCB], dn[RS];
+  };
+  auto load = [&](Frags& f, int cl) {
+    const MT* blk =
+        reinterpret_cast<const MT*>(ws + ((size_t)cl * B * H + (size_t)b * H + h) * L::bytes);
+    const float* Dn = reinterpret_cast<const float*>(blk + L::nT);
+#pragma unroll
+    for (int i = 0; i < RU; ++i) {
+      const int rb = wv + NW * i;
+      if (rb < NRU) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          f.w[i][ks] = M::ld(blk + L::oW + ((size_t)(rb * NKS + ks) * kWave + lane) * KPL);
+          f.q[i][ks] = M::ld(blk + L::oQ + ((size_t)(rb * NKS + ks) * kWave + lane) * KPL);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKP; ++ks)
+          f.p[i][ks] = M::ld(blk + L::oP + (size_t)(16 * rb + l16) * CP + ks * KS + koff);
+#pragma unroll
+        for (int ct = 0; ct < NCB; ++ct) {
+          const MT* up = blk + L::oU +
+                         ((size_t)(rb * (DV / 16) + cb0 / 16 + ct) * kWave + lane) * 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f.u[i][ct][e] = to_f32(up[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const int rb = wv + NW * i;
+      if (rb < NRS) {
+#pragma unroll
+        for (int ks = 0; ks < NKP; ++ks)
+          f.k[i][ks] = M::ld(blk + L::oK + ((size_t)(rb * NKP + ks) * kWave + lane) * KPL);
+        f.dn[i] = *reinterpret_cast<const f32x4*>(Dn + 16 * rb + r4);
+      }
+    }
+  };
 
   float* Sg = a.S + ((long)b * H + h) * DK * DV + cb0;
-  f32x4 accS[SPW];
+  f32x4 accS[RS][NCB];
 #pragma unroll
-  for (int sl = 0; sl < SPW; ++sl) {
-    const int s = wv + kNW * sl;
-    accS[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (s < NS) {
-      const int i0 = 16 * (s / NCB) + r4, col = 16 * (s % NCB) + l16;
+  for (int i = 0; i < RS; ++i) {
+    const int rb = wv + NW * i;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) accS[sl][e] = Sg[(long)(i0 + e) * DV + col];
+    for (int ct = 0; ct < NCB; ++ct) {
+      accS[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (rb < NRS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          accS[i][ct][e] = Sg[(long)(16 * rb + r4 + e) * DV + 16 * ct + l16];
+      }
     }
   }
+  Frags cur;
+  load(cur, 0);
   __syncthreads();
 
   for (int cl = 0; cl < ncs; ++cl) {
-    const MT* blk = reinterpret_cast<const MT*>(ws + ((size_t)cl * B * H + (size_t)b * H + h) * L::bytes);
-    const float* Dn = reinterpret_cast<const float*>(blk + L::nT);
+    Frags nxt = cur;
+    if (cl + 1 < ncs) load(nxt, cl + 1);
     const int tstart = t0 + cl * C;
     const int n = min(C, T - tstart);
 
     // (i) S -> LDS, transposed, in the MFMA operand type
 #pragma unroll
-    for (int sl = 0; sl < SPW; ++sl) {
-      const int s = wv + kNW * sl;
-      if (s < NS) {
-        const int i0 = 16 * (s / NCB) + r4, col = 16 * (s % NCB) + l16;
+    for (int i = 0; i < RS; ++i) {
+      const int rb = wv + NW * i;
+      if (rb < NRS) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sST[col][i0 + e] = (MT)accS[sl][e];
+        for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sST[16 * ct + l16][16 * rb + r4 + e] = (MT)accS[i][ct][e];
       }
     }
     __syncthreads();
 
     // (ii) U = U' - W S and O = Q~ S
-    f32x4 accO[UPW];
+    f32x4 accO[RU][NCB];
 #pragma unroll
-    for (int sl = 0; sl < UPW; ++sl) {
-      const int u = wv + kNW * sl;
-      accO[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u < NU) {
-        const int rb = u / NCB, cbt = u % NCB;
-        const int col = 16 * cbt + l16;
-        f32x4 accU;
+    for (int i = 0; i < RU; ++i) {
+      const int rb = wv + NW * i;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          accU[e] = to_f32(blk[L::oU + (size_t)(16 * rb + r4 + e) * DV + cb0 + col]);
-        const MT* wrow = blk + L::oW + (size_t)(16 * rb + l16) * DKP + koff;
-        const MT* qrow = blk + L::oQ + (size_t)(16 * rb + l16) * DKP + koff;
-        const MT* srow = &sST[col][koff];
+      for (int ct = 0; ct < NCB; ++ct) {
+        accO[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (rb < NRU) {
+          f32x4 accU = cur.u[i][ct];
 #pragma unroll
-        for (int ks = 0; ks < DKP / M::KS; ++ks) {
-          const typename M::frag fs = M::ld(srow + ks * M::KS);
-          accU = M::mma(M::ld(wrow + ks * M::KS), fs, accU);
-          accO[sl] = M::mma(M::ld(qrow + ks * M::KS), fs, accO[sl]);
+          for (int ks = 0; ks < NKS; ++ks) {
+            const frag fs = M::ld(&sST[16 * ct + l16][ks * KS + koff]);
+            accU = M::mma(cur.w[i][ks], fs, accU);
+            accO[i][ct] = M::mma(cur.q[i][ks], fs, accO[i][ct]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sUT[16 * ct + l16][16 * rb + r4 + e] = (MT)accU[e];
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sUT[col][16 * rb + r4 + e] = (MT)accU[e];
       }
     }
     __syncthreads();
 
-    // (iii) O += P U (store), S = Diag(e^{Gam_n}) S + K^^T U
+    // (iii) O += P U (stored), S = Diag(e^{Gam_n}) S + K^^T U
 #pragma unroll
-    for (int sl = 0; sl < UPW; ++sl) {
-      const int u = wv + kNW * sl;
-      if (u < NU) {
-        const int rb = u / NCB, cbt = u % NCB;
-        const int col = 16 * cbt + l16;
-        const MT* prow = blk + L::oP + (size_t)(16 * rb + l16) * CP + koff;
-        const MT* urow = &sUT[col][koff];
+    for (int i = 0; i < RU; ++i) {
+      const int rb = wv + NW * i;
+      if (rb < NRU) {
 #pragma unroll
-        for (int ks = 0; ks < CP / M::KS; ++ks)
-          accO[sl] = M::mma(M::ld(prow + ks * M::KS), M::ld(urow + ks * M::KS), accO[sl]);
-        IO* op = static_cast<IO*>(a.o) + (((long)b * T + tstart) * H + h) * DV + cb0 + col;
+        for (int ct = 0; ct < NCB; ++ct) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rb + r4 + e;
-          if (r < n) op[(long)r * H * DV] = from_f32<IO>(accO[sl][e]);
+          for (int ks = 0; ks < NKP; ++ks)
+            accO[i][ct] = M::mma(cur.p[i][ks], M::ld(&sUT[16 * ct + l16][ks * KS + koff]),
+                                 accO[i][ct]);
+          IO* op = static_cast<IO*>(a.o) + (((long)b * T + tstart) * H + h) * DV + cb0 +
+                   16 * ct + l16;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + r4 + e;
+            if (r < n) op[(long)r * H * DV] = from_f32<IO>(accO[i][ct][e]);
+          }
         }
       }
     }
 #pragma unroll
-    for (int sl = 0; sl < SPW; ++sl) {
-      const int s = wv + kNW * sl;
-      if (s < NS) {
-        const int rb = s / NCB, cbt = s % NCB;
-        const int col = 16 * cbt + l16;
+    for (int i = 0; i < RS; ++i) {
+      const int rb = wv + NW * i;
+      if (rb < NRS) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) accS[sl][e] *= Dn[16 * rb + r4 + e];
-        const MT* krow = blk + L::oK + (size_t)(16 * rb + l16) * CP + koff;
-        const MT* urow = &sUT[col][koff];
+        for (int ct = 0; ct < NCB; ++ct) {
 #pragma unroll
-        for (int ks = 0; ks < CP / M::KS; ++ks)
-          accS[sl] = M::mma(M::ld(krow + ks * M::KS), M::ld(urow + ks * M::KS), accS[sl]);
+          for (int e = 0; e < 4; ++e) accS[i][ct][e] *= cur.dn[i][e];
+#pragma unroll
+          for (int ks = 0; ks < NKP; ++ks)
+            accS[i][ct] = M::mma(cur.k[i][ks], M::ld(&sUT[16 * ct + l16][ks * KS + koff]),
+                                 accS[i][ct]);
+        }
       }
     }
+    cur = nxt;
   }
 
 #pragma unroll
-  for (int sl = 0; sl < SPW; ++sl) {
-    const int s = wv + kNW * sl;
-    if (s < NS) {
-      const int i0 = 16 * (s / NCB) + r4, col = 16 * (s % NCB) + l16;
+  for (int i = 0; i < RS; ++i) {
+    const int rb = wv + NW * i;
+    if (rb < NRS) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Sg[(long)(i0 + e) * DV + col] = accS[sl][e];
+      for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sg[(long)(16 * rb + r4 + e) * DV + 16 * ct + l16] = accS[i][ct][e];
     }
   }
 }
@@ -458,12 +639,12 @@ hipError_t run(const PrefillArgs& a, uint8_t* ws, size_t ws_bytes, hipStream_t s
   for (int c0 = 0; c0 < nchunks; c0 += seg) {
     const int ncs = nchunks - c0 < seg ? nchunks - c0 : seg;
     const int t0 = c0 * C;
-    hipLaunchKernelGGL((prefill_prep_kernel<C, DK, DV, IO, M>), dim3(ncs, a.H, a.B), dim3(kNT),
-                       0, st, a, t0, ws);
+    hipLaunchKernelGGL((prefill_prep_kernel<C, DK, DV, IO, M>), dim3(ncs, a.H, a.B),
+                       dim3(kPrepNT), 0, st, a, t0, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_chain_kernel<C, DK, DV, DVB, IO, M>),
-                       dim3((DV / DVB) * a.H * a.B), dim3(kNT), 0, st, a, t0, ncs,
+                       dim3((DV / DVB) * a.H * a.B), dim3(kChainNT), 0, st, a, t0, ncs,
                        (const uint8_t*)ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -24,8 +24,10 @@
  * (the chunkwise-parallel prefill).
  *
  * Conventions for every call:
- *  - Pointers named as device buffers are HIP device pointers, 16-byte
- *    aligned, densely packed in the layouts given. The caller owns them.
+ *  - Pointers named as device buffers are HIP device pointers, densely
+ *    packed in the layouts given; the caller owns them. q, k, v, o and the
+ *    ring need the alignment of their element type, g and beta 4 bytes;
+ *    conv_w, S (s_mem), ring_mem and the prefill workspace 16 bytes.
  *  - Calls are asynchronous on the given stream (NULL = the default stream)
  *    and never synchronise the host. A kernel fault surfaces at the caller's
  *    next synchronisation.

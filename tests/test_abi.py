@@ -101,8 +101,10 @@ def test_decode_validation(fake_state):
     assert call_decode(None) == K.KDA_ERR_INVALID
     assert call_decode(fake_state, q=None) == K.KDA_ERR_INVALID
     assert "q is NULL" in kda.last_error()
-    assert call_decode(fake_state, beta=FAKE + 4) == K.KDA_ERR_INVALID
-    assert "aligned" in kda.last_error()
+    assert call_decode(fake_state, beta=FAKE + 2) == K.KDA_ERR_INVALID
+    assert "4-byte aligned" in kda.last_error()
+    assert call_decode(fake_state, w=FAKE + 4) == K.KDA_ERR_INVALID
+    assert "conv_w is not 16-byte aligned" in kda.last_error()
     assert call_decode(fake_state, flags=8) == K.KDA_ERR_INVALID
     assert call_decode(fake_state, w=None) == K.KDA_ERR_INVALID
     assert "conv_w" in kda.last_error()
