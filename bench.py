@@ -61,6 +61,34 @@ def prefill_flops(B, T, H, dk, dv, C):
     return B * T * H * per
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SOURCES = ["gated_delta_rule_83_amd/csrc/kda_decode.hip",
+                  "gated_delta_rule_83_amd/csrc/kda_common.h"]
+
+
+def source_digest(paths):
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed FETCH_SIZE/WRITE_SIZE
+    counter runs, or None when the decode kernel's source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest(DECODE_SOURCES):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -179,9 +207,10 @@ def main():
                                inp.beta[:, sl], inp.conv_w, inp.S0, inp.ring0)
             return time.perf_counter() - t0
 
-        t1 = run_oracle(1)
-        n = int(max(1, min(T, args.cpu_seconds / max(t1, 1e-3))))
-        tn = run_oracle(n)
+        n, tn = 4, run_oracle(4)
+        while tn < 0.5 * args.cpu_seconds and n < T:
+            n = int(min(T, max(n + 1, n * args.cpu_seconds / max(tn, 1e-3))))
+            tn = run_oracle(n)
         cpu = {"value": B * n / tn, "unit": "tokens/s", "cores": kda_oracle.max_threads(),
                "kind": "oracle",
                "sample": f"fp64 sequential oracle, first {n} of the 256 staged decode steps "
@@ -206,8 +235,9 @@ def main():
                                "(inputs of 256 consecutive steps staged in HBM)",
                    "batch": B, "heads": H, "d_k": dk, "d_v": dv, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "decode_step_kernel<128,128,256,bf16>",
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(),
+                     "kernel": "decode_step_kernel<128,128,1024,bf16,nontemporal>",
                      "bytes_per_launch": dbytes, "avg_launch_us": per_launch_s * 1e6},
         "prefill": {"workload": "chunked prefill T=4096, batch 1, 96 heads, chunk 64, bf16",
                     "tokens_per_s": pT * pB / (pre_ms / 1e3), "ms": pre_ms,

@@ -25,7 +25,24 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
-__device__ __forceinline__ float silu(float y) { return y / (1.0f + __expf(-y)); }
+// Raw buffer stores: a store whose byte offset is at or past the resource's
+// size is dropped by the hardware range check, so row tails need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int off, float v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int off, float v, bf16*) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)v), r, off, 0,
+                                        0);
+}
+
+// SiLU(y) = y * sigmoid(y), with the hardware reciprocal (about 1 ulp) in place
+// of an IEEE division; y -> -inf gives -0.
+__device__ __forceinline__ float silu(float y) {
+  return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+}
 
 // Sum over the 64 lanes of a wave; every lane receives the total.
 __device__ __forceinline__ float wave_sum(float x) {

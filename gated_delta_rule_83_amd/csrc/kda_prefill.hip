@@ -37,6 +37,11 @@ struct MmaBf16 {
   static constexpr int KS = 32, KPL = 8;
   __device__ static frag ld(const T* p) { return *reinterpret_cast<const frag*>(p); }
   __device__ static void st(T* p, frag f) { *reinterpret_cast<frag*>(p) = f; }
+  using quad = bf16x4;  // four elements as loaded (converted at first use)
+  __device__ static quad ld4(const T* p) { return *reinterpret_cast<const quad*>(p); }
+  __device__ static f32x4 cvt4(quad v) {
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
   __device__ static frag mk(const float* v) {
     frag f;
 #pragma unroll
@@ -55,6 +60,9 @@ struct MmaF32 {
   static constexpr int KS = 4, KPL = 1;
   __device__ static frag ld(const T* p) { return *p; }
   __device__ static void st(T* p, frag f) { *p = f; }
+  using quad = f32x4;
+  __device__ static quad ld4(const T* p) { return *reinterpret_cast<const quad*>(p); }
+  __device__ static f32x4 cvt4(quad v) { return v; }
   __device__ static frag mk(const float* v) { return v[0]; }
   __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -96,22 +104,72 @@ constexpr size_t ws_block_bytes(int C, int DK, int DV, int KS, size_t esz) {
 constexpr int kPrepNT = 512;
 constexpr int kPrepNW = kPrepNT / kWave;
 
+// Eight consecutive elements of the token I/O type, as one or two 16-byte loads.
+template <typename IO> struct Vec8;
+template <> struct Vec8<bf16> {
+  bf16x8 v;
+  __device__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ float operator[](int e) const { return (float)v[e]; }
+};
+template <> struct Vec8<float> {
+  f32x4 lo, hi;
+  __device__ void load(const float* p) {
+    lo = reinterpret_cast<const f32x4*>(p)[0];
+    hi = reinterpret_cast<const f32x4*>(p)[1];
+  }
+  __device__ float operator[](int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
+};
+
+// n consecutive fp32 LDS values (16-byte aligned when n is a multiple of 4)
+template <int N>
+__device__ __forceinline__ void lds_rd(const float* p, float (&v)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const f32x4 t = reinterpret_cast<const f32x4*>(p)[i];
+      v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = p[i];
+  }
+}
+
+// eight values to 16-byte aligned LDS in the operand type
+__device__ __forceinline__ void st8(bf16* p, const float* v) {
+  bf16x8 t;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = (bf16)v[e];
+  *reinterpret_cast<bf16x8*>(p) = t;
+}
+__device__ __forceinline__ void st8(float* p, const float* v) {
+  reinterpret_cast<f32x4*>(p)[0] = f32x4{v[0], v[1], v[2], v[3]};
+  reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
+}
+
 template <int C, int DK, int DV, typename IO, class M>
 struct PrepSmem {
-  using ST = IO;                                   // storage of v^ in LDS
-  static constexpr int LDK = DK + 4, LDC = C + 4;  // fp32 row strides
-  static constexpr int LDV = DV + 16 / (int)sizeof(ST);
-  static constexpr size_t oQ = 0;                                    // q^ (later -W staging)
-  static constexpr size_t oK = oQ + (size_t)C * LDK * 4;             // k^ (later beta e^Gam k^)
-  static constexpr size_t nGX = (size_t)C * (LDK > LDC ? LDK : LDC) * 4;
-  static constexpr size_t oGX = oK + (size_t)C * LDK * 4;            // Gam, later X
-  static constexpr size_t oL = oGX + nGX;                            // beta * strict_lower(A)
-  static constexpr size_t oV = oL + (size_t)C * LDC * 4;             // v^
-  static constexpr size_t oB = oV + (size_t)C * LDV * sizeof(ST);    // beta
-  static constexpr size_t bytes = oB + (size_t)C * 4;
+  using MT = typename M::T;
+  static constexpr int DKP = rup(DK, M::KS), CP = rup(C, M::KS);
+  static constexpr int LDK = DK + 4, LDC = C + 4;                      // fp32 row strides
+  static constexpr int LDT = CP + (sizeof(MT) == 2 ? 8 : 4);           // MT rows over tokens
+  static constexpr int TS = 16, NSTRIP = C / TS;                       // token strips
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  // region Q: q^ (fp32), later (beta e^Gam k^)^T as MT [DK][LDT]
+  static constexpr size_t oQ = 0, nQ = mx((size_t)C * LDK * 4, (size_t)DK * LDT * sizeof(MT));
+  // region K: k^ (fp32), later -W staging as MT [C][DKP]
+  static constexpr size_t oK = oQ + nQ, nK = mx((size_t)C * LDK * 4, (size_t)C * DKP * sizeof(MT));
+  // region G: Gam (fp32), later X (fp32 [C][LDC]) followed by X as MT [C][LDT]
+  static constexpr size_t oG = oK + nK;
+  static constexpr size_t oXb = oG + (size_t)C * LDC * 4;
+  static constexpr size_t nG = mx((size_t)C * LDK * 4, (size_t)C * LDC * 4 + (size_t)C * LDT * sizeof(MT));
+  static constexpr size_t oL = oG + nG;                              // beta*strict_lower(A)
+  static constexpr size_t oV = oL + (size_t)C * LDC * 4;             // (beta v^)^T as MT [DV][LDT]
+  static constexpr size_t oB = oV + (size_t)DV * LDT * sizeof(MT);   // beta [C]
+  static constexpr size_t oT = oB + (size_t)C * 4;                   // strip totals of g
+  static constexpr size_t bytes = oT + (size_t)NSTRIP * DK * 4;
   static_assert(bytes <= 160 * 1024, "prep LDS exceeds 160 KiB");
-  static_assert((size_t)C * rup(DK, M::KS) * sizeof(typename M::T) <= (size_t)C * LDK * 4,
-                "-W staging does not fit in the q^ region");
+  static_assert(C % TS == 0, "chunk must be a multiple of the token strip");
 };
 
 template <int C, int DK, int DV, typename IO, class M>
@@ -120,21 +178,27 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
   using L = Ws<C, DK, DV, M>;
   using SM = PrepSmem<C, DK, DV, IO, M>;
   using MT = typename M::T;
-  using ST = typename SM::ST;
   using frag = typename M::frag;
-  constexpr int LDK = SM::LDK, LDC = SM::LDC, LDV = SM::LDV;
+  constexpr int LDK = SM::LDK, LDC = SM::LDC, LDT = SM::LDT;
   constexpr int DKP = L::DKP, CP = L::CP;
   constexpr int NRB = C / 16;
   constexpr int KS = M::KS, KPL = M::KPL;
+  constexpr int TS = SM::TS, NSTRIP = SM::NSTRIP;
+  constexpr int CGK = DK / 8, CGV = DV / 8, CG4 = DK / 4;
+  constexpr int NQ = CGK * NSTRIP, NV = CGV * NSTRIP, NG = CG4 * NSTRIP;
+  static_assert(2 * NQ + NV + NG + C <= kPrepNT, "not enough threads for the load roles");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SM::bytes];
   float (*sQ)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oQ);
+  MT (*sKT)[LDT] = reinterpret_cast<MT (*)[LDT]>(smem + SM::oQ);
   float (*sK)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oK);
-  float (*sG)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oGX);
-  float (*sX)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oGX);
+  MT (*sWst)[DKP] = reinterpret_cast<MT (*)[DKP]>(smem + SM::oK);
+  float (*sG)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oG);
+  float (*sX)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oG);
+  MT (*sXb)[LDT] = reinterpret_cast<MT (*)[LDT]>(smem + SM::oXb);
   float (*sL)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oL);
-  ST (*sV)[LDV] = reinterpret_cast<ST (*)[LDV]>(smem + SM::oV);
+  MT (*sVT)[LDT] = reinterpret_cast<MT (*)[LDT]>(smem + SM::oV);
   float* sB = reinterpret_cast<float*>(smem + SM::oB);
-  MT (*sWst)[DKP] = reinterpret_cast<MT (*)[DKP]>(smem + SM::oQ);
+  float (*sTot)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oT);
 
   const int cl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
@@ -148,91 +212,120 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
   const bool do_conv = !(a.flags & KDA_F_SKIP_CONV);
   const bool do_l2 = !(a.flags & KDA_F_SKIP_L2);
 
-  // ---- 1. every global input of the chunk, loaded up front ---------------
-  // Threads [0, DK) own q channels, [DK, 2DK) k channels, [2DK, 2DK+DV) v
-  // channels: each loads its channel for the C tokens and the three before
-  // (ring or earlier tokens), convolves with a rolling window and writes the
-  // activation to LDS. Threads [2DK+DV, 2DK+DV+DK) own the g channels and
-  // form the in-chunk prefix sums. Loads use clamped, always-valid addresses
-  // and masks instead of branches so that they are all in flight together.
-  if (tid < C) sB[tid] = tid < n ? a.beta[((long)b * T + tstart + tid) * H + h] : 0.f;
-  if (tid < 2 * DK + DV) {
-    int p, c, d;
-    const IO* x;
-    long chan;
-    if (tid < DK) {
-      p = 0; c = tid; d = DK; x = static_cast<const IO*>(a.q); chan = (long)h * DK + c;
-    } else if (tid < 2 * DK) {
-      p = 1; c = tid - DK; d = DK; x = static_cast<const IO*>(a.k);
-      chan = (long)H * DK + (long)h * DK + c;
-    } else {
-      p = 2; c = tid - 2 * DK; d = DV; x = static_cast<const IO*>(a.v);
-      chan = 2L * H * DK + (long)h * DV + c;
-    }
-    const IO* ring = static_cast<const IO*>(a.ring) + (long)b * 3 * ctot + chan;
-    const IO* xc = x + ((long)b * T * H + h) * d + c;   // token 0 of this channel
-    const long ts = (long)H * d;                        // token stride
-    float raw[C + 3];
+  // token-padding columns of the MT operand tiles are zero (only when the
+  // chunk is shorter than the MFMA depth)
+  if constexpr (CP > C) {
+    for (int idx = tid; idx < DV * (CP - C); idx += kPrepNT)
+      sVT[idx / (CP - C)][C + idx % (CP - C)] = (MT)0.f;
+  }
+
+  // ---- 1. all global inputs of the chunk, 16-byte loads ------------------
+  // q, k, v threads: 8 channels x a strip of 16 tokens (+ the 3 raw tokens
+  // before it, from the ring at the sequence start) -> conv, SiLU, and for
+  // q, k the L2 norm by an xor-shuffle over the lanes that share the token.
+  // g threads: 4 channels x 16 tokens -> strip-local prefix sums of g.
+  float gacc[TS][4];
+  int gs = 0, gc0 = 0;
+  const bool g_role = tid >= 2 * NQ + NV && tid < 2 * NQ + NV + NG;
+  if (tid < 2 * NQ + NV) {
+    const int p = tid < NQ ? 0 : (tid < 2 * NQ ? 1 : 2);
+    const int t = tid - (p == 0 ? 0 : (p == 1 ? NQ : 2 * NQ));
+    const int CG = p == 2 ? CGV : CGK;
+    const int d = p == 2 ? DV : DK;
+    const int cg = t % CG, s = t / CG;
+    const int c0 = 8 * cg, r0 = s * TS;
+    const IO* x = static_cast<const IO*>(p == 0 ? a.q : (p == 1 ? a.k : a.v));
+    const long chan0 = (p == 0 ? 0L : (p == 1 ? (long)H * DK : 2L * H * DK)) + (long)h * d + c0;
+    const IO* ring = static_cast<const IO*>(a.ring) + (long)b * 3 * ctot + chan0;
+    const IO* xc = x + ((long)b * T * H + h) * d + c0;   // token 0, channel c0
+    const long ts = (long)H * d;
+    Vec8<IO> raw[TS + 3];
 #pragma unroll
-    for (int i = 0; i < C + 3; ++i) {
-      const int tok = tstart - 3 + i;
+    for (int i = 0; i < TS + 3; ++i) {
+      const int tok = tstart + r0 - 3 + i;
       const int tcl = tok < T ? tok : T - 1;
-      const IO* src = tcl >= 0 ? xc + (long)tcl * ts
-                               : (do_conv ? ring + (long)(3 + tcl) * ctot : xc);
-      const float val = to_f32(*src);
-      raw[i] = ((i >= 3 || do_conv) && tok < T) ? val : 0.f;
+      const IO* src = tcl >= 0 ? xc + (long)tcl * ts : (do_conv ? ring + (long)(3 + tcl) * ctot : xc);
+      raw[i].load(src);
     }
-    f32x4 w = {0.f, 0.f, 0.f, 1.f};
-    if (do_conv) w = *reinterpret_cast<const f32x4*>(a.conv_w + 4 * chan);
+    f32x4 w[8];
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      float y = raw[r + 3];
-      if (do_conv) y = silu(w.x * raw[r] + w.y * raw[r + 1] + w.z * raw[r + 2] + w.w * raw[r + 3]);
-      y = r < n ? y : 0.f;
-      if (p == 0) sQ[r][c] = y;
-      else if (p == 1) sK[r][c] = y;
-      else sV[r][c] = (ST)y;
-    }
-  } else if (tid < 2 * DK + DV + DK) {
-    const int c = tid - (2 * DK + DV);
-    const float* gc = a.g + ((long)b * T * H + h) * DK + c;
-    float gv[C];
+    for (int e = 0; e < 8; ++e)
+      w[e] = do_conv ? *reinterpret_cast<const f32x4*>(a.conv_w + 4 * (chan0 + e))
+                     : f32x4{0.f, 0.f, 0.f, 1.f};
+    float bv[TS];
+    if (p == 2) {
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      const int tcl = tstart + r < T ? tstart + r : T - 1;
-      gv[r] = gc[(long)tcl * H * DK];
+      for (int r = 0; r < TS; ++r) {
+        const int tcl = min(tstart + r0 + r, T - 1);
+        bv[r] = a.beta[((long)b * T + tcl) * H + h];
+      }
     }
-    float acc = 0.f;
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      acc += r < n ? gv[r] : 0.f;
-      sG[r][c] = acc;
+    for (int r = 0; r < TS; ++r) {
+      const bool valid = r0 + r < n;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x3 = raw[r + 3][e];
+        const float v = do_conv ? silu(w[e].x * raw[r][e] + w[e].y * raw[r + 1][e] +
+                                       w[e].z * raw[r + 2][e] + w[e].w * x3)
+                                : x3;
+        y[e] = valid ? v : 0.f;
+      }
+      if (p < 2) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
+#pragma unroll
+        for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off, kWave);
+        const float inv = do_l2 ? 1.0f / sqrtf(ss + kL2Eps) : 1.0f;
+        float* dst = p == 0 ? &sQ[r0 + r][c0] : &sK[r0 + r][c0];
+        reinterpret_cast<f32x4*>(dst)[0] = f32x4{y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv};
+        reinterpret_cast<f32x4*>(dst)[1] = f32x4{y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv};
+      } else {
+        const float bb = valid ? bv[r] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sVT[c0 + e][r0 + r] = (MT)(bb * y[e]);
+      }
     }
+  } else if (g_role) {
+    const int t = tid - (2 * NQ + NV);
+    gc0 = 4 * (t % CG4);
+    gs = t / CG4;
+    const int r0 = gs * TS;
+#pragma unroll
+    for (int r = 0; r < TS; ++r) {
+      const int tcl = min(tstart + r0 + r, T - 1);
+      const f32x4 gv =
+          *reinterpret_cast<const f32x4*>(a.g + (((long)b * T + tcl) * H + h) * DK + gc0);
+      const bool valid = r0 + r < n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gacc[r][e] = valid ? gv[e] : 0.f;
+    }
+#pragma unroll
+    for (int r = 1; r < TS; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gacc[r][e] += gacc[r - 1][e];
+    *reinterpret_cast<f32x4*>(&sTot[gs][gc0]) =
+        f32x4{gacc[TS - 1][0], gacc[TS - 1][1], gacc[TS - 1][2], gacc[TS - 1][3]};
+  } else if (tid < 2 * NQ + NV + NG + C) {
+    const int r = tid - (2 * NQ + NV + NG);
+    sB[r] = r < n ? a.beta[((long)b * T + tstart + r) * H + h] : 0.f;
+  }
+  __syncthreads();
+  if (g_role) {
+    float off[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < gs; ++s2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) off[e] += sTot[s2][gc0 + e];
+#pragma unroll
+    for (int r = 0; r < TS; ++r)
+      *reinterpret_cast<f32x4*>(&sG[gs * TS + r][gc0]) =
+          f32x4{gacc[r][0] + off[0], gacc[r][1] + off[1], gacc[r][2] + off[2], gacc[r][3] + off[3]};
   }
   __syncthreads();
 
-  // ---- 2. L2 normalisation of q~ and k~, 8 threads per token -------------
-  if (do_l2 && tid < 8 * C) {
-    const int r = tid / 8, part = tid % 8;
-    float sq = 0.f, sk = 0.f;
-    for (int c = part; c < DK; c += 8) {
-      sq += sQ[r][c] * sQ[r][c];
-      sk += sK[r][c] * sK[r][c];
-    }
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) {
-      sq += __shfl_xor(sq, off, kWave);
-      sk += __shfl_xor(sk, off, kWave);
-    }
-    const float iq = 1.0f / sqrtf(sq + kL2Eps), ik = 1.0f / sqrtf(sk + kL2Eps);
-    for (int c = part; c < DK; c += 8) {
-      sQ[r][c] *= iq;
-      sK[r][c] *= ik;
-    }
-  }
-  __syncthreads();
-
-  // ---- 3. A (beta-scaled, strictly lower) to LDS and P (lower) to the
+  // ---- 2. A (beta-scaled, strictly lower) to LDS and P (lower) to the
   //         workspace, one 16x16 tile (a, bc <= a) per wave at a time --------
   {
     constexpr int NKS = DKP / KS;
@@ -245,18 +338,26 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
       f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
+        const int c0 = ks * KS + g16 * KPL;
         float vk[KPL], vq[KPL], vc[KPL];
+        if (c0 < DK) {
+          float gr[KPL], gm[KPL], gj[KPL];
+          lds_rd(&sG[r][c0], gr);
+          lds_rd(&sG[m][c0], gm);
+          lds_rd(&sG[j][c0], gj);
+          lds_rd(&sK[r][c0], vk);
+          lds_rd(&sQ[r][c0], vq);
+          lds_rd(&sK[j][c0], vc);
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-          const int c = ks * KS + g16 * KPL + e;
-          vk[e] = vq[e] = vc[e] = 0.f;
-          if (c < DK) {
-            const float gm = sG[m][c];
-            const float ex = __expf(sG[r][c] - gm);
-            vk[e] = sK[r][c] * ex;
-            vq[e] = sQ[r][c] * ex;
-            vc[e] = sK[j][c] * __expf(gm - sG[j][c]);
+          for (int e = 0; e < KPL; ++e) {
+            const float ex = __expf(gr[e] - gm[e]);
+            vk[e] *= ex;
+            vq[e] *= ex;
+            vc[e] *= __expf(gm[e] - gj[e]);
           }
+        } else {
+#pragma unroll
+          for (int e = 0; e < KPL; ++e) vk[e] = vq[e] = vc[e] = 0.f;
         }
         const frag fc = M::mk(vc);
         accA = M::mma(M::mk(vk), fc, accA);
@@ -278,27 +379,31 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
       }
     }
   }
-  __syncthreads();
 
-  // ---- 4. Q~ and K^^T (fragment-major) and e^{Gam_n} to the workspace ----
+  // ---- 3. Q~ and K^^T (fragment-major) and e^{Gam_n} to the workspace ----
   {
-    constexpr int NQ = C * DKP / KPL;   // lane pieces of Q~
+    constexpr int NPQ = C * DKP / KPL;   // lane pieces of Q~
 #pragma unroll 1
-    for (int pc = tid; pc < NQ; pc += kPrepNT) {
+    for (int pc = tid; pc < NPQ; pc += kPrepNT) {
       const int ln = pc % kWave, frg = pc / kWave;
       const int rb = frg / (DKP / KS), ks = frg % (DKP / KS);
       const int r = 16 * rb + ln % 16, c0 = ks * KS + (ln / 16) * KPL;
       float v[KPL];
+      if (c0 < DK) {
+        float gq[KPL];
+        lds_rd(&sG[r][c0], gq);
+        lds_rd(&sQ[r][c0], v);
 #pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        const int c = c0 + e;
-        v[e] = c < DK ? __expf(sG[r][c]) * sQ[r][c] : 0.f;
+        for (int e = 0; e < KPL; ++e) v[e] *= __expf(gq[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) v[e] = 0.f;
       }
       M::st(blk + L::oQ + (size_t)pc * KPL, M::mk(v));
     }
-    constexpr int NKP = DK * CP / KPL;  // lane pieces of K^^T
+    constexpr int NPK = DK * CP / KPL;  // lane pieces of K^^T
 #pragma unroll 1
-    for (int pc = tid; pc < NKP; pc += kPrepNT) {
+    for (int pc = tid; pc < NPK; pc += kPrepNT) {
       const int ln = pc % kWave, frg = pc / kWave;
       const int rb = frg / (CP / KS), ks = frg % (CP / KS);
       const int c = 16 * rb + ln % 16, j0 = ks * KS + (ln / 16) * KPL;
@@ -314,14 +419,20 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
     if (tid < DK) Dn[tid] = __expf(sG[C - 1][tid]);
   }
   __syncthreads();
-  // k^ -> beta e^{Gam} k^ (the right-hand side of W); Gam is dead after this
-  for (int idx = tid; idx < C * DK; idx += kPrepNT) {
-    const int r = idx / DK, c = idx % DK;
-    sK[r][c] *= sB[r] * __expf(sG[r][c]);
+  // (beta e^{Gam} k^)^T into the q^ region: the B operand of W
+  for (int idx = tid; idx < DK * (CP / 8); idx += kPrepNT) {
+    const int c = idx / (CP / 8), j0 = 8 * (idx % (CP / 8));
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int jj = j0 + e;
+      v[e] = jj < C ? sB[jj] * __expf(sG[jj][c]) * sK[jj][c] : 0.f;
+    }
+    st8(&sKT[c][j0], v);
   }
   __syncthreads();
 
-  // ---- 5. X = (I + L)^{-1}, L = beta * strict_lower(A), in 16x16 blocks --
+  // ---- 4. X = (I + L)^{-1}, L = beta * strict_lower(A), in 16x16 blocks --
   //  diagonal blocks: forward substitution, one lane per column;
   //  X_ab = -X_aa * sum_{c=b}^{a-1} L_ac X_cb, by block distance a - b,
   //  on fp32 MFMA.
@@ -363,38 +474,33 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
     }
     __syncthreads();
   }
+  // X in the MFMA operand type, zero-padded to CP columns
+  for (int idx = tid; idx < C * (CP / 8); idx += kPrepNT) {
+    const int r = idx / (CP / 8), j0 = 8 * (idx % (CP / 8));
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = j0 + e < C ? sX[r][j0 + e] : 0.f;
+    st8(&sXb[r][j0], v);
+  }
+  __syncthreads();
 
-  // ---- 6. W = X (beta e^Gam K) and U' = X (beta V) on MFMA ---------------
+  // ---- 5. W = X (beta e^Gam K) and U' = X (beta V) on MFMA ---------------
   {
     constexpr int NCBW = DK / 16, NCBU = DV / 16;
     constexpr int NKC = CP / KS;
     for (int cbk = wv; cbk < NCBW + NCBU; cbk += kPrepNW) {
       const bool isw = cbk < NCBW;
       const int col = (isw ? cbk : cbk - NCBW) * 16 + l16;
+      const MT* brow = isw ? &sKT[col][0] : &sVT[col][0];
       frag fb[NKC];
 #pragma unroll
-      for (int ks = 0; ks < NKC; ++ks) {
-        float v[KPL];
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-          const int jj = ks * KS + g16 * KPL + e;
-          v[e] = jj < C ? (isw ? sK[jj][col] : sB[jj] * to_f32(sV[jj][col])) : 0.f;
-        }
-        fb[ks] = M::mk(v);
-      }
+      for (int ks = 0; ks < NKC; ++ks) fb[ks] = M::ld(brow + ks * KS + g16 * KPL);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKC; ++ks) {
-          float v[KPL];
-#pragma unroll
-          for (int e = 0; e < KPL; ++e) {
-            const int jj = ks * KS + g16 * KPL + e;
-            v[e] = jj < C ? sX[16 * rb + l16][jj] : 0.f;
-          }
-          acc = M::mma(M::mk(v), fb[ks], acc);
-        }
+        for (int ks = 0; ks < NKC; ++ks)
+          acc = M::mma(M::ld(&sXb[16 * rb + l16][ks * KS + g16 * KPL]), fb[ks], acc);
         if (isw) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) sWst[16 * rb + 4 * g16 + e][col] = (MT)(-acc[e]);
@@ -413,9 +519,9 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
   __syncthreads();
   // -W, fragment-major
   {
-    constexpr int NQ = C * DKP / KPL;
+    constexpr int NPW = C * DKP / KPL;
 #pragma unroll 1
-    for (int pc = tid; pc < NQ; pc += kPrepNT) {
+    for (int pc = tid; pc < NPW; pc += kPrepNT) {
       const int ln = pc % kWave, frg = pc / kWave;
       const int rb = frg / (DKP / KS), ks = frg % (DKP / KS);
       const int r = 16 * rb + ln % 16, c0 = ks * KS + (ln / 16) * KPL;
@@ -424,7 +530,6 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
   }
 }
 
-// ---------------------------------------------------------------------------
 // chain: one workgroup of 256 threads per (dv-block, head, sequence) walks the
 // chunks in order. Wave w owns the U/O row blocks w, w+4, ... and the S row
 // blocks w, w+4, ... (all column tiles of the dv-block). The next chunk's
@@ -476,8 +581,12 @@ __global__ __launch_bounds__(kChainNT) void prefill_chain_kernel(PrefillArgs a, 
 
   struct Frags {
     frag w[RU][NKS], q[RU][NKS], p[RU][NKP], k[RS][NKP];
-    f32x4 u[RU][NCB], dn[RS];
+    typename M::quad u[RU][NCB];
+    f32x4 dn[RS];
   };
+  // row-block guards that are compile-time true when the tiling divides
+  auto u_ok = [&](int rb) { return (NRU % NW == 0) || rb < NRU; };
+  auto s_ok = [&](int rb) { return (NRS % NW == 0) || rb < NRS; };
   auto load = [&](Frags& f, int cl) {
     const MT* blk =
         reinterpret_cast<const MT*>(ws + ((size_t)cl * B * H + (size_t)b * H + h) * L::bytes);
@@ -485,7 +594,7 @@ __global__ __launch_bounds__(kChainNT) void prefill_chain_kernel(PrefillArgs a, 
 #pragma unroll
     for (int i = 0; i < RU; ++i) {
       const int rb = wv + NW * i;
-      if (rb < NRU) {
+      if (u_ok(rb)) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           f.w[i][ks] = M::ld(blk + L::oW + ((size_t)(rb * NKS + ks) * kWave + lane) * KPL);
@@ -495,18 +604,15 @@ __global__ __launch_bounds__(kChainNT) void prefill_chain_kernel(PrefillArgs a, 
         for (int ks = 0; ks < NKP; ++ks)
           f.p[i][ks] = M::ld(blk + L::oP + (size_t)(16 * rb + l16) * CP + ks * KS + koff);
 #pragma unroll
-        for (int ct = 0; ct < NCB; ++ct) {
-          const MT* up = blk + L::oU +
-                         ((size_t)(rb * (DV / 16) + cb0 / 16 + ct) * kWave + lane) * 4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f.u[i][ct][e] = to_f32(up[e]);
-        }
+        for (int ct = 0; ct < NCB; ++ct)
+          f.u[i][ct] = M::ld4(blk + L::oU +
+                              ((size_t)(rb * (DV / 16) + cb0 / 16 + ct) * kWave + lane) * 4);
       }
     }
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
       const int rb = wv + NW * i;
-      if (rb < NRS) {
+      if (s_ok(rb)) {
 #pragma unroll
         for (int ks = 0; ks < NKP; ++ks)
           f.k[i][ks] = M::ld(blk + L::oK + ((size_t)(rb * NKP + ks) * kWave + lane) * KPL);
@@ -523,20 +629,15 @@ __global__ __launch_bounds__(kChainNT) void prefill_chain_kernel(PrefillArgs a, 
 #pragma unroll
     for (int ct = 0; ct < NCB; ++ct) {
       accS[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (rb < NRS) {
+      if (s_ok(rb)) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           accS[i][ct][e] = Sg[(long)(16 * rb + r4 + e) * DV + 16 * ct + l16];
       }
     }
   }
-  Frags cur;
-  load(cur, 0);
-  __syncthreads();
-
-  for (int cl = 0; cl < ncs; ++cl) {
-    Frags nxt = cur;
-    if (cl + 1 < ncs) load(nxt, cl + 1);
+  // One chunk of the chain with the operands in `cur`.
+  auto step = [&](const Frags& cur, int cl) {
     const int tstart = t0 + cl * C;
     const int n = min(C, T - tstart);
 
@@ -544,7 +645,7 @@ __global__ __launch_bounds__(kChainNT) void prefill_chain_kernel(PrefillArgs a, 
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
       const int rb = wv + NW * i;
-      if (rb < NRS) {
+      if (s_ok(rb)) {
 #pragma unroll
         for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
@@ -561,8 +662,8 @@ __global__ __launch_bounds__(kChainNT) void prefill_chain_kernel(PrefillArgs a, 
 #pragma unroll
       for (int ct = 0; ct < NCB; ++ct) {
         accO[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (rb < NRU) {
-          f32x4 accU = cur.u[i][ct];
+        if (u_ok(rb)) {
+          f32x4 accU = M::cvt4(cur.u[i][ct]);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const frag fs = M::ld(&sST[16 * ct + l16][ks * KS + koff]);
@@ -576,31 +677,32 @@ __global__ __launch_bounds__(kChainNT) void prefill_chain_kernel(PrefillArgs a, 
     }
     __syncthreads();
 
-    // (iii) O += P U (stored), S = Diag(e^{Gam_n}) S + K^^T U
+    // (iii) O += P U (stored), S = Diag(e^{Gam_n}) S + K^^T U. Rows past
+    // the chunk's last token fall outside the store resource and are dropped.
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(static_cast<IO*>(a.o) + (((long)b * T + tstart) * H + h) * DV + cb0,
+                  n * H * DV * (int)sizeof(IO));
 #pragma unroll
     for (int i = 0; i < RU; ++i) {
       const int rb = wv + NW * i;
-      if (rb < NRU) {
+      if (u_ok(rb)) {
 #pragma unroll
         for (int ct = 0; ct < NCB; ++ct) {
 #pragma unroll
           for (int ks = 0; ks < NKP; ++ks)
             accO[i][ct] = M::mma(cur.p[i][ks], M::ld(&sUT[16 * ct + l16][ks * KS + koff]),
                                  accO[i][ct]);
-          IO* op = static_cast<IO*>(a.o) + (((long)b * T + tstart) * H + h) * DV + cb0 +
-                   16 * ct + l16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rb + r4 + e;
-            if (r < n) op[(long)r * H * DV] = from_f32<IO>(accO[i][ct][e]);
-          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e)
+            buf_store(orsrc, ((16 * rb + r4 + e) * H * DV + 16 * ct + l16) * (int)sizeof(IO),
+                      accO[i][ct][e], (IO*)nullptr);
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
       const int rb = wv + NW * i;
-      if (rb < NRS) {
+      if (s_ok(rb)) {
 #pragma unroll
         for (int ct = 0; ct < NCB; ++ct) {
 #pragma unroll
@@ -612,13 +714,27 @@ __global__ __launch_bounds__(kChainNT) void prefill_chain_kernel(PrefillArgs a, 
         }
       }
     }
-    cur = nxt;
+  };
+  // Two named operand sets, alternated by a 2x unrolled loop: the loads of
+  // chunk c+1 are issued before chunk c runs and waited for only at their
+  // first use (no register copies, no wait on the chunk's own stores).
+  Frags f0, f1;
+  load(f0, 0);
+  __syncthreads();
+  // (Prefetch indices are clamped rather than branched on, so that the
+  // loads are unconditional and the wait counts stay exact.)
+  for (int cl = 0; cl < ncs; cl += 2) {
+    load(f1, min(cl + 1, ncs - 1));
+    step(f0, cl);
+    if (cl + 1 >= ncs) break;
+    load(f0, min(cl + 2, ncs - 1));
+    step(f1, cl + 1);
   }
 
 #pragma unroll
   for (int i = 0; i < RS; ++i) {
     const int rb = wv + NW * i;
-    if (rb < NRS) {
+    if (s_ok(rb)) {
 #pragma unroll
       for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
