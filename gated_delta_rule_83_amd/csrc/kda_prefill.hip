@@ -37,6 +37,9 @@ struct MmaBf16 {
   static constexpr int KS = 32, KPL = 8;
   __device__ static frag ld(const T* p) { return *reinterpret_cast<const frag*>(p); }
   __device__ static void st(T* p, frag f) { *reinterpret_cast<frag*>(p) = f; }
+  __device__ static void st4(T* p, f32x4 v) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  }
   using quad = bf16x4;  // four elements as loaded (converted at first use)
   __device__ static quad ld4(const T* p) { return *reinterpret_cast<const quad*>(p); }
   __device__ static f32x4 cvt4(quad v) {
@@ -60,6 +63,7 @@ struct MmaF32 {
   static constexpr int KS = 4, KPL = 1;
   __device__ static frag ld(const T* p) { return *p; }
   __device__ static void st(T* p, frag f) { *p = f; }
+  __device__ static void st4(T* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
   using quad = f32x4;
   __device__ static quad ld4(const T* p) { return *reinterpret_cast<const quad*>(p); }
   __device__ static f32x4 cvt4(quad v) { return v; }
@@ -100,25 +104,12 @@ constexpr size_t ws_block_bytes(int C, int DK, int DV, int KS, size_t esz) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: one workgroup of 512 threads per (chunk, head, sequence).
+// prep: one workgroup of 512 threads per (chunk, head, sequence) item.
+// (A persistent variant that loaded the next item's inputs into registers
+// during the current item was measured: the loop-carried registers spill and
+// the gain was small.)
 constexpr int kPrepNT = 512;
 constexpr int kPrepNW = kPrepNT / kWave;
-
-// Eight consecutive elements of the token I/O type, as one or two 16-byte loads.
-template <typename IO> struct Vec8;
-template <> struct Vec8<bf16> {
-  bf16x8 v;
-  __device__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
-  __device__ float operator[](int e) const { return (float)v[e]; }
-};
-template <> struct Vec8<float> {
-  f32x4 lo, hi;
-  __device__ void load(const float* p) {
-    lo = reinterpret_cast<const f32x4*>(p)[0];
-    hi = reinterpret_cast<const f32x4*>(p)[1];
-  }
-  __device__ float operator[](int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
-};
 
 // n consecutive fp32 LDS values (16-byte aligned when n is a multiple of 4)
 template <int N>
@@ -147,389 +138,519 @@ __device__ __forceinline__ void st8(float* p, const float* v) {
   reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
 }
 
+// Eight values of one channel row of a transposed tile, held in registers in
+// the operand type until written as one (bf16) or two (fp32) 16-byte pieces.
+template <typename MT> struct VTile;
+template <> struct VTile<bf16> {
+  using type = bf16x8;
+  __device__ static void set(type& t, int i, float v) { t[i] = (bf16)v; }
+  __device__ static void store(bf16* p, const type& t) { *reinterpret_cast<bf16x8*>(p) = t; }
+};
+template <> struct VTile<float> {
+  struct type { float v[8]; };
+  __device__ static void set(type& t, int i, float v) { t.v[i] = v; }
+  __device__ static void store(float* p, const type& t) { st8(p, t.v); }
+};
+
+// Eight consecutive token elements as 16-byte pieces: one for bf16, two for fp32.
+template <typename IO> struct Tok8 {
+  static constexpr int NP = sizeof(IO) == 2 ? 1 : 2;  // 16-byte pieces per 8 elements
+  __device__ static void load(const IO* p, f32x4* dst) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) dst[i] = reinterpret_cast<const f32x4*>(p)[i];
+  }
+  __device__ static float get(const f32x4* src, int e) {
+    if constexpr (sizeof(IO) == 2) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, src[0]);
+      return (float)v[e];
+    } else {
+      return src[e / 4][e % 4];
+    }
+  }
+};
+
 template <int C, int DK, int DV, typename IO, class M>
 struct PrepSmem {
   using MT = typename M::T;
   static constexpr int DKP = rup(DK, M::KS), CP = rup(C, M::KS);
-  static constexpr int LDK = DK + 4, LDC = C + 4;                      // fp32 row strides
-  static constexpr int LDT = CP + (sizeof(MT) == 2 ? 8 : 4);           // MT rows over tokens
-  static constexpr int TS = 16, NSTRIP = C / TS;                       // token strips
+  static constexpr int NRB = C / 16;
+  static constexpr int LDK = DK + 4, LDC = C + 4;                 // fp32 row strides
+  static constexpr int LDT = CP + (sizeof(MT) == 2 ? 8 : 0);      // MT rows over tokens
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-  // region Q: q^ (fp32), later (beta e^Gam k^)^T as MT [DK][LDT]
+  // Q: q^ (fp32), later (beta e^Gam k^)^T as MT [DK][LDT]
   static constexpr size_t oQ = 0, nQ = mx((size_t)C * LDK * 4, (size_t)DK * LDT * sizeof(MT));
-  // region K: k^ (fp32), later -W staging as MT [C][DKP]
-  static constexpr size_t oK = oQ + nQ, nK = mx((size_t)C * LDK * 4, (size_t)C * DKP * sizeof(MT));
-  // region G: Gam (fp32), later X (fp32 [C][LDC]) followed by X as MT [C][LDT]
-  static constexpr size_t oG = oK + nK;
-  static constexpr size_t oXb = oG + (size_t)C * LDC * 4;
-  static constexpr size_t nG = mx((size_t)C * LDK * 4, (size_t)C * LDC * 4 + (size_t)C * LDT * sizeof(MT));
-  static constexpr size_t oL = oG + nG;                              // beta*strict_lower(A)
-  static constexpr size_t oV = oL + (size_t)C * LDC * 4;             // (beta v^)^T as MT [DV][LDT]
+  // K: k^ (fp32), later -W staging as MT [C][LDW] (rows padded by 16 bytes so
+  // that the 16 rows of a fragment read fall in different LDS banks)
+  static constexpr int LDW = DKP + 16 / (int)sizeof(MT);
+  static constexpr size_t oK = oQ + nQ, nK = mx((size_t)C * LDK * 4, (size_t)C * LDW * sizeof(MT));
+  // R: e^{Gam_r - Gam_m(r)} (fp32), later X (fp32 [C][LDC]) then X as MT [C][LDT]
+  static constexpr size_t oR = oK + nK;
+  static constexpr size_t oXb = oR + (size_t)C * LDC * 4;
+  static constexpr size_t nR = mx((size_t)C * LDK * 4, (size_t)C * LDC * 4 + (size_t)C * LDT * sizeof(MT));
+  // L: beta * strict_lower(A) (fp32 [C][LDC]); before that, the g strip sums
+  static constexpr size_t oL = oR + nR;
+  static constexpr size_t nL = mx((size_t)C * LDC * 4, (size_t)2 * NRB * DK * 4);
+  static constexpr size_t oV = oL + nL;                              // (beta v^)^T as MT [DV][LDT]
   static constexpr size_t oB = oV + (size_t)DV * LDT * sizeof(MT);   // beta [C]
-  static constexpr size_t oT = oB + (size_t)C * 4;                   // strip totals of g
-  static constexpr size_t bytes = oT + (size_t)NSTRIP * DK * 4;
+  // block decays: EB[a] = e^{Gam_16a}, EN[a] = e^{Gam_{C-1} - Gam_16a},
+  // BT[a][b] = e^{Gam_16a - Gam_16b} for b < a
+  static constexpr size_t oE = oB + (size_t)C * 4;
+  static constexpr int NBT = NRB * (NRB - 1) / 2;
+  static constexpr size_t bytes = oE + (size_t)(2 * NRB + NBT) * DK * 4;
   static_assert(bytes <= 160 * 1024, "prep LDS exceeds 160 KiB");
-  static_assert(C % TS == 0, "chunk must be a multiple of the token strip");
 };
 
-template <int C, int DK, int DV, typename IO, class M>
-__global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, int t0,
+// thread roles of the load/activation phase
+template <int C, int DK, int DV, typename IO>
+struct PrepRoles {
+  static constexpr int QS = 8;                         // tokens per q/k/v strip
+  static constexpr int NQ = (DK / 8) * (C / QS);       // q threads (8 channels x 8 tokens)
+  static constexpr int NV = (DV / 8) * (C / QS);       // v threads
+  static constexpr int GS = 16;                        // tokens per g strip (= one 16-row block)
+  static constexpr int NG = (DK / 4) * (C / GS);       // g threads (4 channels x 16 tokens)
+  static constexpr int QB = (QS + 3) * Tok8<IO>::NP;   // 16-byte pieces per q/k/v thread
+  static constexpr int NBUF = QB > GS ? QB : GS;
+  static_assert(2 * NQ + NV + NG <= kPrepNT, "not enough threads for the load roles");
+};
+
+// CONV: the short convolution is applied (a compile-time switch, so that the
+// unrolled activation loop carries no branches).
+template <int C, int DK, int DV, typename IO, class M, bool CONV>
+__global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, int t0, int ncs,
                                                                uint8_t* ws) {
   using L = Ws<C, DK, DV, M>;
   using SM = PrepSmem<C, DK, DV, IO, M>;
+  using RO = PrepRoles<C, DK, DV, IO>;
   using MT = typename M::T;
   using frag = typename M::frag;
   constexpr int LDK = SM::LDK, LDC = SM::LDC, LDT = SM::LDT;
   constexpr int DKP = L::DKP, CP = L::CP;
   constexpr int NRB = C / 16;
   constexpr int KS = M::KS, KPL = M::KPL;
-  constexpr int TS = SM::TS, NSTRIP = SM::NSTRIP;
-  constexpr int CGK = DK / 8, CGV = DV / 8, CG4 = DK / 4;
-  constexpr int NQ = CGK * NSTRIP, NV = CGV * NSTRIP, NG = CG4 * NSTRIP;
-  static_assert(2 * NQ + NV + NG + C <= kPrepNT, "not enough threads for the load roles");
+  constexpr int QS = RO::QS, GS = RO::GS, NQ = RO::NQ, NV = RO::NV, NG = RO::NG;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SM::bytes];
   float (*sQ)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oQ);
   MT (*sKT)[LDT] = reinterpret_cast<MT (*)[LDT]>(smem + SM::oQ);
   float (*sK)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oK);
-  MT (*sWst)[DKP] = reinterpret_cast<MT (*)[DKP]>(smem + SM::oK);
-  float (*sG)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oG);
-  float (*sX)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oG);
+  MT (*sWst)[SM::LDW] = reinterpret_cast<MT (*)[SM::LDW]>(smem + SM::oK);
+  float (*sR)[LDK] = reinterpret_cast<float (*)[LDK]>(smem + SM::oR);
+  float (*sX)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oR);
   MT (*sXb)[LDT] = reinterpret_cast<MT (*)[LDT]>(smem + SM::oXb);
   float (*sL)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oL);
+  float (*sTot)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oL);
+  float (*sFirst)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oL + (size_t)NRB * DK * 4);
   MT (*sVT)[LDT] = reinterpret_cast<MT (*)[LDT]>(smem + SM::oV);
   float* sB = reinterpret_cast<float*>(smem + SM::oB);
-  float (*sTot)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oT);
+  float (*sEB)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oE);
+  float (*sEN)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oE + (size_t)NRB * DK * 4);
+  float (*sBT)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oE + (size_t)2 * NRB * DK * 4);
 
-  const int cl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int l16 = lane % 16, g16 = lane / 16;
   const int H = a.H, T = a.T;
-  const int tstart = t0 + cl * C;
-  const int n = min(C, T - tstart);
-  MT* blk = reinterpret_cast<MT*>(ws + ((size_t)cl * a.B * H + (size_t)b * H + h) * L::bytes);
-  float* Dn = reinterpret_cast<float*>(blk + L::nT);
   const long ctot = (long)H * (2 * DK + DV);
-  const bool do_conv = !(a.flags & KDA_F_SKIP_CONV);
   const bool do_l2 = !(a.flags & KDA_F_SKIP_L2);
+  const int nitems = ncs * H * a.B;
 
-  // token-padding columns of the MT operand tiles are zero (only when the
-  // chunk is shorter than the MFMA depth)
+  // role of this thread in the load/activation phase
+  // 0: q, 1: k, 2: v (8 channels x 8 tokens), 3: g (4 channels x 16 tokens), 4: none
+  const int role = tid < NQ ? 0 : (tid < 2 * NQ ? 1 : (tid < 2 * NQ + NV ? 2 : (tid < 2 * NQ + NV + NG ? 3 : 4)));
+  const int rt = tid - (role == 0 ? 0 : role == 1 ? NQ : role == 2 ? 2 * NQ : 2 * NQ + NV);
+  // q, k: channel group fastest (the lanes of one token form a group for the
+  // L2 shuffle); v: token strip fastest (the lanes of one channel row write
+  // adjacent 16-byte pieces of the transposed tile)
+  const int cgn = DK / 8, nst = C / QS;
+  const int qc0 = role == 2 ? 8 * (rt / nst) : 8 * (rt % cgn);
+  const int qr0 = role == 2 ? QS * (rt % nst) : QS * (rt / cgn);
+  const int gc0 = 4 * (rt % (DK / 4)), gs = rt / (DK / 4);  // g: first channel, strip
+  const int dproj = role == 2 ? DV : DK;
+  const long chan0 = (role == 0 ? 0L : (role == 1 ? (long)H * DK : 2L * H * DK)) + qc0;
+  const IO* xproj = static_cast<const IO*>(role == 0 ? a.q : (role == 1 ? a.k : a.v));
+
+  // token-padding columns of the (beta v^)^T tile (when the chunk is shorter
+  // than the MFMA depth) are never written per item: zero them once
   if constexpr (CP > C) {
     for (int idx = tid; idx < DV * (CP - C); idx += kPrepNT)
       sVT[idx / (CP - C)][C + idx % (CP - C)] = (MT)0.f;
   }
 
-  // ---- 1. all global inputs of the chunk, 16-byte loads ------------------
-  // q, k, v threads: 8 channels x a strip of 16 tokens (+ the 3 raw tokens
-  // before it, from the ring at the sequence start) -> conv, SiLU, and for
-  // q, k the L2 norm by an xor-shuffle over the lanes that share the token.
-  // g threads: 4 channels x 16 tokens -> strip-local prefix sums of g.
-  float gacc[TS][4];
-  int gs = 0, gc0 = 0;
-  const bool g_role = tid >= 2 * NQ + NV && tid < 2 * NQ + NV + NG;
-  if (tid < 2 * NQ + NV) {
-    const int p = tid < NQ ? 0 : (tid < 2 * NQ ? 1 : 2);
-    const int t = tid - (p == 0 ? 0 : (p == 1 ? NQ : 2 * NQ));
-    const int CG = p == 2 ? CGV : CGK;
-    const int d = p == 2 ? DV : DK;
-    const int cg = t % CG, s = t / CG;
-    const int c0 = 8 * cg, r0 = s * TS;
-    const IO* x = static_cast<const IO*>(p == 0 ? a.q : (p == 1 ? a.k : a.v));
-    const long chan0 = (p == 0 ? 0L : (p == 1 ? (long)H * DK : 2L * H * DK)) + (long)h * d + c0;
-    const IO* ring = static_cast<const IO*>(a.ring) + (long)b * 3 * ctot + chan0;
-    const IO* xc = x + ((long)b * T * H + h) * d + c0;   // token 0, channel c0
-    const long ts = (long)H * d;
-    Vec8<IO> raw[TS + 3];
+  f32x4 buf[RO::NBUF];  // raw inputs of the item being loaded
+  auto issue_loads = [&](int item) {
+    const int cl = item % ncs, h = (item / ncs) % H, b = item / (ncs * H);
+    const int tstart = t0 + cl * C;
+    if (role <= 2) {
+      const IO* xc = xproj + ((long)b * T * H + h) * dproj + qc0;
+      const long ts = (long)H * dproj;  // token stride
+      const int tok0 = tstart + qr0 - 3;
+      if (tok0 >= 0 && tok0 + QS + 2 < T) {  // the whole window is inside the inputs
+        const IO* p = xc + (long)tok0 * ts;
 #pragma unroll
-    for (int i = 0; i < TS + 3; ++i) {
-      const int tok = tstart + r0 - 3 + i;
-      const int tcl = tok < T ? tok : T - 1;
-      const IO* src = tcl >= 0 ? xc + (long)tcl * ts : (do_conv ? ring + (long)(3 + tcl) * ctot : xc);
-      raw[i].load(src);
-    }
-    f32x4 w[8];
+        for (int i = 0; i < QS + 3; ++i, p += ts) Tok8<IO>::load(p, &buf[i * Tok8<IO>::NP]);
+      } else {  // history from the ring before token 0; clamped reads past T
+        const IO* ring = static_cast<const IO*>(a.ring) + (long)b * 3 * ctot + chan0 + (long)h * dproj;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      w[e] = do_conv ? *reinterpret_cast<const f32x4*>(a.conv_w + 4 * (chan0 + e))
-                     : f32x4{0.f, 0.f, 0.f, 1.f};
-    float bv[TS];
-    if (p == 2) {
-#pragma unroll
-      for (int r = 0; r < TS; ++r) {
-        const int tcl = min(tstart + r0 + r, T - 1);
-        bv[r] = a.beta[((long)b * T + tcl) * H + h];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < TS; ++r) {
-      const bool valid = r0 + r < n;
-      float y[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x3 = raw[r + 3][e];
-        const float v = do_conv ? silu(w[e].x * raw[r][e] + w[e].y * raw[r + 1][e] +
-                                       w[e].z * raw[r + 2][e] + w[e].w * x3)
-                                : x3;
-        y[e] = valid ? v : 0.f;
-      }
-      if (p < 2) {
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
-#pragma unroll
-        for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off, kWave);
-        const float inv = do_l2 ? 1.0f / sqrtf(ss + kL2Eps) : 1.0f;
-        float* dst = p == 0 ? &sQ[r0 + r][c0] : &sK[r0 + r][c0];
-        reinterpret_cast<f32x4*>(dst)[0] = f32x4{y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv};
-        reinterpret_cast<f32x4*>(dst)[1] = f32x4{y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv};
-      } else {
-        const float bb = valid ? bv[r] : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sVT[c0 + e][r0 + r] = (MT)(bb * y[e]);
-      }
-    }
-  } else if (g_role) {
-    const int t = tid - (2 * NQ + NV);
-    gc0 = 4 * (t % CG4);
-    gs = t / CG4;
-    const int r0 = gs * TS;
-#pragma unroll
-    for (int r = 0; r < TS; ++r) {
-      const int tcl = min(tstart + r0 + r, T - 1);
-      const f32x4 gv =
-          *reinterpret_cast<const f32x4*>(a.g + (((long)b * T + tcl) * H + h) * DK + gc0);
-      const bool valid = r0 + r < n;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gacc[r][e] = valid ? gv[e] : 0.f;
-    }
-#pragma unroll
-    for (int r = 1; r < TS; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gacc[r][e] += gacc[r - 1][e];
-    *reinterpret_cast<f32x4*>(&sTot[gs][gc0]) =
-        f32x4{gacc[TS - 1][0], gacc[TS - 1][1], gacc[TS - 1][2], gacc[TS - 1][3]};
-  } else if (tid < 2 * NQ + NV + NG + C) {
-    const int r = tid - (2 * NQ + NV + NG);
-    sB[r] = r < n ? a.beta[((long)b * T + tstart + r) * H + h] : 0.f;
-  }
-  __syncthreads();
-  if (g_role) {
-    float off[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < gs; ++s2)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) off[e] += sTot[s2][gc0 + e];
-#pragma unroll
-    for (int r = 0; r < TS; ++r)
-      *reinterpret_cast<f32x4*>(&sG[gs * TS + r][gc0]) =
-          f32x4{gacc[r][0] + off[0], gacc[r][1] + off[1], gacc[r][2] + off[2], gacc[r][3] + off[3]};
-  }
-  __syncthreads();
-
-  // ---- 2. A (beta-scaled, strictly lower) to LDS and P (lower) to the
-  //         workspace, one 16x16 tile (a, bc <= a) per wave at a time --------
-  {
-    constexpr int NKS = DKP / KS;
-    constexpr int NTILE = NRB * (NRB + 1) / 2;
-    for (int tile = wv; tile < NTILE; tile += kPrepNW) {
-      int arb = 0, rem = tile;
-      while (rem > arb) { rem -= arb + 1; ++arb; }
-      const int bc = rem;
-      const int m = 16 * arb, r = m + l16, j = 16 * bc + l16;
-      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int c0 = ks * KS + g16 * KPL;
-        float vk[KPL], vq[KPL], vc[KPL];
-        if (c0 < DK) {
-          float gr[KPL], gm[KPL], gj[KPL];
-          lds_rd(&sG[r][c0], gr);
-          lds_rd(&sG[m][c0], gm);
-          lds_rd(&sG[j][c0], gj);
-          lds_rd(&sK[r][c0], vk);
-          lds_rd(&sQ[r][c0], vq);
-          lds_rd(&sK[j][c0], vc);
-#pragma unroll
-          for (int e = 0; e < KPL; ++e) {
-            const float ex = __expf(gr[e] - gm[e]);
-            vk[e] *= ex;
-            vq[e] *= ex;
-            vc[e] *= __expf(gm[e] - gj[e]);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < KPL; ++e) vk[e] = vq[e] = vc[e] = 0.f;
+        for (int i = 0; i < QS + 3; ++i) {
+          const int tok = tok0 + i;
+          const int tcl = tok < T ? tok : T - 1;
+          const IO* src = tcl >= 0 ? xc + (long)tcl * ts
+                                   : (CONV ? ring + (long)(3 + tcl) * ctot : xc);
+          Tok8<IO>::load(src, &buf[i * Tok8<IO>::NP]);
         }
-        const frag fc = M::mk(vc);
-        accA = M::mma(M::mk(vk), fc, accA);
-        accP = M::mma(M::mk(vq), fc, accP);
       }
+    } else if (role == 3) {
+      const long ts = (long)H * DK;
+      const int tok0 = tstart + GS * gs;
+      const float* gb = a.g + ((long)b * T * H + h) * DK + gc0;
+      if (tok0 + GS - 1 < T) {
+        const float* p = gb + (long)tok0 * ts;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = m + 4 * g16 + e, jj = 16 * bc + l16;
-        sL[rr][jj] = jj < rr ? sB[rr] * accA[e] : 0.f;
-        blk[L::oP + (size_t)rr * CP + jj] = (MT)(jj <= rr ? accP[e] : 0.f);
-      }
-    }
-    // the upper tiles of L and P are zero; P's padding columns too
-    for (int idx = tid; idx < C * CP; idx += kPrepNT) {
-      const int rr = idx / CP, jj = idx % CP;
-      if (jj >= C || jj / 16 > rr / 16) {
-        blk[L::oP + idx] = (MT)0.f;
-        if (jj < C) sL[rr][jj] = 0.f;
-      }
-    }
-  }
-
-  // ---- 3. Q~ and K^^T (fragment-major) and e^{Gam_n} to the workspace ----
-  {
-    constexpr int NPQ = C * DKP / KPL;   // lane pieces of Q~
-#pragma unroll 1
-    for (int pc = tid; pc < NPQ; pc += kPrepNT) {
-      const int ln = pc % kWave, frg = pc / kWave;
-      const int rb = frg / (DKP / KS), ks = frg % (DKP / KS);
-      const int r = 16 * rb + ln % 16, c0 = ks * KS + (ln / 16) * KPL;
-      float v[KPL];
-      if (c0 < DK) {
-        float gq[KPL];
-        lds_rd(&sG[r][c0], gq);
-        lds_rd(&sQ[r][c0], v);
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) v[e] *= __expf(gq[e]);
+        for (int r = 0; r < GS; ++r, p += ts) buf[r] = *reinterpret_cast<const f32x4*>(p);
       } else {
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) v[e] = 0.f;
+        for (int r = 0; r < GS; ++r)
+          buf[r] = *reinterpret_cast<const f32x4*>(gb + (long)min(tok0 + r, T - 1) * ts);
       }
-      M::st(blk + L::oQ + (size_t)pc * KPL, M::mk(v));
     }
-    constexpr int NPK = DK * CP / KPL;  // lane pieces of K^^T
-#pragma unroll 1
-    for (int pc = tid; pc < NPK; pc += kPrepNT) {
-      const int ln = pc % kWave, frg = pc / kWave;
-      const int rb = frg / (CP / KS), ks = frg % (CP / KS);
-      const int c = 16 * rb + ln % 16, j0 = ks * KS + (ln / 16) * KPL;
-      const float gn = sG[C - 1][c];
-      float v[KPL];
-#pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        const int jj = j0 + e;
-        v[e] = jj < C ? __expf(gn - sG[jj][c]) * sK[jj][c] : 0.f;
-      }
-      M::st(blk + L::oK + (size_t)pc * KPL, M::mk(v));
-    }
-    if (tid < DK) Dn[tid] = __expf(sG[C - 1][tid]);
-  }
-  __syncthreads();
-  // (beta e^{Gam} k^)^T into the q^ region: the B operand of W
-  for (int idx = tid; idx < DK * (CP / 8); idx += kPrepNT) {
-    const int c = idx / (CP / 8), j0 = 8 * (idx % (CP / 8));
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int jj = j0 + e;
-      v[e] = jj < C ? sB[jj] * __expf(sG[jj][c]) * sK[jj][c] : 0.f;
-    }
-    st8(&sKT[c][j0], v);
-  }
-  __syncthreads();
+  };
 
-  // ---- 4. X = (I + L)^{-1}, L = beta * strict_lower(A), in 16x16 blocks --
-  //  diagonal blocks: forward substitution, one lane per column;
-  //  X_ab = -X_aa * sum_{c=b}^{a-1} L_ac X_cb, by block distance a - b,
-  //  on fp32 MFMA.
-  for (int idx = tid; idx < C * C; idx += kPrepNT) {
-    const int rr = idx / C, jj = idx % C;
-    if (jj / 16 > rr / 16) sX[rr][jj] = 0.f;
-  }
-  if (wv < NRB && lane < 16) {
-    const int m = 16 * wv, j = lane;
-    float x[16];
+  {
+    const int item = blockIdx.x;
+    if (item >= nitems) return;
+    issue_loads(item);
+    const int cl = item % ncs, h = (item / ncs) % H, b = item / (ncs * H);
+    const int tstart = t0 + cl * C;
+    const int n = min(C, T - tstart);
+    MT* blk = reinterpret_cast<MT*>(ws + ((size_t)cl * a.B * H + (size_t)b * H + h) * L::bytes);
+    float* Dn = reinterpret_cast<float*>(blk + L::nT);
+
+    // ---- 1a. activations from the raw inputs ---------------------------
+    if (role <= 2) {
+      f32x4 w[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = r == j ? 1.f : 0.f;
+      for (int e = 0; e < 8; ++e)
+        w[e] = CONV ? *reinterpret_cast<const f32x4*>(a.conv_w + 4 * (chan0 + (long)h * dproj + e))
+                       : f32x4{0.f, 0.f, 0.f, 1.f};
+      float bv[QS];
+      typename VTile<MT>::type vt[8];  // (beta v^) for 8 channels x 8 tokens
+      if (role == 2) {
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc -= sL[m + r][m + i] * x[i];
-      x[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sX[m + r][m + j] = x[r];
-  }
-  __syncthreads();
-  for (int dist = 1; dist < NRB; ++dist) {
-    if (wv < NRB - dist) {
-      const int ab = wv + dist, bb = wv;
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
-      for (int cb = bb; cb < ab; ++cb) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          y = mma_f32x4(sL[16 * ab + l16][16 * cb + 4 * s + g16],
-                        sX[16 * cb + 4 * s + g16][16 * bb + l16], y);
+        for (int r = 0; r < QS; ++r)
+          bv[r] = a.beta[((long)b * T + min(tstart + qr0 + r, T - 1)) * H + h];
       }
-      // X_aa * Y with the contraction index of step s taken as 4*(lane/16)+s:
-      // Y's rows are then exactly the accumulator elements each lane holds.
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) x = mma_f32x4(sX[16 * ab + l16][16 * ab + 4 * g16 + s], y[s], x);
+      for (int r = 0; r < QS; ++r) {
+        const bool valid = qr0 + r < n;
+        float y[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sX[16 * ab + 4 * g16 + e][16 * bb + l16] = -x[e];
+        for (int e = 0; e < 8; ++e) {
+          const float x3 = Tok8<IO>::get(&buf[(r + 3) * Tok8<IO>::NP], e);
+          const float v = CONV
+              ? silu(w[e].x * Tok8<IO>::get(&buf[r * Tok8<IO>::NP], e) +
+                     w[e].y * Tok8<IO>::get(&buf[(r + 1) * Tok8<IO>::NP], e) +
+                     w[e].z * Tok8<IO>::get(&buf[(r + 2) * Tok8<IO>::NP], e) + w[e].w * x3)
+              : x3;
+          y[e] = valid ? v : 0.f;
+        }
+        if (role < 2) {
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
+#pragma unroll
+          for (int off = 1; off < DK / 8; off <<= 1) ss += __shfl_xor(ss, off, kWave);
+          const float inv = do_l2 ? __builtin_amdgcn_rsqf(ss + kL2Eps) : 1.0f;
+          float* dst = role == 0 ? &sQ[qr0 + r][qc0] : &sK[qr0 + r][qc0];
+          reinterpret_cast<f32x4*>(dst)[0] = f32x4{y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv};
+          reinterpret_cast<f32x4*>(dst)[1] = f32x4{y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv};
+        } else {
+          const float bb = valid ? bv[r] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) VTile<MT>::set(vt[e], r, bb * y[e]);
+          if (qc0 == 0) sB[qr0 + r] = bb;  // beta, once per token
+        }
+      }
+      if (role == 2) {
+        static_assert(QS == 8, "v rows are written as 8-token pieces");
+#pragma unroll
+        for (int e = 0; e < 8; ++e) VTile<MT>::store(&sVT[qc0 + e][qr0], vt[e]);
+      }
+    } else if (role == 3) {
+      // strip-local inclusive prefix sums of g, parked in the R region
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < GS; ++r) {
+        const bool valid = GS * gs + r < n;
+        const f32x4 gv = valid ? buf[r] : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (r == 0) *reinterpret_cast<f32x4*>(&sFirst[gs][gc0]) = gv;
+        acc += gv;
+        *reinterpret_cast<f32x4*>(&sR[GS * gs + r][gc0]) = acc;
+      }
+      *reinterpret_cast<f32x4*>(&sTot[gs][gc0]) = acc;
     }
     __syncthreads();
-  }
-  // X in the MFMA operand type, zero-padded to CP columns
-  for (int idx = tid; idx < C * (CP / 8); idx += kPrepNT) {
-    const int r = idx / (CP / 8), j0 = 8 * (idx % (CP / 8));
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = j0 + e < C ? sX[r][j0 + e] : 0.f;
-    st8(&sXb[r][j0], v);
-  }
-  __syncthreads();
 
-  // ---- 5. W = X (beta e^Gam K) and U' = X (beta V) on MFMA ---------------
-  {
-    constexpr int NCBW = DK / 16, NCBU = DV / 16;
-    constexpr int NKC = CP / KS;
-    for (int cbk = wv; cbk < NCBW + NCBU; cbk += kPrepNW) {
-      const bool isw = cbk < NCBW;
-      const int col = (isw ? cbk : cbk - NCBW) * 16 + l16;
-      const MT* brow = isw ? &sKT[col][0] : &sVT[col][0];
-      frag fb[NKC];
+    // ---- 1b. Gam, R = e^{Gam_r - Gam_16a}, block decays, e^{Gam_n} -----
+    if (role == 3) {
+      float off[4] = {0.f, 0.f, 0.f, 0.f}, last[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int s2 = 0; s2 < NRB; ++s2)
 #pragma unroll
-      for (int ks = 0; ks < NKC; ++ks) fb[ks] = M::ld(brow + ks * KS + g16 * KPL);
+        for (int e = 0; e < 4; ++e) {
+          if (s2 < gs) off[e] += sTot[s2][gc0 + e];
+          last[e] += sTot[s2][gc0 + e];
+        }
+      // Gam at each block start m = 16*s2: sum of earlier strip totals + the
+      // first token's g of that strip
+      float gm[NRB][4];
+      float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s2 = 0; s2 < NRB; ++s2)
 #pragma unroll
-        for (int ks = 0; ks < NKC; ++ks)
-          acc = M::mma(M::ld(&sXb[16 * rb + l16][ks * KS + g16 * KPL]), fb[ks], acc);
-        if (isw) {
+        for (int e = 0; e < 4; ++e) {
+          gm[s2][e] = run[e] + sFirst[s2][gc0 + e];
+          run[e] += sTot[s2][gc0 + e];
+        }
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sR[GS * gs][gc0]);
+      const float g0[4] = {l0[0] + off[0], l0[1] + off[1], l0[2] + off[2], l0[3] + off[3]};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sWst[16 * rb + 4 * g16 + e][col] = (MT)(-acc[e]);
-        } else {
-          MT* dst = blk + L::oU + ((size_t)(rb * NCBU + (cbk - NCBW)) * kWave + lane) * 4;
+      for (int r = 0; r < GS; ++r) {
+        f32x4* rp = reinterpret_cast<f32x4*>(&sR[GS * gs + r][gc0]);
+        const f32x4 lr = *rp;
+        f32x4 rv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = (MT)acc[e];
+        for (int e = 0; e < 4; ++e) rv[e] = __expf(lr[e] - l0[e]);
+        *rp = rv;
+      }
+      f32x4 eb, en;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        eb[e] = __expf(g0[e]);
+        en[e] = __expf(last[e] - g0[e]);
+      }
+      *reinterpret_cast<f32x4*>(&sEB[gs][gc0]) = eb;
+      *reinterpret_cast<f32x4*>(&sEN[gs][gc0]) = en;
+      // BT[gs][b2] for b2 < gs, stored at pair index gs*(gs-1)/2 + b2
+#pragma unroll
+      for (int b2 = 0; b2 < NRB; ++b2) {
+        if (b2 < gs) {
+          f32x4 bt;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bt[e] = __expf(g0[e] - gm[b2][e]);
+          *reinterpret_cast<f32x4*>(&sBT[gs * (gs - 1) / 2 + b2][gc0]) = bt;
+        }
+      }
+      if (gs == 0) {
+        f32x4 dn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dn[e] = __expf(last[e]);
+        *reinterpret_cast<f32x4*>(Dn + gc0) = dn;
+      }
+    }
+    __syncthreads();
+
+    // ---- 2. A (beta-scaled, strictly lower) to LDS and P (lower) to the
+    //         workspace: tile (a, bc <= a) on MFMA with factors
+    //         k_r R_r and k_j / R_j * BT[a][bc] (both finite, see header) ----
+    {
+      constexpr int NKS = DKP / KS;
+      constexpr int NTILE = NRB * (NRB + 1) / 2;
+      for (int tile = wv; tile < NTILE; tile += kPrepNW) {
+        int arb = 0, rem = tile;
+        while (rem > arb) { rem -= arb + 1; ++arb; }
+        const int bc = rem;
+        const int r = 16 * arb + l16, j = 16 * bc + l16;
+        const float* bt = bc < arb ? &sBT[arb * (arb - 1) / 2 + bc][0] : nullptr;
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        // (unrolled by 2 only: fully unrolled, the LDS reads of all slices are
+        //  hoisted together and the registers spill)
+#pragma unroll 2
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int c0 = ks * KS + g16 * KPL;
+          float vk[KPL], vq[KPL], vc[KPL];
+          if (c0 < DK) {
+            float rr[KPL], rj[KPL];
+            lds_rd(&sR[r][c0], rr);
+            lds_rd(&sR[j][c0], rj);
+            lds_rd(&sK[r][c0], vk);
+            lds_rd(&sQ[r][c0], vq);
+            lds_rd(&sK[j][c0], vc);
+            float bv[KPL];
+            if (bt) lds_rd(bt + c0, bv);
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) {
+              vk[e] *= rr[e];
+              vq[e] *= rr[e];
+              vc[e] *= __builtin_amdgcn_rcpf(rj[e]) * (bt ? bv[e] : 1.f);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) vk[e] = vq[e] = vc[e] = 0.f;
+          }
+          const frag fc = M::mk(vc);
+          accA = M::mma(M::mk(vk), fc, accA);
+          accP = M::mma(M::mk(vq), fc, accP);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 16 * arb + 4 * g16 + e, jj = 16 * bc + l16;
+          sL[rr][jj] = jj < rr ? sB[rr] * accA[e] : 0.f;
+          blk[L::oP + (size_t)rr * CP + jj] = (MT)(jj <= rr ? accP[e] : 0.f);
+        }
+      }
+      for (int idx = tid; idx < C * CP; idx += kPrepNT) {
+        const int rr = idx / CP, jj = idx % CP;
+        if (jj >= C || jj / 16 > rr / 16) {
+          blk[L::oP + idx] = (MT)0.f;
+          if (jj < C) sL[rr][jj] = 0.f;
         }
       }
     }
-    if constexpr (DKP > DK) {
-      for (int idx = tid; idx < C * (DKP - DK); idx += kPrepNT)
-        sWst[idx / (DKP - DK)][DK + idx % (DKP - DK)] = (MT)0.f;
-    }
-  }
-  __syncthreads();
-  // -W, fragment-major
-  {
-    constexpr int NPW = C * DKP / KPL;
+
+    // ---- 3. Q~ = e^{Gam_16a} R q^ and K^^T = e^{Gam_n - Gam_16a} / R k^
+    //         (fragment-major) to the workspace ------------------------
+    {
+      constexpr int NPQ = C * DKP / KPL;
 #pragma unroll 1
-    for (int pc = tid; pc < NPW; pc += kPrepNT) {
-      const int ln = pc % kWave, frg = pc / kWave;
-      const int rb = frg / (DKP / KS), ks = frg % (DKP / KS);
-      const int r = 16 * rb + ln % 16, c0 = ks * KS + (ln / 16) * KPL;
-      M::st(blk + L::oW + (size_t)pc * KPL, M::ld(&sWst[r][c0]));
+      for (int pc = tid; pc < NPQ; pc += kPrepNT) {
+        const int ln = pc % kWave, frg = pc / kWave;
+        const int rb = frg / (DKP / KS), ks = frg % (DKP / KS);
+        const int r = 16 * rb + ln % 16, c0 = ks * KS + (ln / 16) * KPL;
+        float v[KPL];
+        if (c0 < DK) {
+          float rr[KPL], eb[KPL];
+          lds_rd(&sR[r][c0], rr);
+          lds_rd(&sEB[rb][c0], eb);
+          lds_rd(&sQ[r][c0], v);
+#pragma unroll
+          for (int e = 0; e < KPL; ++e) v[e] *= rr[e] * eb[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < KPL; ++e) v[e] = 0.f;
+        }
+        M::st(blk + L::oQ + (size_t)pc * KPL, M::mk(v));
+      }
+      constexpr int NPK = DK * CP / KPL;
+#pragma unroll 1
+      for (int pc = tid; pc < NPK; pc += kPrepNT) {
+        const int ln = pc % kWave, frg = pc / kWave;
+        const int rb = frg / (CP / KS), ks = frg % (CP / KS);
+        const int c = 16 * rb + ln % 16, j0 = ks * KS + (ln / 16) * KPL;
+        float v[KPL];
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          const int jj = j0 + e;
+          v[e] = jj < C ? sEN[jj / 16][c] * __builtin_amdgcn_rcpf(sR[jj][c]) * sK[jj][c] : 0.f;
+        }
+        M::st(blk + L::oK + (size_t)pc * KPL, M::mk(v));
+      }
+    }
+    __syncthreads();
+    // (beta e^{Gam} k^)^T = (beta e^{Gam_16a} R k^)^T into the q^ region
+    for (int idx = tid; idx < DK * (CP / 8); idx += kPrepNT) {
+      const int c = idx % DK, j0 = 8 * (idx / DK);  // lanes walk channels: no bank conflicts
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jj = j0 + e;
+        v[e] = jj < C ? sB[jj] * sEB[jj / 16][c] * sR[jj][c] * sK[jj][c] : 0.f;
+      }
+      st8(&sKT[c][j0], v);
+    }
+    __syncthreads();
+
+    // ---- 4. X = (I + L)^{-1} in 16x16 blocks ----------------------------
+    for (int idx = tid; idx < C * C; idx += kPrepNT) {
+      const int rr = idx / C, jj = idx % C;
+      if (jj / 16 > rr / 16) sX[rr][jj] = 0.f;
+    }
+    if (wv < NRB && lane < 16) {
+      const int m = 16 * wv, j = lane;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) acc -= sL[m + r][m + i] * x[i];
+        x[r] = acc;
+        __builtin_amdgcn_sched_barrier(0);  // one row of L in flight at a time
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sX[m + r][m + j] = x[r];
+    }
+    __syncthreads();
+    for (int dist = 1; dist < NRB; ++dist) {
+      if (wv < NRB - dist) {
+        const int ab = wv + dist, bb = wv;
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        for (int cb = bb; cb < ab; ++cb) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            y = mma_f32x4(sL[16 * ab + l16][16 * cb + 4 * s + g16],
+                          sX[16 * cb + 4 * s + g16][16 * bb + l16], y);
+        }
+        // X_aa * Y with the contraction index of step s taken as 4*(lane/16)+s:
+        // Y's rows are then exactly the accumulator elements each lane holds.
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x = mma_f32x4(sX[16 * ab + l16][16 * ab + 4 * g16 + s], y[s], x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sX[16 * ab + 4 * g16 + e][16 * bb + l16] = -x[e];
+      }
+      __syncthreads();
+    }
+    for (int idx = tid; idx < C * (CP / 8); idx += kPrepNT) {
+      const int r = idx / (CP / 8), j0 = 8 * (idx % (CP / 8));
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = j0 + e < C ? sX[r][j0 + e] : 0.f;
+      st8(&sXb[r][j0], v);
+    }
+    __syncthreads();
+
+    // ---- 5. W = X (beta e^Gam K) and U' = X (beta V) on MFMA ------------
+    {
+      constexpr int NCBW = DK / 16, NCBU = DV / 16;
+      constexpr int NKC = CP / KS;
+      for (int cbk = wv; cbk < NCBW + NCBU; cbk += kPrepNW) {
+        const bool isw = cbk < NCBW;
+        const int col = (isw ? cbk : cbk - NCBW) * 16 + l16;
+        const MT* brow = isw ? &sKT[col][0] : &sVT[col][0];
+        frag fb[NKC];
+#pragma unroll
+        for (int ks = 0; ks < NKC; ++ks) fb[ks] = M::ld(brow + ks * KS + g16 * KPL);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKC; ++ks)
+            acc = M::mma(M::ld(&sXb[16 * rb + l16][ks * KS + g16 * KPL]), fb[ks], acc);
+          if (isw) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sWst[16 * rb + 4 * g16 + e][col] = (MT)(-acc[e]);
+          } else {
+            MT* dst = blk + L::oU + ((size_t)(rb * NCBU + (cbk - NCBW)) * kWave + lane) * 4;
+            M::st4(dst, acc);
+          }
+        }
+      }
+      if constexpr (DKP > DK) {
+        for (int idx = tid; idx < C * (DKP - DK); idx += kPrepNT)
+          sWst[idx / (DKP - DK)][DK + idx % (DKP - DK)] = (MT)0.f;
+      }
+    }
+    __syncthreads();
+    {
+      constexpr int NPW = C * DKP / KPL;
+#pragma unroll 1
+      for (int pc = tid; pc < NPW; pc += kPrepNT) {
+        const int ln = pc % kWave, frg = pc / kWave;
+        const int rb = frg / (DKP / KS), ks = frg % (DKP / KS);
+        const int r = 16 * rb + ln % 16, c0 = ks * KS + (ln / 16) * KPL;
+        M::st(blk + L::oW + (size_t)pc * KPL, M::ld(&sWst[r][c0]));
+      }
     }
   }
 }
 
+// ---------------------------------------------------------------------------
 // chain: one workgroup of 256 threads per (dv-block, head, sequence) walks the
 // chunks in order. Wave w owns the U/O row blocks w, w+4, ... and the S row
 // blocks w, w+4, ... (all column tiles of the dv-block). The next chunk's
@@ -755,8 +876,13 @@ hipError_t run(const PrefillArgs& a, uint8_t* ws, size_t ws_bytes, hipStream_t s
   for (int c0 = 0; c0 < nchunks; c0 += seg) {
     const int ncs = nchunks - c0 < seg ? nchunks - c0 : seg;
     const int t0 = c0 * C;
-    hipLaunchKernelGGL((prefill_prep_kernel<C, DK, DV, IO, M>), dim3(ncs, a.H, a.B),
-                       dim3(kPrepNT), 0, st, a, t0, ws);
+    const long items = (long)ncs * a.H * a.B;
+    if (a.flags & KDA_F_SKIP_CONV)
+      hipLaunchKernelGGL((prefill_prep_kernel<C, DK, DV, IO, M, false>), dim3((unsigned)items),
+                         dim3(kPrepNT), 0, st, a, t0, ncs, ws);
+    else
+      hipLaunchKernelGGL((prefill_prep_kernel<C, DK, DV, IO, M, true>), dim3((unsigned)items),
+                         dim3(kPrepNT), 0, st, a, t0, ncs, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_chain_kernel<C, DK, DV, DVB, IO, M>),
