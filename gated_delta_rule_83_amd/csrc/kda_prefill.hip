@@ -388,37 +388,31 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
     }
     __syncthreads();
 
-    // ---- 1b. Gam, R = e^{Gam_r - Gam_16a}, block decays, e^{Gam_n} -----
+    // ---- 1b. (g threads) block-level decays from the strip sums:
+    //          EB[a] = e^{Gam_16a}, EN[a] = e^{Gam_{C-1} - Gam_16a},
+    //          BT[a][b] = e^{Gam_16a - Gam_16b} (b < a), e^{Gam_n} to the workspace;
+    //          (all threads) R = e^{Gam_r - Gam_16a} from the strip-local sums
+    //          (Gam_r - Gam_16a = L_r - L_16a, L_16a = the strip's first g) and
+    //          the MFMA-ready factors, in place: q^ <- q^ R, k^ <- k^ R,
+    //          L <- k^ / R (all finite, see header).
     if (role == 3) {
       float off[4] = {0.f, 0.f, 0.f, 0.f}, last[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < NRB; ++s2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (s2 < gs) off[e] += sTot[s2][gc0 + e];
-          last[e] += sTot[s2][gc0 + e];
-        }
-      // Gam at each block start m = 16*s2: sum of earlier strip totals + the
-      // first token's g of that strip
       float gm[NRB][4];
       float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s2 = 0; s2 < NRB; ++s2)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          gm[s2][e] = run[e] + sFirst[s2][gc0 + e];
-          run[e] += sTot[s2][gc0 + e];
+          const float tot = sTot[s2][gc0 + e];
+          gm[s2][e] = run[e] + sFirst[s2][gc0 + e];  // Gam at block start 16*s2
+          if (s2 < gs) off[e] += tot;
+          run[e] += tot;
+          last[e] += tot;
         }
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sR[GS * gs][gc0]);
-      const float g0[4] = {l0[0] + off[0], l0[1] + off[1], l0[2] + off[2], l0[3] + off[3]};
+      float g0[4];
 #pragma unroll
-      for (int r = 0; r < GS; ++r) {
-        f32x4* rp = reinterpret_cast<f32x4*>(&sR[GS * gs + r][gc0]);
-        const f32x4 lr = *rp;
-        f32x4 rv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rv[e] = __expf(lr[e] - l0[e]);
-        *rp = rv;
-      }
+      for (int e = 0; e < 4; ++e) g0[e] = gm[gs][e];
+      (void)off;
       f32x4 eb, en;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -427,7 +421,6 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
       }
       *reinterpret_cast<f32x4*>(&sEB[gs][gc0]) = eb;
       *reinterpret_cast<f32x4*>(&sEN[gs][gc0]) = en;
-      // BT[gs][b2] for b2 < gs, stored at pair index gs*(gs-1)/2 + b2
 #pragma unroll
       for (int b2 = 0; b2 < NRB; ++b2) {
         if (b2 < gs) {
@@ -444,11 +437,29 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
         *reinterpret_cast<f32x4*>(Dn + gc0) = dn;
       }
     }
+    for (int idx = tid; idx < C * (DK / 4); idx += kPrepNT) {
+      const int r = idx / (DK / 4), c0 = 4 * (idx % (DK / 4));
+      f32x4* pr = reinterpret_cast<f32x4*>(&sR[r][c0]);
+      f32x4* pk = reinterpret_cast<f32x4*>(&sK[r][c0]);
+      f32x4* pq = reinterpret_cast<f32x4*>(&sQ[r][c0]);
+      const f32x4 lr = *pr, lm = *reinterpret_cast<const f32x4*>(&sFirst[r / 16][c0]);
+      const f32x4 kv = *pk;
+      f32x4 rv, kc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rv[e] = __expf(lr[e] - lm[e]);
+        kc[e] = kv[e] * __expf(lm[e] - lr[e]);
+      }
+      *pq = *pq * rv;
+      *pk = kv * rv;
+      *pr = kc;
+    }
     __syncthreads();
+    // from here on: sQ = q^ R, sK = k^ R, sR = k^ / R
 
     // ---- 2. A (beta-scaled, strictly lower) to LDS and P (lower) to the
-    //         workspace: tile (a, bc <= a) on MFMA with factors
-    //         k_r R_r and k_j / R_j * BT[a][bc] (both finite, see header) ----
+    //         workspace: tile (a, bc <= a) on MFMA; row factors k^ R, q^ R,
+    //         column factors k^ / R scaled by BT[a][bc] = e^{Gam_16a - Gam_16bc}
     {
       constexpr int NKS = DKP / KS;
       constexpr int NTILE = NRB * (NRB + 1) / 2;
@@ -459,26 +470,19 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
         const int r = 16 * arb + l16, j = 16 * bc + l16;
         const float* bt = bc < arb ? &sBT[arb * (arb - 1) / 2 + bc][0] : nullptr;
         f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-        // (unrolled by 2 only: fully unrolled, the LDS reads of all slices are
-        //  hoisted together and the registers spill)
-#pragma unroll 2
+#pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const int c0 = ks * KS + g16 * KPL;
           float vk[KPL], vq[KPL], vc[KPL];
           if (c0 < DK) {
-            float rr[KPL], rj[KPL];
-            lds_rd(&sR[r][c0], rr);
-            lds_rd(&sR[j][c0], rj);
             lds_rd(&sK[r][c0], vk);
             lds_rd(&sQ[r][c0], vq);
-            lds_rd(&sK[j][c0], vc);
-            float bv[KPL];
-            if (bt) lds_rd(bt + c0, bv);
+            lds_rd(&sR[j][c0], vc);
+            if (bt) {
+              float bv[KPL];
+              lds_rd(bt + c0, bv);
 #pragma unroll
-            for (int e = 0; e < KPL; ++e) {
-              vk[e] *= rr[e];
-              vq[e] *= rr[e];
-              vc[e] *= __builtin_amdgcn_rcpf(rj[e]) * (bt ? bv[e] : 1.f);
+              for (int e = 0; e < KPL; ++e) vc[e] *= bv[e];
             }
           } else {
 #pragma unroll
@@ -504,7 +508,7 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
       }
     }
 
-    // ---- 3. Q~ = e^{Gam_16a} R q^ and K^^T = e^{Gam_n - Gam_16a} / R k^
+    // ---- 3. Q~ = e^{Gam_16a} (q^ R) and K^^T = e^{Gam_n - Gam_16a} (k^ / R)
     //         (fragment-major) to the workspace ------------------------
     {
       constexpr int NPQ = C * DKP / KPL;
@@ -515,12 +519,11 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
         const int r = 16 * rb + ln % 16, c0 = ks * KS + (ln / 16) * KPL;
         float v[KPL];
         if (c0 < DK) {
-          float rr[KPL], eb[KPL];
-          lds_rd(&sR[r][c0], rr);
+          float eb[KPL];
           lds_rd(&sEB[rb][c0], eb);
           lds_rd(&sQ[r][c0], v);
 #pragma unroll
-          for (int e = 0; e < KPL; ++e) v[e] *= rr[e] * eb[e];
+          for (int e = 0; e < KPL; ++e) v[e] *= eb[e];
         } else {
 #pragma unroll
           for (int e = 0; e < KPL; ++e) v[e] = 0.f;
@@ -537,20 +540,20 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
 #pragma unroll
         for (int e = 0; e < KPL; ++e) {
           const int jj = j0 + e;
-          v[e] = jj < C ? sEN[jj / 16][c] * __builtin_amdgcn_rcpf(sR[jj][c]) * sK[jj][c] : 0.f;
+          v[e] = jj < C ? sEN[jj / 16][c] * sR[jj][c] : 0.f;
         }
         M::st(blk + L::oK + (size_t)pc * KPL, M::mk(v));
       }
     }
     __syncthreads();
-    // (beta e^{Gam} k^)^T = (beta e^{Gam_16a} R k^)^T into the q^ region
+    // (beta e^{Gam} k^)^T = (beta e^{Gam_16a} (k^ R))^T into the q^ region
     for (int idx = tid; idx < DK * (CP / 8); idx += kPrepNT) {
       const int c = idx % DK, j0 = 8 * (idx / DK);  // lanes walk channels: no bank conflicts
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int jj = j0 + e;
-        v[e] = jj < C ? sB[jj] * sEB[jj / 16][c] * sR[jj][c] * sK[jj][c] : 0.f;
+        v[e] = jj < C ? sB[jj] * sEB[jj / 16][c] * sK[jj][c] : 0.f;
       }
       st8(&sKT[c][j0], v);
     }
@@ -609,6 +612,11 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
     {
       constexpr int NCBW = DK / 16, NCBU = DV / 16;
       constexpr int NKC = CP / KS;
+      frag xa[NRB][NKC];  // the rows of X as A operands, loaded once per wave
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int ks = 0; ks < NKC; ++ks) xa[rb][ks] = M::ld(&sXb[16 * rb + l16][ks * KS + g16 * KPL]);
       for (int cbk = wv; cbk < NCBW + NCBU; cbk += kPrepNW) {
         const bool isw = cbk < NCBW;
         const int col = (isw ? cbk : cbk - NCBW) * 16 + l16;
@@ -620,8 +628,7 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
         for (int rb = 0; rb < NRB; ++rb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < NKC; ++ks)
-            acc = M::mma(M::ld(&sXb[16 * rb + l16][ks * KS + g16 * KPL]), fb[ks], acc);
+          for (int ks = 0; ks < NKC; ++ks) acc = M::mma(xa[rb][ks], fb[ks], acc);
           if (isw) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) sWst[16 * rb + 4 * g16 + e][col] = (MT)(-acc[e]);
