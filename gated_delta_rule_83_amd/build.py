@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prologue.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prologue.hip", "kda_prefill.hip", "kda_prep_rows.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

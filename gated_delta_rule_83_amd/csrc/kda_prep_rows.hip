@@ -1,0 +1,537 @@
+// Chunked-prefill preparation in the token-row layout, for bf16 inputs.
+//
+// Computes, per (chunk, head, sequence), the S-independent part of the chunk
+// recurrence ("为什么 Kimi K3 敢把 KV Cache 扔掉？一篇讲透 GPT-2 到 K3 的架构进化",
+// section 5 for the WY form, section 6 for the in-chunk cumulative decay,
+// section 7 for KDA's per-channel decay) and writes the same workspace block
+// as the general preparation kernel: -W, Q~, K^^T, P, U' and e^{Gam_n}.
+//
+// Layout. One workgroup of C/16 waves per item; wave w owns tokens
+// 16w .. 16w+15 of the chunk, and lane l holds token 16w + l%16 for the
+// channels 32s + 8(l/16) + e (e = 0..7) of every 32-channel slice s. A lane's
+// eight channels of one slice are exactly its piece of a
+// v_mfma_f32_16x16x32_bf16 operand (row l%16, depth 8(l/16)..+7), so the
+// activations feed the Gram products from registers. Along a 16-lane DPP
+// row the lanes are consecutive tokens, so
+//   - the short convolution takes its three history taps with row shifts
+//     (lanes 0..2 load token t-3 once, which also serves lanes 1 and 2 of
+//     the shifted copies), and
+//   - the in-block prefix sums of g are a 4-step row scan.
+// Transposes (token-contiguous operands for the contractions over tokens)
+// go through MFMAs with a 0/1 selection matrix as B: the product returns
+// four consecutive tokens of one channel per lane, exactly, and two lanes
+// (l and l^16) pair up into one 16-byte fragment piece.
+//
+// LDS holds only what crosses waves (about 51 KiB at C = 64, d = 128), so
+// several items share a CU and one item's loads overlap another's math.
+#include "kda_prefill.h"
+
+namespace kda {
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRowShr = 0x110;  // DPP row_shr:n is kRowShr + n
+constexpr int kRowShl = 0x100;  // DPP row_shl:n is kRowShl + n
+
+// Lane value from `CTRL`'s source lane inside the 16-lane row; lanes whose
+// source falls outside the row keep `old`.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp(unsigned old, unsigned src) {
+  return (unsigned)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float old, float src) {
+  return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(unsigned, old),
+                                             __builtin_bit_cast(unsigned, src)));
+}
+
+// element e of eight packed bf16 (exact)
+__device__ __forceinline__ float bfe(const u32x4& w, int e) {
+  const unsigned x = w[e / 2];
+  return __builtin_bit_cast(float, (e & 1) ? (x & 0xffff0000u) : (x << 16));
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* v) {
+  bf16x8 t;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = (bf16)v[e];
+  return t;
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
+  return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
+// Two 16x16 tiles d0, d1 in the accumulator layout (lane: rows 4(l/16)+e,
+// column l%16), to one 16-byte piece per lane of 8 consecutive rows: lanes
+// with even l/16 take d0's rows 8(l/32)..+7, lanes with odd l/16 take d1's
+// (the partner lane is l^16).
+__device__ __forceinline__ u32x4 pair_piece(f32x4 d0, f32x4 d1, int gq) {
+  const u32x2 v0 = __builtin_bit_cast(u32x2, to_bf16x4(d0));
+  const u32x2 v1 = __builtin_bit_cast(u32x2, to_bf16x4(d1));
+  const bool odd = gq & 1;
+  const u32x2 send = odd ? v0 : v1;
+  const u32x2 recv = {(unsigned)__shfl_xor((int)send[0], 16, kWave),
+                      (unsigned)__shfl_xor((int)send[1], 16, kWave)};
+  return odd ? u32x4{recv[0], recv[1], v1[0], v1[1]} : u32x4{v0[0], v0[1], recv[0], recv[1]};
+}
+
+template <int C, int DK, int DV>
+struct RowsSmem {
+  static constexpr int NRB = C / 16, NCH = 2 * DK + DV;
+  static constexpr int LDC = C + 4, LDT = C + 8;
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  // A: k^/R (fragment-major) -> X (fp32) -> (beta e^Gam k^)^T [DK][LDT]
+  static constexpr size_t nA =
+      mx(mx((size_t)C * DK * 2, (size_t)C * LDC * 4), (size_t)DK * LDT * 2);
+  // B: conv weights (one 16-byte pad per 8 channels) -> beta A (fp32) -> (beta v^)^T
+  static constexpr int NWQ = NCH + NCH / 8;
+  static constexpr size_t nB =
+      mx(mx((size_t)NWQ * 16, (size_t)C * LDC * 4), (size_t)DV * LDT * 2);
+  static constexpr size_t oB = nA, oC = oB + nB;
+  static constexpr size_t oE = oC + (size_t)C * LDT * 2;  // X as bf16 [C][LDT]
+  // E: g of each block's first token, block sums of the rest, Gam at each
+  // block's first token, Gam at the chunk's last token, beta per token
+  static constexpr size_t oTot = oE + (size_t)NRB * DK * 4;
+  static constexpr size_t oGm = oTot + (size_t)NRB * DK * 4;
+  static constexpr size_t oGn = oGm + (size_t)NRB * DK * 4;
+  static constexpr size_t oBeta = oGn + (size_t)DK * 4;
+  static constexpr size_t bytes = oBeta + (size_t)C * 4;
+};
+
+template <int C, int DK, int DV, bool CONV>
+__global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs a, int t0, int ncs,
+                                                                  uint8_t* ws) {
+  using M = MmaBf16;
+  using L = Ws<C, DK, DV, M>;
+  using SM = RowsSmem<C, DK, DV>;
+  constexpr int NRB = C / 16, NT = kWave * NRB;
+  constexpr int NKS = DK / 32, NVS = DV / 32, NKC = C / 32;
+  constexpr int LDC = SM::LDC, LDT = SM::LDT, CP = L::CP;
+  static_assert(C % 32 == 0 && DK % 32 == 0 && DV % 32 == 0, "row layout needs 32 | C, dk, dv");
+  static_assert(L::DKP == DK && CP == C, "no padding in the row layout");
+  static_assert(SM::bytes <= 64 * 1024, "row-layout prep LDS budget");
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SM::bytes];
+  bf16* sKi = reinterpret_cast<bf16*>(smem);
+  float (*sX)[LDC] = reinterpret_cast<float (*)[LDC]>(smem);
+  bf16 (*sKT)[LDT] = reinterpret_cast<bf16 (*)[LDT]>(smem);
+  f32x4* sW = reinterpret_cast<f32x4*>(smem + SM::oB);
+  float (*sL)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oB);
+  bf16 (*sVT)[LDT] = reinterpret_cast<bf16 (*)[LDT]>(smem + SM::oB);
+  bf16 (*sXb)[LDT] = reinterpret_cast<bf16 (*)[LDT]>(smem + SM::oC);
+  float (*sFirst)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oE);
+  float (*sTot)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oTot);
+  float (*sGm)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oGm);
+  float* sGn = reinterpret_cast<float*>(smem + SM::oGn);
+  float* sB = reinterpret_cast<float*>(smem + SM::oBeta);
+
+  const int tid = threadIdx.x, lane = tid % kWave, rb = tid / kWave;
+  const int i = lane % 16, gq = lane / 16;
+  const int H = a.H, T = a.T;
+  const int item = blockIdx.x;
+  const int cl = item % ncs, h = (item / ncs) % H, b = item / (ncs * H);
+  const int tstart = t0 + cl * C;
+  const int n = min(C, T - tstart);
+  const int r = 16 * rb + i;  // this lane's token in the chunk
+  const bool valid = r < n;
+  const int t = tstart + r;
+  const long row = ((long)b * T + min(t, T - 1)) * H + h;  // (b, token, h), clamped
+  const bool do_l2 = !(a.flags & KDA_F_SKIP_L2);
+  bf16* blk = reinterpret_cast<bf16*>(ws + ((size_t)cl * a.B * H + (size_t)b * H + h) * L::bytes);
+  float* Dn = reinterpret_cast<float*>(blk + L::nT);
+
+  // ---- 0. loads: conv weights of the head (to LDS), then the lane's token
+  //         (q, k, v, g, beta) and, for lanes 0..2 of a row, token t-3 -----
+  constexpr int NWR = (SM::NCH + NT - 1) / NT;
+  f32x4 wreg[NWR];
+  if constexpr (CONV) {
+#pragma unroll
+    for (int u = 0; u < NWR; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < SM::NCH) {
+        const long chan = idx < DK ? (long)h * DK + idx
+                        : idx < 2 * DK ? (long)H * DK + (long)h * DK + (idx - DK)
+                                       : 2L * H * DK + (long)h * DV + (idx - 2 * DK);
+        wreg[u] = *reinterpret_cast<const f32x4*>(a.conv_w + 4 * chan);
+      }
+    }
+  }
+  const float betav = valid ? a.beta[row] : 0.f;
+  const bf16* qsrc = static_cast<const bf16*>(a.q) + row * DK + 8 * gq;
+  const bf16* ksrc = static_cast<const bf16*>(a.k) + row * DK + 8 * gq;
+  const bf16* vsrc = static_cast<const bf16*>(a.v) + row * DV + 8 * gq;
+  u32x4 xq[NKS], xk[NKS], xv[NVS], yq[NKS], yk[NKS], yv[NVS];
+  f32x4 gl[NKS][2];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    xq[s] = *reinterpret_cast<const u32x4*>(qsrc + 32 * s);
+    xk[s] = *reinterpret_cast<const u32x4*>(ksrc + 32 * s);
+  }
+#pragma unroll
+  for (int s = 0; s < NVS; ++s) xv[s] = *reinterpret_cast<const u32x4*>(vsrc + 32 * s);
+  const float* gsrc = a.g + row * DK + 8 * gq;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    gl[s][0] = *reinterpret_cast<const f32x4*>(gsrc + 32 * s);
+    gl[s][1] = *reinterpret_cast<const f32x4*>(gsrc + 32 * s + 4);
+  }
+  if constexpr (CONV) {
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) yq[s] = yk[s] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < NVS; ++s) yv[s] = u32x4{0u, 0u, 0u, 0u};
+    if (i < 3) {
+      const int t3 = t - 3;
+      const bf16 *q3, *k3, *v3;
+      if (t3 >= 0) {  // inside the inputs (clamped for tokens past T, never used)
+        const long row3 = ((long)b * T + min(t3, T - 1)) * H + h;
+        q3 = static_cast<const bf16*>(a.q) + row3 * DK;
+        k3 = static_cast<const bf16*>(a.k) + row3 * DK;
+        v3 = static_cast<const bf16*>(a.v) + row3 * DV;
+      } else {  // before the first token of the call: the ring, slot 3 + t3
+        const long ctot = (long)H * SM::NCH;
+        const bf16* ring = static_cast<const bf16*>(a.ring) + ((long)b * 3 + (3 + t3)) * ctot;
+        q3 = ring + (long)h * DK;
+        k3 = ring + (long)H * DK + (long)h * DK;
+        v3 = ring + 2L * H * DK + (long)h * DV;
+      }
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        yq[s] = *reinterpret_cast<const u32x4*>(q3 + 32 * s + 8 * gq);
+        yk[s] = *reinterpret_cast<const u32x4*>(k3 + 32 * s + 8 * gq);
+      }
+#pragma unroll
+      for (int s = 0; s < NVS; ++s) yv[s] = *reinterpret_cast<const u32x4*>(v3 + 32 * s + 8 * gq);
+    }
+#pragma unroll
+    for (int u = 0; u < NWR; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < SM::NCH) sW[idx + idx / 8] = wreg[u];
+    }
+  }
+
+  // ---- 1a. g: in-block prefix sums (row scan) and R = e^{Gam_r - Gam_m},
+  //          m = the block's first token; block first values and sums of
+  //          the rest to LDS ------------------------------------------------
+  float R[NKS][8];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float gv = valid ? gl[s][e / 4][e % 4] : 0.f;
+      p[e] = i == 0 ? 0.f : gv;
+      if (e % 4 == 3 && i == 0)
+        *reinterpret_cast<f32x4*>(&sFirst[rb][32 * s + 8 * gq + e - 3]) =
+            valid ? gl[s][e / 4] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] += dppf<kRowShr + 1>(0.f, p[e]);
+      p[e] += dppf<kRowShr + 2>(0.f, p[e]);
+      p[e] += dppf<kRowShr + 4>(0.f, p[e]);
+      p[e] += dppf<kRowShr + 8>(0.f, p[e]);
+      R[s][e] = __expf(p[e]);
+    }
+    if (i == 15) {
+      *reinterpret_cast<f32x4*>(&sTot[rb][32 * s + 8 * gq]) = f32x4{p[0], p[1], p[2], p[3]};
+      *reinterpret_cast<f32x4*>(&sTot[rb][32 * s + 8 * gq + 4]) = f32x4{p[4], p[5], p[6], p[7]};
+    }
+  }
+  if constexpr (CONV) __syncthreads();  // conv weights visible
+
+  // ---- 1a. q, k, v: short conv + SiLU (taps by row shifts), L2 of q, k ----
+  // z = SiLU(w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t); tap x_{t-d} of
+  // lane j is x_t of lane j-d, or for j < d the t-3 load of lane j+3-d.
+  auto activate = [&](u32x4 x, u32x4 y, int wbase, float* z) {
+    if constexpr (CONV) {
+      // pin the raw words here, so that the shifted copies are made slice by
+      // slice and not all at once ahead of the weights' barrier
+      asm volatile("" : "+v"(x), "+v"(y));
+      u32x4 t1, t2, t3;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        t1[w] = dpp<kRowShr + 1>(dpp<kRowShl + 2>(0u, y[w]), x[w]);
+        t2[w] = dpp<kRowShr + 2>(dpp<kRowShl + 1>(0u, y[w]), x[w]);
+        t3[w] = dpp<kRowShr + 3>(y[w], x[w]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wi = wbase + e;
+        const f32x4 wt = sW[wi + wi / 8];
+        z[e] = silu(wt.x * bfe(t3, e) + wt.y * bfe(t2, e) + wt.z * bfe(t1, e) + wt.w * bfe(x, e));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = bfe(x, e);
+    }
+  };
+  bf16x8 vb[NVS];  // beta v^ (the B side of U' after a transpose)
+#pragma unroll
+  for (int s = 0; s < NVS; ++s) {
+    float z[8];
+    activate(xv[s], yv[s], 2 * DK + 32 * s + 8 * gq, z);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] *= betav;
+    vb[s] = to_bf16x8(z);
+    asm volatile("" : "+v"(vb[s]));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float qf[NKS][8], kf[NKS][8];
+  {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      activate(xq[s], yq[s], 32 * s + 8 * gq, qf[s]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq += qf[s][e] * qf[s][e];
+      __builtin_amdgcn_sched_barrier(0);  // one slice's weights in flight at a time
+    }
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      activate(xk[s], yk[s], DK + 32 * s + 8 * gq, kf[s]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sk += kf[s][e] * kf[s][e];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sq += __shfl_xor(sq, 16, kWave);
+    sq += __shfl_xor(sq, 32, kWave);
+    sk += __shfl_xor(sk, 16, kWave);
+    sk += __shfl_xor(sk, 32, kWave);
+    const float iq = !valid ? 0.f : do_l2 ? __builtin_amdgcn_rsqf(sq + kL2Eps) : 1.f;
+    const float ik = !valid ? 0.f : do_l2 ? __builtin_amdgcn_rsqf(sk + kL2Eps) : 1.f;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qf[s][e] *= iq;
+        kf[s][e] *= ik;
+      }
+  }
+  if (gq == 0) sB[r] = betav;
+  __syncthreads();
+
+  // ---- 1b. Gam at each block's first token and at the chunk's end, from
+  //          the block first values and the sums of the rest --------------
+  for (int c = tid; c < DK; c += NT) {
+    float cum = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < NRB; ++bb) {
+      const float f = sFirst[bb][c];
+      sGm[bb][c] = cum + f;
+      cum += f + sTot[bb][c];
+    }
+    sGn[c] = cum;
+    Dn[c] = __expf(cum);
+  }
+  __syncthreads();
+
+  // selection matrices: B_hf[k][n] = (k == n + 16 hf) picks channel half hf
+  bf16x8 sel[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[hf][e] = (bf16)(8 * gq + e == i + 16 * hf ? 1.f : 0.f);
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // ---- 1c. per slice: Q~ = e^{Gam} q^ and K^^T = e^{Gam_n - Gam} k^ to the
+  //          workspace, k^/R to LDS; q^ <- q^ R and k^ <- k^ R (the Gram
+  //          row factors) --------------------------------------------------
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const f32x4* pm = reinterpret_cast<const f32x4*>(&sGm[rb][32 * s + 8 * gq]);
+    const f32x4* pn = reinterpret_cast<const f32x4*>(&sGn[32 * s + 8 * gq]);
+    const f32x4 m0 = pm[0], m1 = pm[1], n0 = pn[0], n1 = pn[1];
+    float qt[8], ki[8], kh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float gmr = e < 4 ? m0[e] : m1[e - 4], gn = e < 4 ? n0[e] : n1[e - 4];
+      const float eb = __expf(gmr), en = __expf(gn - gmr);
+      const float rr = R[s][e];
+      const float qr = qf[s][e] * rr, kr = kf[s][e] * rr;
+      ki[e] = kf[s][e] * __builtin_amdgcn_rcpf(rr);
+      qt[e] = eb * qr;
+      kh[e] = en * ki[e];
+      qf[s][e] = qr;
+      kf[s][e] = kr;
+    }
+    *reinterpret_cast<bf16x8*>(blk + L::oQ + ((size_t)(rb * NKS + s) * kWave + lane) * 8) =
+        to_bf16x8(qt);
+    *reinterpret_cast<bf16x8*>(sKi + ((size_t)(rb * NKS + s) * kWave + lane) * 8) = to_bf16x8(ki);
+    // K^^T: channel rows 32s + 16hf + i, tokens 16rb + 4gq + e per selection
+    const bf16x8 khb = to_bf16x8(kh);
+    const f32x4 d0 = M::mma(khb, sel[0], zero4), d1 = M::mma(khb, sel[1], zero4);
+    const u32x4 pc = pair_piece(d0, d1, gq);
+    const int cb = 2 * s + (gq & 1), lk = 16 * (2 * (rb % 2) + gq / 2) + i;
+    *reinterpret_cast<u32x4*>(blk + L::oK + ((size_t)(cb * NKC + rb / 2) * kWave + lk) * 8) = pc;
+    __builtin_amdgcn_sched_barrier(0);  // one slice at a time
+  }
+  __syncthreads();
+
+  // ---- 2. Gram tiles of this wave's block row: A (beta-scaled, strictly
+  //         lower) to LDS, P (lower) to the workspace. Tile (rb, bc) takes
+  //         rows (k^ R) and (q^ R) scaled by e^{Gam_m(rb) - Gam_m(bc)} and
+  //         columns k^/R of block bc. Then beta e^{Gam} k^ = beta
+  //         e^{Gam_m(rb)} (k^ R), the B side of W after a transpose. ------
+  bf16x8 kb[NKS];
+  {
+    const f32x4 bq = *reinterpret_cast<const f32x4*>(&sB[16 * rb + 4 * gq]);
+#pragma unroll
+    for (int bc = 0; bc < NRB; ++bc) {
+      f32x4 accA = zero4, accP = zero4;
+      if (bc <= rb) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          const bf16x8 fb =
+              *reinterpret_cast<const bf16x8*>(sKi + ((size_t)(bc * NKS + s) * kWave + lane) * 8);
+          float ak[8], aq[8];
+          if (bc < rb) {
+            const f32x4* pm = reinterpret_cast<const f32x4*>(&sGm[rb][32 * s + 8 * gq]);
+            const f32x4* pc = reinterpret_cast<const f32x4*>(&sGm[bc][32 * s + 8 * gq]);
+            const f32x4 m0 = pm[0], m1 = pm[1], c0 = pc[0], c1 = pc[1];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float sc = __expf(e < 4 ? m0[e] - c0[e] : m1[e - 4] - c1[e - 4]);
+              ak[e] = kf[s][e] * sc;
+              aq[e] = qf[s][e] * sc;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              ak[e] = kf[s][e];
+              aq[e] = qf[s][e];
+            }
+          }
+          accA = M::mma(to_bf16x8(ak), fb, accA);
+          accP = M::mma(to_bf16x8(aq), fb, accP);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * rb + 4 * gq + e, jj = 16 * bc + i;
+        if (bc <= rb) sL[rr][jj] = jj < rr ? bq[e] * accA[e] : 0.f;
+        blk[L::oP + (size_t)rr * CP + jj] = (bf16)(jj <= rr ? accP[e] : 0.f);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const f32x4* pm = reinterpret_cast<const f32x4*>(&sGm[rb][32 * s + 8 * gq]);
+      const f32x4 m0 = pm[0], m1 = pm[1];
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = betav * __expf(e < 4 ? m0[e] : m1[e - 4]) * kf[s][e];
+      kb[s] = to_bf16x8(v);
+      asm volatile("" : "+v"(kb[s]));  // made here, so that k^ R dies here
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. X = (I + beta A)^{-1}, then X as bf16 and (beta v^)^T ---------
+  unit_lower_inverse<C, NT>(sL, sX, tid);
+  for (int idx = tid; idx < C * (C / 8); idx += NT) {
+    const int rr = idx / (C / 8), j0 = 8 * (idx % (C / 8));
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(&sX[rr][j0]);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(&sX[rr][j0 + 4]);
+    const float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    *reinterpret_cast<bf16x8*>(&sXb[rr][j0]) = to_bf16x8(v);
+  }
+#pragma unroll
+  for (int s = 0; s < NVS; ++s) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 d = M::mma(vb[s], sel[hf], zero4);
+      *reinterpret_cast<bf16x4*>(&sVT[32 * s + 16 * hf + i][16 * rb + 4 * gq]) = to_bf16x4(d);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 d = M::mma(kb[s], sel[hf], zero4);
+      *reinterpret_cast<bf16x4*>(&sKT[32 * s + 16 * hf + i][16 * rb + 4 * gq]) = to_bf16x4(d);
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. U' = X (beta V) (accumulator layout) and W^T = (beta e^Gam K)^T
+  //         X^T, stored as -W pieces (fragment-major) --------------------
+  bf16x8 xb[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) xb[kc] = *reinterpret_cast<const bf16x8*>(&sXb[r][32 * kc + 8 * gq]);
+#pragma unroll
+  for (int vt = 0; vt < DV / 16; ++vt) {
+    f32x4 acc = zero4;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+      acc = M::mma(xb[kc], *reinterpret_cast<const bf16x8*>(&sVT[16 * vt + i][32 * kc + 8 * gq]), acc);
+    *reinterpret_cast<bf16x4*>(blk + L::oU + ((size_t)(rb * (DV / 16) + vt) * kWave + lane) * 4) =
+        to_bf16x4(acc);
+  }
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    f32x4 d[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 acc = zero4;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+        acc = M::mma(*reinterpret_cast<const bf16x8*>(&sKT[32 * s + 16 * hf + i][32 * kc + 8 * gq]),
+                     xb[kc], acc);
+      d[hf] = -acc;
+    }
+    const u32x4 pc = pair_piece(d[0], d[1], gq);
+    const int lw = 16 * (2 * (gq & 1) + gq / 2) + i;
+    *reinterpret_cast<u32x4*>(blk + L::oW + ((size_t)(rb * NKS + s) * kWave + lw) * 8) = pc;
+  }
+}
+
+template <int C, int DK, int DV>
+hipError_t launch_t(const PrefillArgs& a, int t0, int ncs, uint8_t* ws, hipStream_t st) {
+  const long items = (long)ncs * a.H * a.B;
+  if (a.flags & KDA_F_SKIP_CONV)
+    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, false>), dim3((unsigned)items),
+                       dim3(C * 4), 0, st, a, t0, ncs, ws);
+  else
+    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, true>), dim3((unsigned)items),
+                       dim3(C * 4), 0, st, a, t0, ncs, ws);
+  return hipGetLastError();
+}
+
+template <int C, int DK>
+hipError_t launch_dv(const PrefillArgs& a, int t0, int ncs, uint8_t* ws, hipStream_t st) {
+  switch (a.dv) {
+    case 32: return launch_t<C, DK, 32>(a, t0, ncs, ws, st);
+    case 64: return launch_t<C, DK, 64>(a, t0, ncs, ws, st);
+    case 128: return launch_t<C, DK, 128>(a, t0, ncs, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int C>
+hipError_t launch_dk(const PrefillArgs& a, int t0, int ncs, uint8_t* ws, hipStream_t st) {
+  switch (a.dk) {
+    case 32: return launch_dv<C, 32>(a, t0, ncs, ws, st);
+    case 64: return launch_dv<C, 64>(a, t0, ncs, ws, st);
+    case 128: return launch_dv<C, 128>(a, t0, ncs, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool prep_rows_supported(int chunk, int dk, int dv, kda_dtype io) {
+  return io == KDA_BF16 && (chunk == 32 || chunk == 64) && dk >= 32 && dv >= 32;
+}
+
+hipError_t launch_prep_rows(const PrefillArgs& a, int t0, int ncs, void* ws, hipStream_t st) {
+  if (!prep_rows_supported(a.chunk, a.dk, a.dv, KDA_BF16)) return hipErrorInvalidValue;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  return a.chunk == 32 ? launch_dk<32>(a, t0, ncs, w, st) : launch_dk<64>(a, t0, ncs, w, st);
+}
+
+}  // namespace kda

@@ -74,6 +74,43 @@ def test_prefill_bf16_small(chunk, overrides):
     np.testing.assert_array_equal(f64(st.ring), ref_ring)
 
 
+@pytest.mark.parametrize("chunk,overrides", [
+    (64, dict(T=150, B=2, H=2, dk=128, dv=32, io="bf16", s0_random=True, seed=45)),
+    (32, dict(T=70, B=1, H=3, dk=32, dv=128, io="bf16", s0_random=True, ring_random=True,
+              seed=46)),
+    (64, dict(T=3, B=2, H=2, dk=64, dv=128, io="bf16", s0_random=True, ring_random=True,
+              seed=47)),
+    (32, dict(T=1, B=1, H=2, dk=128, dv=64, io="bf16", s0_random=True, ring_random=True,
+              seed=48)),
+    (64, dict(T=129, B=1, H=2, dk=32, dv=32, io="bf16", ring_random=True, seed=49)),
+])
+def test_prefill_bf16_row_layout_shapes(chunk, overrides):
+    """bf16 shapes of the token-row preparation kernel: d_k != d_v, chunk 32
+    and 64, ragged tails, T below the conv history (history from the ring)."""
+    test_prefill_bf16_small(chunk, overrides)
+
+
+@pytest.mark.parametrize("flags", [kda.KDA_F_SKIP_CONV, kda.KDA_F_SKIP_CONV | kda.KDA_F_SKIP_L2])
+def test_prefill_bf16_flags(flags):
+    """bf16 chunk 64, 128x128 with the conv (and the L2 step) skipped; for
+    KDA_F_SKIP_L2 the inputs are unit-norm q, k rounded to bf16."""
+    dev = device()
+    inp = workloads.make("tiny", T=90, B=1, H=2, dk=128, dv=128, io="bf16", s0_random=True,
+                         ring_random=True, seed=52)
+    if flags & kda.KDA_F_SKIP_L2:
+        for name in ("q", "k"):
+            x = getattr(inp, name).double()
+            x = x / x.pow(2).sum(-1, keepdim=True).sqrt()
+            setattr(inp, name, x.to(getattr(inp, name).dtype))
+    ref_o, ref_S, _ = kda_oracle.forward(inp.q, inp.k, inp.v, inp.g, inp.beta, None, inp.S0,
+                                         inp.ring0, flags=flags)
+    st, o = _prefill(inp, dev, 64, torch.bfloat16, flags=flags)
+    eo, es = rel_err(f64(o), ref_o), rel_err(f64(st.S), ref_S)
+    print(f"prefill bf16 flags={flags}: rel err o={eo:.2e} S={es:.2e}")
+    assert eo <= 2e-2 and es <= 2e-2
+    np.testing.assert_array_equal(f64(st.ring), f64(inp.ring0))
+
+
 def test_prefill_4k_bf16_full_size():
     """T=4096, 96 heads of 128x128, chunk 64, bf16 I/O, slow decay: the full
     launch the benchmark times; the oracle checks 8 sampled heads over all
