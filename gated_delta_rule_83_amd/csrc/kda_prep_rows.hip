@@ -80,29 +80,29 @@ __device__ __forceinline__ u32x4 pair_piece(f32x4 d0, f32x4 d1, int gq) {
 
 template <int C, int DK, int DV>
 struct RowsSmem {
-  static constexpr int NRB = C / 16, NCH = 2 * DK + DV;
+  static constexpr int NRB = C / 16, NCH = 2 * DK + DV, NBT = NRB * (NRB - 1) / 2;
   static constexpr int LDC = C + 4, LDT = C + 8;
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-  // A: k^/R (fragment-major) -> X (fp32) -> (beta e^Gam k^)^T [DK][LDT]
-  static constexpr size_t nA =
-      mx(mx((size_t)C * DK * 2, (size_t)C * LDC * 4), (size_t)DK * LDT * 2);
+  // A: g of each block's first token and block sums of the rest (fp32
+  //    [NRB][DK] each) -> k^/R (fragment-major) -> X (fp32 [C][LDC]) ->
+  //    (beta e^Gam k^)^T [DK][LDT]
+  static constexpr size_t nA = mx(mx((size_t)2 * NRB * DK * 4, (size_t)C * DK * 2),
+                                  mx((size_t)C * LDC * 4, (size_t)DK * LDT * 2));
   // B: conv weights (one 16-byte pad per 8 channels) -> beta A (fp32) -> (beta v^)^T
   static constexpr int NWQ = NCH + NCH / 8;
   static constexpr size_t nB =
       mx(mx((size_t)NWQ * 16, (size_t)C * LDC * 4), (size_t)DV * LDT * 2);
+  // C: the raw inputs of the three tokens before each block ([NRB][3][NCH]
+  //    bf16) -> block decays EB[a] = e^{Gam_m(a)}, EN[a] = e^{Gam_n - Gam_m(a)}
+  //    and BT[a][b] = e^{Gam_m(a) - Gam_m(b)} (b < a), fp32 [.][DK] -> X as bf16
+  static constexpr size_t nC = mx(mx((size_t)NRB * 3 * NCH * 2, (size_t)(2 * NRB + NBT) * DK * 4),
+                                  (size_t)C * LDT * 2);
   static constexpr size_t oB = nA, oC = oB + nB;
-  static constexpr size_t oE = oC + (size_t)C * LDT * 2;  // X as bf16 [C][LDT]
-  // E: g of each block's first token, block sums of the rest, Gam at each
-  // block's first token, Gam at the chunk's last token, beta per token
-  static constexpr size_t oTot = oE + (size_t)NRB * DK * 4;
-  static constexpr size_t oGm = oTot + (size_t)NRB * DK * 4;
-  static constexpr size_t oGn = oGm + (size_t)NRB * DK * 4;
-  static constexpr size_t oBeta = oGn + (size_t)DK * 4;
-  static constexpr size_t bytes = oBeta + (size_t)C * 4;
+  static constexpr size_t bytes = oC + nC;
 };
 
 template <int C, int DK, int DV, bool CONV>
-__global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs a, int t0, int ncs,
+__global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs a, int t0, int ncs,
                                                                   uint8_t* ws) {
   using M = MmaBf16;
   using L = Ws<C, DK, DV, M>;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
   constexpr int LDC = SM::LDC, LDT = SM::LDT, CP = L::CP;
   static_assert(C % 32 == 0 && DK % 32 == 0 && DV % 32 == 0, "row layout needs 32 | C, dk, dv");
   static_assert(L::DKP == DK && CP == C, "no padding in the row layout");
-  static_assert(SM::bytes <= 64 * 1024, "row-layout prep LDS budget");
+  static_assert(SM::bytes <= 53 * 1024, "row-layout prep LDS budget (three items per CU)");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[SM::bytes];
   bf16* sKi = reinterpret_cast<bf16*>(smem);
@@ -122,11 +122,12 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
   float (*sL)[LDC] = reinterpret_cast<float (*)[LDC]>(smem + SM::oB);
   bf16 (*sVT)[LDT] = reinterpret_cast<bf16 (*)[LDT]>(smem + SM::oB);
   bf16 (*sXb)[LDT] = reinterpret_cast<bf16 (*)[LDT]>(smem + SM::oC);
-  float (*sFirst)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oE);
-  float (*sTot)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oTot);
-  float (*sGm)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oGm);
-  float* sGn = reinterpret_cast<float*>(smem + SM::oGn);
-  float* sB = reinterpret_cast<float*>(smem + SM::oBeta);
+  float (*sFirst)[DK] = reinterpret_cast<float (*)[DK]>(smem);
+  float (*sTot)[DK] = reinterpret_cast<float (*)[DK]>(smem + (size_t)NRB * DK * 4);
+  bf16 (*sHist)[3][SM::NCH] = reinterpret_cast<bf16 (*)[3][SM::NCH]>(smem + SM::oC);
+  float (*sEB)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oC);
+  float (*sEN)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oC + (size_t)NRB * DK * 4);
+  float (*sBT)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oC + (size_t)2 * NRB * DK * 4);
 
   const int tid = threadIdx.x, lane = tid % kWave, rb = tid / kWave;
   const int i = lane % 16, gq = lane / 16;
@@ -144,7 +145,9 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
   float* Dn = reinterpret_cast<float*>(blk + L::nT);
 
   // ---- 0. loads: conv weights of the head (to LDS), then the lane's token
-  //         (q, k, v, g, beta) and, for lanes 0..2 of a row, token t-3 -----
+  //         (q, k, v, g, beta); the conv history of each block to LDS: the
+  //         last three tokens of the block before it, or for block 0 the
+  //         three tokens before the chunk (from the ring before token 0) -----
   constexpr int NWR = (SM::NCH + NT - 1) / NT;
   f32x4 wreg[NWR];
   if constexpr (CONV) {
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
   const bf16* qsrc = static_cast<const bf16*>(a.q) + row * DK + 8 * gq;
   const bf16* ksrc = static_cast<const bf16*>(a.k) + row * DK + 8 * gq;
   const bf16* vsrc = static_cast<const bf16*>(a.v) + row * DV + 8 * gq;
-  u32x4 xq[NKS], xk[NKS], xv[NVS], yq[NKS], yk[NKS], yv[NVS];
+  u32x4 xq[NKS], xk[NKS], xv[NVS];
   f32x4 gl[NKS][2];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
@@ -179,15 +182,11 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
     gl[s][1] = *reinterpret_cast<const f32x4*>(gsrc + 32 * s + 4);
   }
   if constexpr (CONV) {
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) yq[s] = yk[s] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int s = 0; s < NVS; ++s) yv[s] = u32x4{0u, 0u, 0u, 0u};
-    if (i < 3) {
-      const int t3 = t - 3;
+    if (rb == 0 && i < 3) {
+      const int t3 = tstart - 3 + i;
       const bf16 *q3, *k3, *v3;
-      if (t3 >= 0) {  // inside the inputs (clamped for tokens past T, never used)
-        const long row3 = ((long)b * T + min(t3, T - 1)) * H + h;
+      if (t3 >= 0) {
+        const long row3 = ((long)b * T + t3) * H + h;
         q3 = static_cast<const bf16*>(a.q) + row3 * DK;
         k3 = static_cast<const bf16*>(a.k) + row3 * DK;
         v3 = static_cast<const bf16*>(a.v) + row3 * DV;
@@ -200,11 +199,25 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
       }
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        yq[s] = *reinterpret_cast<const u32x4*>(q3 + 32 * s + 8 * gq);
-        yk[s] = *reinterpret_cast<const u32x4*>(k3 + 32 * s + 8 * gq);
+        *reinterpret_cast<u32x4*>(&sHist[0][i][32 * s + 8 * gq]) =
+            *reinterpret_cast<const u32x4*>(q3 + 32 * s + 8 * gq);
+        *reinterpret_cast<u32x4*>(&sHist[0][i][DK + 32 * s + 8 * gq]) =
+            *reinterpret_cast<const u32x4*>(k3 + 32 * s + 8 * gq);
       }
 #pragma unroll
-      for (int s = 0; s < NVS; ++s) yv[s] = *reinterpret_cast<const u32x4*>(v3 + 32 * s + 8 * gq);
+      for (int s = 0; s < NVS; ++s)
+        *reinterpret_cast<u32x4*>(&sHist[0][i][2 * DK + 32 * s + 8 * gq]) =
+            *reinterpret_cast<const u32x4*>(v3 + 32 * s + 8 * gq);
+    }
+    if (rb + 1 < NRB && i >= 13) {
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        *reinterpret_cast<u32x4*>(&sHist[rb + 1][i - 13][32 * s + 8 * gq]) = xq[s];
+        *reinterpret_cast<u32x4*>(&sHist[rb + 1][i - 13][DK + 32 * s + 8 * gq]) = xk[s];
+      }
+#pragma unroll
+      for (int s = 0; s < NVS; ++s)
+        *reinterpret_cast<u32x4*>(&sHist[rb + 1][i - 13][2 * DK + 32 * s + 8 * gq]) = xv[s];
     }
 #pragma unroll
     for (int u = 0; u < NWR; ++u) {
@@ -241,13 +254,15 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
       *reinterpret_cast<f32x4*>(&sTot[rb][32 * s + 8 * gq + 4]) = f32x4{p[4], p[5], p[6], p[7]};
     }
   }
-  if constexpr (CONV) __syncthreads();  // conv weights visible
+  if constexpr (CONV) __syncthreads();  // conv weights and history visible
 
   // ---- 1a. q, k, v: short conv + SiLU (taps by row shifts), L2 of q, k ----
   // z = SiLU(w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t); tap x_{t-d} of
-  // lane j is x_t of lane j-d, or for j < d the t-3 load of lane j+3-d.
-  auto activate = [&](u32x4 x, u32x4 y, int wbase, float* z) {
+  // lane j is x_t of lane j-d, or for j < d the history token j+3-d of the
+  // block, which lane j+3-d (< 3) reads from LDS.
+  auto activate = [&](u32x4 x, int wbase, float* z) {
     if constexpr (CONV) {
+      u32x4 y = *reinterpret_cast<const u32x4*>(&sHist[rb][i < 3 ? i : 2][wbase]);
       // pin the raw words here, so that the shifted copies are made slice by
       // slice and not all at once ahead of the weights' barrier
       asm volatile("" : "+v"(x), "+v"(y));
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
 #pragma unroll
   for (int s = 0; s < NVS; ++s) {
     float z[8];
-    activate(xv[s], yv[s], 2 * DK + 32 * s + 8 * gq, z);
+    activate(xv[s], 2 * DK + 32 * s + 8 * gq, z);
 #pragma unroll
     for (int e = 0; e < 8; ++e) z[e] *= betav;
     vb[s] = to_bf16x8(z);
@@ -285,14 +300,14 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      activate(xq[s], yq[s], 32 * s + 8 * gq, qf[s]);
+      activate(xq[s], 32 * s + 8 * gq, qf[s]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sq += qf[s][e] * qf[s][e];
       __builtin_amdgcn_sched_barrier(0);  // one slice's weights in flight at a time
     }
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      activate(xk[s], yk[s], DK + 32 * s + 8 * gq, kf[s]);
+      activate(xk[s], DK + 32 * s + 8 * gq, kf[s]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sk += kf[s][e] * kf[s][e];
       __builtin_amdgcn_sched_barrier(0);
@@ -311,20 +326,26 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
         kf[s][e] *= ik;
       }
   }
-  if (gq == 0) sB[r] = betav;
   __syncthreads();
 
-  // ---- 1b. Gam at each block's first token and at the chunk's end, from
-  //          the block first values and the sums of the rest --------------
+  // ---- 1b. block decays from Gam at each block's first token,
+  //          Gam_m(a) = sum_{b < a} (first + rest)[b] + first[a], and at the
+  //          chunk's last token (Gam_n; e^{Gam_n} also to the workspace) -----
   for (int c = tid; c < DK; c += NT) {
-    float cum = 0.f;
+    float gm[NRB], cum = 0.f;
 #pragma unroll
     for (int bb = 0; bb < NRB; ++bb) {
       const float f = sFirst[bb][c];
-      sGm[bb][c] = cum + f;
+      gm[bb] = cum + f;
       cum += f + sTot[bb][c];
     }
-    sGn[c] = cum;
+#pragma unroll
+    for (int bb = 0; bb < NRB; ++bb) {
+      sEB[bb][c] = __expf(gm[bb]);
+      sEN[bb][c] = __expf(cum - gm[bb]);
+#pragma unroll
+      for (int b2 = 0; b2 < bb; ++b2) sBT[bb * (bb - 1) / 2 + b2][c] = __expf(gm[bb] - gm[b2]);
+    }
     Dn[c] = __expf(cum);
   }
   __syncthreads();
@@ -339,17 +360,16 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
 
   // ---- 1c. per slice: Q~ = e^{Gam} q^ and K^^T = e^{Gam_n - Gam} k^ to the
   //          workspace, k^/R to LDS; q^ <- q^ R and k^ <- k^ R (the Gram
-  //          row factors) --------------------------------------------------
+  //          row factors). A barrier first: sKi overwrites the block sums ---
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
-    const f32x4* pm = reinterpret_cast<const f32x4*>(&sGm[rb][32 * s + 8 * gq]);
-    const f32x4* pn = reinterpret_cast<const f32x4*>(&sGn[32 * s + 8 * gq]);
-    const f32x4 m0 = pm[0], m1 = pm[1], n0 = pn[0], n1 = pn[1];
+    const f32x4* pb = reinterpret_cast<const f32x4*>(&sEB[rb][32 * s + 8 * gq]);
+    const f32x4* pn = reinterpret_cast<const f32x4*>(&sEN[rb][32 * s + 8 * gq]);
+    const f32x4 b0 = pb[0], b1 = pb[1], n0 = pn[0], n1 = pn[1];
     float qt[8], ki[8], kh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float gmr = e < 4 ? m0[e] : m1[e - 4], gn = e < 4 ? n0[e] : n1[e - 4];
-      const float eb = __expf(gmr), en = __expf(gn - gmr);
+      const float eb = e < 4 ? b0[e] : b1[e - 4], en = e < 4 ? n0[e] : n1[e - 4];
       const float rr = R[s][e];
       const float qr = qf[s][e] * rr, kr = kf[s][e] * rr;
       ki[e] = kf[s][e] * __builtin_amdgcn_rcpf(rr);
@@ -371,59 +391,72 @@ __global__ __launch_bounds__(C * 4, 2) void prefill_prep_rows_kernel(PrefillArgs
   }
   __syncthreads();
 
-  // ---- 2. Gram tiles of this wave's block row: A (beta-scaled, strictly
-  //         lower) to LDS, P (lower) to the workspace. Tile (rb, bc) takes
-  //         rows (k^ R) and (q^ R) scaled by e^{Gam_m(rb) - Gam_m(bc)} and
-  //         columns k^/R of block bc. Then beta e^{Gam} k^ = beta
-  //         e^{Gam_m(rb)} (k^ R), the B side of W after a transpose. ------
+  // ---- 2. Gram tiles of this wave's block row, transposed: the product of
+  //         A operand k^/R of block bc (LDS) and B operand (k^ R), (q^ R) of
+  //         this wave's tokens, scaled by BT[rb][bc] for bc < rb, is the
+  //         tile (rows j of block bc, columns r of block rb) of A^T and P^T.
+  //         Lane (l%16, l/16) then holds A_rj, P_rj for r = 16rb + l%16 and
+  //         j = 16bc + 4(l/16) + e: beta_r A_rj (strictly lower) goes to
+  //         LDS as one 16-byte row piece, P (lower) to the workspace as
+  //         16-byte pieces of 8 columns (two tiles paired). Then beta
+  //         e^{Gam} k^ = beta EB[rb] (k^ R), the B side of W after a
+  //         transpose. -------------------------------------------------------
   bf16x8 kb[NKS];
   {
-    const f32x4 bq = *reinterpret_cast<const f32x4*>(&sB[16 * rb + 4 * gq]);
+    f32x4 pt[2];
 #pragma unroll
     for (int bc = 0; bc < NRB; ++bc) {
       f32x4 accA = zero4, accP = zero4;
       if (bc <= rb) {
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          const bf16x8 fb =
+          const bf16x8 fa =
               *reinterpret_cast<const bf16x8*>(sKi + ((size_t)(bc * NKS + s) * kWave + lane) * 8);
-          float ak[8], aq[8];
+          float bk[8], bqv[8];
           if (bc < rb) {
-            const f32x4* pm = reinterpret_cast<const f32x4*>(&sGm[rb][32 * s + 8 * gq]);
-            const f32x4* pc = reinterpret_cast<const f32x4*>(&sGm[bc][32 * s + 8 * gq]);
-            const f32x4 m0 = pm[0], m1 = pm[1], c0 = pc[0], c1 = pc[1];
+            const f32x4* pb = reinterpret_cast<const f32x4*>(
+                &sBT[rb * (rb - 1) / 2 + bc][32 * s + 8 * gq]);
+            const f32x4 t0v = pb[0], t1v = pb[1];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float sc = __expf(e < 4 ? m0[e] - c0[e] : m1[e - 4] - c1[e - 4]);
-              ak[e] = kf[s][e] * sc;
-              aq[e] = qf[s][e] * sc;
+              const float sc = e < 4 ? t0v[e] : t1v[e - 4];
+              bk[e] = kf[s][e] * sc;
+              bqv[e] = qf[s][e] * sc;
             }
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              ak[e] = kf[s][e];
-              aq[e] = qf[s][e];
+              bk[e] = kf[s][e];
+              bqv[e] = qf[s][e];
             }
           }
-          accA = M::mma(to_bf16x8(ak), fb, accA);
-          accP = M::mma(to_bf16x8(aq), fb, accP);
+          accA = M::mma(fa, to_bf16x8(bk), accA);
+          accP = M::mma(fa, to_bf16x8(bqv), accP);
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
+        f32x4 la;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = 16 * rb + 4 * gq + e, jj = 16 * bc + i;
-        if (bc <= rb) sL[rr][jj] = jj < rr ? bq[e] * accA[e] : 0.f;
-        blk[L::oP + (size_t)rr * CP + jj] = (bf16)(jj <= rr ? accP[e] : 0.f);
+        for (int e = 0; e < 4; ++e) {
+          const int jj = 16 * bc + 4 * gq + e;
+          la[e] = jj < r ? betav * accA[e] : 0.f;
+          accP[e] = jj <= r ? accP[e] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(&sL[r][16 * bc + 4 * gq]) = la;
+      }
+      pt[bc % 2] = accP;
+      if (bc % 2 == 1) {
+        const u32x4 pc = pair_piece(pt[0], pt[1], gq);
+        const int j0 = 16 * (bc - 1 + (gq & 1)) + 8 * (gq / 2);
+        *reinterpret_cast<u32x4*>(blk + L::oP + (size_t)r * CP + j0) = pc;
       }
     }
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const f32x4* pm = reinterpret_cast<const f32x4*>(&sGm[rb][32 * s + 8 * gq]);
-      const f32x4 m0 = pm[0], m1 = pm[1];
+      const f32x4* pb = reinterpret_cast<const f32x4*>(&sEB[rb][32 * s + 8 * gq]);
+      const f32x4 b0 = pb[0], b1 = pb[1];
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = betav * __expf(e < 4 ? m0[e] : m1[e - 4]) * kf[s][e];
+      for (int e = 0; e < 8; ++e) v[e] = betav * (e < 4 ? b0[e] : b1[e - 4]) * kf[s][e];
       kb[s] = to_bf16x8(v);
       asm volatile("" : "+v"(kb[s]));  // made here, so that k^ R dies here
     }
