@@ -41,6 +41,11 @@ template <int CTRL>
 __device__ __forceinline__ unsigned dpp(unsigned old, unsigned src) {
   return (unsigned)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, 0xF, 0xF, false);
 }
+// Lane value from `CTRL`'s source lane inside the row; 0 where it falls outside.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp0(unsigned src) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)src, CTRL, 0xF, 0xF, true);
+}
 template <int CTRL>
 __device__ __forceinline__ float dppf(float old, float src) {
   return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(unsigned, old),
@@ -269,8 +274,8 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
       u32x4 t1, t2, t3;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        t1[w] = dpp<kRowShr + 1>(dpp<kRowShl + 2>(0u, y[w]), x[w]);
-        t2[w] = dpp<kRowShr + 2>(dpp<kRowShl + 1>(0u, y[w]), x[w]);
+        t1[w] = dpp<kRowShr + 1>(dpp0<kRowShl + 2>(y[w]), x[w]);
+        t2[w] = dpp<kRowShr + 2>(dpp0<kRowShl + 1>(y[w]), x[w]);
         t3[w] = dpp<kRowShr + 3>(y[w], x[w]);
       }
 #pragma unroll
