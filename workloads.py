@@ -95,3 +95,43 @@ def make(name: str, **overrides) -> Inputs:
     inp = draw(**params)
     inp.meta["name"] = name
     return inp
+
+
+# ---------------------------------------------------------------------------
+# The stacked K3 KDA workload: 69 KDA layers, 16 sequences, 96 heads of
+# 128x128; each (layer, sequence) has a 32768-token prefill from a zero state
+# and zero ring, then 64 decode steps. It is far too large for host memory,
+# so it is drawn on the device, one (layer, sequence) at a time, with a
+# generator of that device seeded per (layer, sequence); the checked pairs
+# are copied back to the host for the oracle.
+STACK = dict(layers=69, B=16, T=32768, decode_steps=64, H=96, dk=128, dv=128)
+
+
+def stack_seed(layer: int, seq: int) -> int:
+    return 4_000_000 + 100 * layer + seq
+
+
+def draw_stack_seq(layer: int, seq: int, T: int, H: int, dk: int, dv: int,
+                   device) -> dict:
+    """Tokens 0..T-1 of one (layer, sequence): q, k, v bf16 [1, T, H, d],
+    g fp32 [1, T, H, dk], beta fp32 [1, T, H]; drawn in the order q, k, v,
+    g_raw, beta_raw with the distributions of the module docstring (g_mu 0)."""
+    gen = torch.Generator(device=device).manual_seed(stack_seed(layer, seq))
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
+
+    q = randn(1, T, H, dk).to(torch.bfloat16)
+    k = randn(1, T, H, dk).to(torch.bfloat16)
+    v = randn(1, T, H, dv).to(torch.bfloat16)
+    g = torch.nn.functional.logsigmoid(randn(1, T, H, dk))
+    beta = torch.sigmoid(randn(1, T, H))
+    return dict(q=q, k=k, v=v, g=g, beta=beta)
+
+
+def draw_stack_conv_w(layer: int, H: int, dk: int, dv: int, device) -> torch.Tensor:
+    """The conv weights of one layer, [H*(2dk+dv), 4] fp32 ~ 0.5 N(0, 1), from
+    the generator seeded 4,000,000 + 100 layer + 99 (no sequence uses 99)."""
+    gen = torch.Generator(device=device).manual_seed(4_000_000 + 100 * layer + 99)
+    return 0.5 * torch.randn(H * (2 * dk + dv), 4, generator=gen, dtype=torch.float32,
+                             device=device)
