@@ -10,7 +10,10 @@ short conv + SiLU + L2, decay, delta, rank-1 write and readout, fused in one
 kernel launch. Inputs for 256 consecutive steps are staged in HBM before the
 timed region; step i uses staged step i % 256. The chunked prefill of 4096
 tokens (batch 1, 96 heads, chunk 64, bf16) is timed separately in the same
-run and reported under "prefill". One JSON line is printed.
+run and reported under "prefill", and the 69-layer stack (16 sequences, one
+decode token through all 69 layers as one captured HIP graph over 6.5 GiB of
+state; one layer's 32768-token prefill of the 16 sequences) under "stack".
+One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -89,6 +92,99 @@ def measured_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
+def stack_bench(kda, workloads, torch, dev, args):
+    """The 69-layer stack of the K3 KDA layers (16 sequences, 96 heads of
+    128x128 per layer): one decode token through all layers, the 69 launches
+    captured in one HIP graph and replayed (each replay advances every
+    layer's state and ring); and one layer's 32768-token chunked prefill of
+    the 16 sequences. Inputs are drawn on the device with the stack recipe
+    and are resident before timing."""
+    cfg = workloads.STACK
+    L, B, T, H, dk, dv = (cfg[x] for x in ("layers", "B", "T", "H", "dk", "dv"))
+    bf = torch.bfloat16
+    gen = torch.Generator(device=dev).manual_seed(5)
+    states, xs, ws_ = [], [], []
+    for layer in range(L):
+        st = kda.KDAState(B, H, dk, dv, io=bf, device=dev)
+        st.S.normal_(0.0, 0.02, generator=gen)
+        st.ring.zero_()
+        states.append(st)
+        # one decode token per sequence: tokens 0..B-1 of the layer's draw
+        x = workloads.draw_stack_seq(layer, 0, B, H, dk, dv, dev)
+        xs.append({name: t[0].contiguous() for name, t in x.items()})
+        ws_.append(workloads.draw_stack_conv_w(layer, H, dk, dv, dev))
+    o = torch.empty(L, B, H, dv, dtype=bf, device=dev)
+
+    def stack_step():
+        for layer in range(L):
+            x = xs[layer]
+            states[layer].decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], ws_[layer],
+                                      o[layer])
+
+    stack_step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack_step()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.stack_reps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    step_s = ev0.elapsed_time(ev1) / 1e3 / args.stack_reps
+    assert all(torch.isfinite(st.S).all().item() for st in states)
+    dbytes = L * decode_bytes(B, H, dk, dv)
+    del graph, states, xs, o
+
+    # one layer's prefill of the 16 sequences, T = 32768
+    q = torch.empty(B, T, H, dk, dtype=bf, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty(B, T, H, dv, dtype=bf, device=dev)
+    g = torch.empty(B, T, H, dk, device=dev)
+    beta = torch.empty(B, T, H, device=dev)
+    for s_ in range(B):
+        x = workloads.draw_stack_seq(0, s_, T, H, dk, dv, dev)
+        for name, buf in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+            buf[s_].copy_(x[name][0])
+        del x
+    o = torch.empty(B, T, H, dv, dtype=bf, device=dev)
+    ws = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    pst = kda.KDAState(B, H, dk, dv, io=bf, device=dev)
+
+    def prefill():
+        pst.reset()
+        pst.prefill(T, q, k, v, g, beta, ws_[0], o, chunk=64, workspace=ws)
+
+    prefill()
+    torch.cuda.synchronize()
+    reps = 3
+    ev0.record()
+    for _ in range(reps):
+        prefill()
+    ev1.record()
+    torch.cuda.synchronize()
+    pre_s = ev0.elapsed_time(ev1) / 1e3 / reps
+    assert torch.isfinite(pst.S).all().item()
+    pbytes = prefill_bytes(B, T, H, dk, dv)
+    del q, k, v, g, beta, o, ws, pst
+    torch.cuda.empty_cache()
+    return {
+        "workload": "69 KDA layers x 16 sequences x 96 heads of 128x128 fp32 state "
+                    "(6.5 GiB), bf16 I/O; decode: one token through all layers (69 launches "
+                    "in one HIP graph); prefill: one layer, 32768 tokens per sequence, chunk 64",
+        "decode_stack_tokens_per_s": B / step_s, "decode_ms_per_stack_step": step_s * 1e3,
+        "decode_bytes_per_stack_step": dbytes, "decode_GBps": dbytes / step_s / 1e9,
+        "decode_hbm_frac": dbytes / step_s / 1e9 / HBM_PEAK_GBPS,
+        "prefill_layer_tokens_per_s": B * T / pre_s, "prefill_layer_ms": pre_s * 1e3,
+        "prefill_hbm_GBps": pbytes / pre_s / 1e9,
+        "prefill_stack_tokens_per_s": B * T / (L * pre_s),
+    }
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -100,6 +196,9 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--no-stack", action="store_true",
+                   help="skip the 69-layer stack measurements")
+    p.add_argument("--stack-reps", type=int, default=20)
     return p.parse_args()
 
 
@@ -180,6 +279,8 @@ def main():
     pflops = prefill_flops(pB, pT, pH, pdk, pdv, 64)
     assert torch.isfinite(pst.S).all().item()
 
+    stack = None if args.no_stack else stack_bench(kda, workloads, torch, dev, args)
+
     copy_gbps = None
     if args.calib_copy:
         n = 1 << 30
@@ -246,6 +347,7 @@ def main():
                     "tflops": pflops / (pre_ms / 1e3) / 1e12,
                     "mfma_frac": pflops / (pre_ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
                     "compulsory_bytes": pbytes, "flops": pflops},
+        "stack": stack,
         "decode_flops_per_step": decode_flops(B, H, dk, dv),
         "wall_s_timed_region": wall,
         "cpu_baseline": cpu,

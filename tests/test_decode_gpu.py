@@ -137,3 +137,42 @@ def test_decode_minus_inf_clears_and_reset_subset():
     torch.cuda.synchronize()
     assert torch.count_nonzero(st.S[1]) == 0 and torch.count_nonzero(st.ring[1]) == 0
     assert torch.equal(st.S[0], S_before[0]) and torch.equal(st.S[2], S_before[2])
+
+
+def test_decode_in_captured_graph_matches_eager():
+    """Decode steps captured in a HIP graph: each replay (with eager work and
+    synchronizations between replays) advances the state exactly as the same
+    launches issued eagerly do."""
+    dev = device()
+    inp = workloads.make("tiny", T=4, B=3, H=4, dk=128, dv=64, io="bf16", s0_random=True,
+                         ring_random=True, seed=81)
+    B, T, H, dk, dv = inp.dims
+    d = to_dev(inp, dev, step_major=True)
+    eager = kda.KDAState(B, H, dk, dv, io=torch.bfloat16, device=dev)
+    cap = kda.KDAState(B, H, dk, dv, io=torch.bfloat16, device=dev)
+    for st in (eager, cap):
+        load_state(st, inp)
+    oe = torch.empty(T, B, H, dv, dtype=torch.bfloat16, device=dev)
+    oc = torch.empty_like(oe)
+
+    def steps(st, o):
+        for t in range(T):
+            st.decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t],
+                           d["conv_w"], o[t])
+
+    steps(cap, oc)                  # warm-up, as eager
+    torch.cuda.synchronize()
+    load_state(cap, inp)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps(cap, oc)
+    load_state(cap, inp)            # capture does not run the launches
+    torch.cuda.synchronize()
+    for rep in range(4):
+        steps(eager, oe)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oc, oe), f"replay {rep}: o differs"
+        assert torch.equal(cap.S, eager.S) and torch.equal(cap.ring, eager.ring), \
+            f"replay {rep}: state differs"
