@@ -790,6 +790,187 @@ __global__ __launch_bounds__(kWave * NW) void prefill_chain_kernel(PrefillArgs a
   }
 }
 
+// chain, role-split form for bf16 operands, chunk 64 and d_k, d_v multiples
+// of 64: one workgroup of 8 waves per (64-column block, head, sequence).
+// Waves 0..3 own U/O row block w (all four column tiles); waves 4..7 own the
+// S row blocks w-4, w, w+4, ... (all column tiles). Every workspace operand
+// is loaded by exactly one wave, each SIMD runs one wave of each role, and
+// the operands of the next two chunks are in flight while a chunk runs.
+// Per chunk: S waves write S^T (bf16) to LDS | U/O waves: U = U' - W S,
+// O = Q~ S, U^T to LDS | U/O waves: O += P U, store O; S waves:
+// S = Diag(e^{Gam_n}) S + K^^T U. Measured at T = 4096, 96 heads of 128x128:
+// 134-143 us against 149-165 us for the generic form with 64-column blocks.
+template <int DK, int DV, typename IO>
+__global__ __launch_bounds__(512) void prefill_chain_roles_kernel(PrefillArgs a, int t0, int ncs,
+                                                                  const uint8_t* ws) {
+  constexpr int C = 64;
+  using M = MmaBf16;
+  using L = Ws<C, DK, DV, M>;
+  using MT = bf16;
+  using frag = bf16x8;
+  constexpr int DVB = 64, NCB = DVB / 16, KS = M::KS, KPL = M::KPL;
+  constexpr int NKS = DK / KS, NKP = C / KS, RS = DK / 64;
+  constexpr int LDST = DK + 8, LDUT = C + 8;
+  static_assert(DK % 64 == 0 && DV % 64 == 0 && L::DKP == DK && L::CP == C, "roles chain shape");
+  __shared__ __attribute__((aligned(16))) MT sST[DVB][LDST];  // S^T
+  __shared__ __attribute__((aligned(16))) MT sUT[DVB][LDUT];  // U^T
+  const int H = a.H, T = a.T, B = a.B;
+  constexpr int nblk = DV / DVB;
+  // Workgroup -> (column block, head, sequence), the column blocks of one
+  // head on one XCD when the (h, b) count allows it (as in the generic form).
+  int cbk, hb;
+  const int L1 = blockIdx.x;
+  const int HB = H * B;
+  if (HB % 8 == 0) {
+    const int xcd = L1 % 8, s = L1 / 8;
+    cbk = s % nblk;
+    hb = (s / nblk) * 8 + xcd;
+  } else {
+    cbk = L1 % nblk;
+    hb = L1 / nblk;
+  }
+  const int h = hb % H, b = hb / H;
+  const int cb0 = cbk * DVB;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l16 = lane % 16, koff = (lane / 16) * KPL, r4 = 4 * (lane / 16);
+  for (int idx = tid; idx < DVB * LDST; idx += 512) (&sST[0][0])[idx] = (MT)0.f;
+  for (int idx = tid; idx < DVB * LDUT; idx += 512) (&sUT[0][0])[idx] = (MT)0.f;
+  auto block = [&](int cl) {
+    return reinterpret_cast<const MT*>(ws + ((size_t)cl * B * H + (size_t)b * H + h) * L::bytes);
+  };
+  // Three operand sets rotated by a 3x unrolled loop: the loads of chunk
+  // c + 2 are issued before chunk c runs; indices are clamped, not branched
+  // on, so the loads are unconditional and the wait counts stay exact. Both
+  // roles pass the same two barriers per chunk.
+  auto walk = [&](auto& f0, auto& f1, auto& f2, auto&& load, auto&& step) {
+    load(f0, 0);
+    load(f1, min(1, ncs - 1));
+    for (int cl = 0; cl < ncs; cl += 3) {
+      load(f2, min(cl + 2, ncs - 1));
+      step(f0, cl);
+      if (cl + 1 >= ncs) break;
+      load(f0, min(cl + 3, ncs - 1));
+      step(f1, cl + 1);
+      if (cl + 2 >= ncs) break;
+      load(f1, min(cl + 4, ncs - 1));
+      step(f2, cl + 2);
+    }
+  };
+  __syncthreads();
+  if (wv < 4) {
+    const int rb = wv;  // U/O row block
+    struct F {
+      frag w[NKS], q[NKS], p[NKP];
+      bf16x4 u[NCB];
+    };
+    auto load = [&](F& f, int cl) {
+      const MT* blk = block(cl);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        f.w[ks] = M::ld(blk + L::oW + ((size_t)(rb * NKS + ks) * kWave + lane) * KPL);
+        f.q[ks] = M::ld(blk + L::oQ + ((size_t)(rb * NKS + ks) * kWave + lane) * KPL);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKP; ++ks)
+        f.p[ks] = M::ld(blk + L::oP + (size_t)(16 * rb + l16) * C + ks * KS + koff);
+#pragma unroll
+      for (int j = 0; j < NCB; ++j)
+        f.u[j] = M::ld4(blk + L::oU + ((size_t)(rb * (DV / 16) + cb0 / 16 + j) * kWave + lane) * 4);
+    };
+    auto step = [&](const F& cur, int cl) {
+      const int tstart = t0 + cl * C;
+      const int n = min(C, T - tstart);
+      __syncthreads();  // S^T of this chunk is in LDS
+      f32x4 accO[NCB];
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) {
+        accO[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 accU = M::cvt4(cur.u[j]);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const frag fs = M::ld(&sST[16 * j + l16][ks * KS + koff]);
+          accU = M::mma(cur.w[ks], fs, accU);
+          accO[j] = M::mma(cur.q[ks], fs, accO[j]);
+        }
+        M::st4(&sUT[16 * j + l16][16 * rb + r4], accU);
+      }
+      __syncthreads();  // U^T in LDS
+      // Rows past the chunk's last token fall outside the store resource.
+      const __amdgpu_buffer_rsrc_t orsrc =
+          make_rsrc(static_cast<IO*>(a.o) + (((long)b * T + tstart) * H + h) * DV + cb0,
+                    n * H * DV * (int)sizeof(IO));
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) {
+#pragma unroll
+        for (int ks = 0; ks < NKP; ++ks)
+          accO[j] = M::mma(cur.p[ks], M::ld(&sUT[16 * j + l16][ks * KS + koff]), accO[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          buf_store(orsrc, ((16 * rb + r4 + e) * H * DV + 16 * j + l16) * (int)sizeof(IO),
+                    accO[j][e], (IO*)nullptr);
+      }
+    };
+    F f0, f1, f2;
+    walk(f0, f1, f2, load, step);
+  } else {
+    const int sw = wv - 4;  // S row blocks sw + 4i
+    struct F {
+      frag k[RS][NKP];
+      f32x4 dn[RS];
+    };
+    auto load = [&](F& f, int cl) {
+      const MT* blk = block(cl);
+      const float* Dn = reinterpret_cast<const float*>(blk + L::nT);
+#pragma unroll
+      for (int i = 0; i < RS; ++i) {
+        const int rb = sw + 4 * i;
+#pragma unroll
+        for (int ks = 0; ks < NKP; ++ks)
+          f.k[i][ks] = M::ld(blk + L::oK + ((size_t)(rb * NKP + ks) * kWave + lane) * KPL);
+        f.dn[i] = *reinterpret_cast<const f32x4*>(Dn + 16 * rb + r4);
+      }
+    };
+    float* Sg = a.S + ((long)b * H + h) * DK * DV + cb0;
+    f32x4 accS[RS][NCB];
+#pragma unroll
+    for (int i = 0; i < RS; ++i)
+#pragma unroll
+      for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          accS[i][ct][e] = Sg[(long)(16 * (sw + 4 * i) + r4 + e) * DV + 16 * ct + l16];
+    auto step = [&](const F& cur, int) {
+#pragma unroll
+      for (int i = 0; i < RS; ++i)
+#pragma unroll
+        for (int ct = 0; ct < NCB; ++ct)
+          M::st4(&sST[16 * ct + l16][16 * (sw + 4 * i) + r4], accS[i][ct]);
+      __syncthreads();  // S^T in LDS
+      __syncthreads();  // U^T in LDS
+#pragma unroll
+      for (int i = 0; i < RS; ++i)
+#pragma unroll
+        for (int ct = 0; ct < NCB; ++ct) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) accS[i][ct][e] *= cur.dn[i][e];
+#pragma unroll
+          for (int ks = 0; ks < NKP; ++ks)
+            accS[i][ct] = M::mma(cur.k[i][ks], M::ld(&sUT[16 * ct + l16][ks * KS + koff]),
+                                 accS[i][ct]);
+        }
+    };
+    F f0, f1, f2;
+    walk(f0, f1, f2, load, step);
+#pragma unroll
+    for (int i = 0; i < RS; ++i)
+#pragma unroll
+      for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Sg[(long)(16 * (sw + 4 * i) + r4 + e) * DV + 16 * ct + l16] = accS[i][ct][e];
+  }
+}
+
 template <int C, int DK, int DV, typename IO, class M>
 hipError_t run(const PrefillArgs& a, uint8_t* ws, size_t ws_bytes, hipStream_t st) {
   using L = Ws<C, DK, DV, M>;
@@ -820,9 +1001,13 @@ hipError_t run(const PrefillArgs& a, uint8_t* ws, size_t ws_bytes, hipStream_t s
       e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_chain_kernel<C, DK, DV, DVB, CNW, 1, IO, M>),
-                       dim3((DV / DVB) * a.H * a.B), dim3(kWave * CNW), 0, st, a, t0, ncs,
-                       (const uint8_t*)ws);
+    if constexpr (sizeof(IO) == 2 && C == 64 && DK % 64 == 0 && DV % 64 == 0)
+      hipLaunchKernelGGL((prefill_chain_roles_kernel<DK, DV, IO>), dim3((DV / 64) * a.H * a.B),
+                         dim3(512), 0, st, a, t0, ncs, (const uint8_t*)ws);
+    else
+      hipLaunchKernelGGL((prefill_chain_kernel<C, DK, DV, DVB, CNW, 1, IO, M>),
+                         dim3((DV / DVB) * a.H * a.B), dim3(kWave * CNW), 0, st, a, t0, ncs,
+                         (const uint8_t*)ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
