@@ -81,6 +81,27 @@ constexpr size_t ws_block_bytes(int C, int DK, int DV, int KS, size_t esz) {
           (size_t)C * DV) * esz + (size_t)DK * 4;
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
+  return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
+// Two 16x16 tiles d0, d1 in the accumulator layout (lane: rows 4(l/16)+e,
+// column l%16), to one 16-byte piece per lane of 8 consecutive rows: lanes
+// with even l/16 take d0's rows 8(l/32)..+7, lanes with odd l/16 take d1's
+// (the partner lane is l^16).
+__device__ __forceinline__ u32x4 pair_piece(f32x4 d0, f32x4 d1, int gq) {
+  const u32x2 v0 = __builtin_bit_cast(u32x2, to_bf16x4(d0));
+  const u32x2 v1 = __builtin_bit_cast(u32x2, to_bf16x4(d1));
+  const bool odd = gq & 1;
+  const u32x2 send = odd ? v0 : v1;
+  const u32x2 recv = {(unsigned)__shfl_xor((int)send[0], 16, kWave),
+                      (unsigned)__shfl_xor((int)send[1], 16, kWave)};
+  return odd ? u32x4{recv[0], recv[1], v1[0], v1[1]} : u32x4{v0[0], v0[1], recv[0], recv[1]};
+}
+
 // X = (I + L)^{-1} for a strictly lower C x C matrix L (fp32, row stride
 // C + 4), by 16 x 16 blocks: forward substitution inside each diagonal block
 // (16 lanes of wave a for block a), then the block rows below the diagonal

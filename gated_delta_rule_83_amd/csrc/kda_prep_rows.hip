@@ -29,9 +29,6 @@
 namespace kda {
 namespace {
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kRowShr = 0x110;  // DPP row_shr:n is kRowShr + n
 constexpr int kRowShl = 0x100;  // DPP row_shl:n is kRowShl + n
 
@@ -63,24 +60,6 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* v) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) t[e] = (bf16)v[e];
   return t;
-}
-
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
-  return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-}
-
-// Two 16x16 tiles d0, d1 in the accumulator layout (lane: rows 4(l/16)+e,
-// column l%16), to one 16-byte piece per lane of 8 consecutive rows: lanes
-// with even l/16 take d0's rows 8(l/32)..+7, lanes with odd l/16 take d1's
-// (the partner lane is l^16).
-__device__ __forceinline__ u32x4 pair_piece(f32x4 d0, f32x4 d1, int gq) {
-  const u32x2 v0 = __builtin_bit_cast(u32x2, to_bf16x4(d0));
-  const u32x2 v1 = __builtin_bit_cast(u32x2, to_bf16x4(d1));
-  const bool odd = gq & 1;
-  const u32x2 send = odd ? v0 : v1;
-  const u32x2 recv = {(unsigned)__shfl_xor((int)send[0], 16, kWave),
-                      (unsigned)__shfl_xor((int)send[1], 16, kWave)};
-  return odd ? u32x4{recv[0], recv[1], v1[0], v1[1]} : u32x4{v0[0], v0[1], recv[0], recv[1]};
 }
 
 template <int C, int DK, int DV>
@@ -146,6 +125,11 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   const int t = tstart + r;
   const long row = ((long)b * T + min(t, T - 1)) * H + h;  // (b, token, h), clamped
   const bool do_l2 = !(a.flags & KDA_F_SKIP_L2);
+  // scale of the activations as computed (see the conv below) and the L2
+  // epsilon in that scale: (z ln2) / sqrt(sum (z ln2)^2 + eps) = z / sqrt(sum z^2 + eps / ln2^2)
+  constexpr float kLn2 = 0.69314718055994531f, kLog2e = 1.4426950408889634f;
+  constexpr float kAct = CONV ? kLn2 : 1.0f;
+  constexpr float kEps = CONV ? kL2Eps / (kLn2 * kLn2) : kL2Eps;
   bf16* blk = reinterpret_cast<bf16*>(ws + ((size_t)cl * a.B * H + (size_t)b * H + h) * L::bytes);
   float* Dn = reinterpret_cast<float*>(blk + L::nT);
 
@@ -227,7 +211,7 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
 #pragma unroll
     for (int u = 0; u < NWR; ++u) {
       const int idx = tid + u * NT;
-      if (idx < SM::NCH) sW[idx + idx / 8] = wreg[u];
+      if (idx < SM::NCH) sW[idx + idx / 8] = wreg[u] * kLog2e;
     }
   }
 
@@ -262,9 +246,13 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   if constexpr (CONV) __syncthreads();  // conv weights and history visible
 
   // ---- 1a. q, k, v: short conv + SiLU (taps by row shifts), L2 of q, k ----
-  // z = SiLU(w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t); tap x_{t-d} of
-  // lane j is x_t of lane j-d, or for j < d the history token j+3-d of the
-  // block, which lane j+3-d (< 3) reads from LDS.
+  // With y = w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t, SiLU(y) =
+  // y / (1 + e^{-y}). The weights in LDS are pre-scaled by log2(e), so the
+  // sum is u = y log2(e) and z = u / (1 + 2^{-u}) = SiLU(y) / ln 2; the 1/ln 2
+  // is taken out again by the L2 step (whose epsilon is scaled to match) or
+  // folded into beta for v. Tap x_{t-d} of lane j is x_t of lane j-d, or for
+  // j < d the history token j+3-d of the block, which lane j+3-d (< 3)
+  // reads from LDS.
   auto activate = [&](u32x4 x, int wbase, float* z) {
     if constexpr (CONV) {
       u32x4 y = *reinterpret_cast<const u32x4*>(&sHist[rb][i < 3 ? i : 2][wbase]);
@@ -282,7 +270,8 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
       for (int e = 0; e < 8; ++e) {
         const int wi = wbase + e;
         const f32x4 wt = sW[wi + wi / 8];
-        z[e] = silu(wt.x * bfe(t3, e) + wt.y * bfe(t2, e) + wt.z * bfe(t1, e) + wt.w * bfe(x, e));
+        const float u = wt.x * bfe(t3, e) + wt.y * bfe(t2, e) + wt.z * bfe(t1, e) + wt.w * bfe(x, e);
+        z[e] = u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u));
       }
     } else {
 #pragma unroll
@@ -295,7 +284,7 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
     float z[8];
     activate(xv[s], 2 * DK + 32 * s + 8 * gq, z);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] *= betav;
+    for (int e = 0; e < 8; ++e) z[e] *= betav * kAct;
     vb[s] = to_bf16x8(z);
     asm volatile("" : "+v"(vb[s]));
   }
@@ -321,8 +310,8 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
     sq += __shfl_xor(sq, 32, kWave);
     sk += __shfl_xor(sk, 16, kWave);
     sk += __shfl_xor(sk, 32, kWave);
-    const float iq = !valid ? 0.f : do_l2 ? __builtin_amdgcn_rsqf(sq + kL2Eps) : 1.f;
-    const float ik = !valid ? 0.f : do_l2 ? __builtin_amdgcn_rsqf(sk + kL2Eps) : 1.f;
+    const float iq = !valid ? 0.f : do_l2 ? __builtin_amdgcn_rsqf(sq + kEps) : kAct;
+    const float ik = !valid ? 0.f : do_l2 ? __builtin_amdgcn_rsqf(sk + kEps) : kAct;
 #pragma unroll
     for (int s = 0; s < NKS; ++s)
 #pragma unroll
