@@ -14,16 +14,17 @@
 // activations feed the Gram products from registers. Along a 16-lane DPP
 // row the lanes are consecutive tokens, so
 //   - the short convolution takes its three history taps with row shifts
-//     (lanes 0..2 load token t-3 once, which also serves lanes 1 and 2 of
-//     the shifted copies), and
+//     (lanes 0..2 of a row take the three tokens before the block from LDS:
+//     the previous block's last three, or those before the chunk), and
 //   - the in-block prefix sums of g are a 4-step row scan.
 // Transposes (token-contiguous operands for the contractions over tokens)
 // go through MFMAs with a 0/1 selection matrix as B: the product returns
 // four consecutive tokens of one channel per lane, exactly, and two lanes
 // (l and l^16) pair up into one 16-byte fragment piece.
 //
-// LDS holds only what crosses waves (about 51 KiB at C = 64, d = 128), so
-// several items share a CU and one item's loads overlap another's math.
+// LDS holds only what crosses waves (45 KiB at C = 64, d = 128, in three
+// regions reused from phase to phase) and the kernel is held to 168 VGPRs,
+// so three items share a CU and one item's loads overlap another's math.
 #include "kda_prefill.h"
 
 namespace kda {
@@ -85,6 +86,8 @@ struct RowsSmem {
   static constexpr size_t bytes = oC + nC;
 };
 
+// (launch bounds: C/16 waves, at least three waves per SIMD, i.e. three
+// items per CU)
 template <int C, int DK, int DV, bool CONV>
 __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs a, int t0, int ncs,
                                                                   uint8_t* ws) {
