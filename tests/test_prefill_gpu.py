@@ -213,3 +213,44 @@ def test_conv_prologue(io):
     assert abs_err(f64(qo), qh) <= tol and abs_err(f64(ko), kh) <= tol
     assert abs_err(f64(vo), vh) <= 1e-4 * max(1.0, np.abs(vh).max())
     np.testing.assert_array_equal(f64(ring_dev), ring)
+
+
+def test_prefill_in_captured_graph_matches_eager():
+    """A prefill call with a caller-provided workspace launches only kernels
+    (preparation, chain, ring advance), so it can be captured in a HIP graph:
+    each replay, with eager work and synchronizations between replays, gives
+    the eager result bit for bit."""
+    dev = device()
+    inp = workloads.make("tiny", T=150, B=2, H=2, dk=128, dv=128, io="bf16", s0_random=True,
+                         ring_random=True, seed=91)
+    B, T, H, dk, dv = inp.dims
+    d = to_dev(inp, dev)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(kda.make_dims(B, H, dk, dv, kda.KDA_BF16),
+                                                     T, 64), dtype=torch.uint8, device=dev)
+    eager = kda.KDAState(B, H, dk, dv, io=torch.bfloat16, device=dev)
+    cap = kda.KDAState(B, H, dk, dv, io=torch.bfloat16, device=dev)
+    oe = torch.empty(B, T, H, dv, dtype=torch.bfloat16, device=dev)
+    oc = torch.empty_like(oe)
+
+    def call(st, o):
+        st.prefill(T, d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], o, chunk=64,
+                   workspace=ws)
+
+    load_state(cap, inp)
+    call(cap, oc)                   # warm-up, eager
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(cap, oc)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        load_state(eager, inp)
+        call(eager, oe)
+        torch.cuda.synchronize()
+        load_state(cap, inp)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oc, oe), f"replay {rep}: o differs"
+        assert torch.equal(cap.S, eager.S) and torch.equal(cap.ring, eager.ring), \
+            f"replay {rep}: state differs"
