@@ -13,6 +13,11 @@ tokens (batch 1, 96 heads, chunk 64, bf16) is timed separately in the same
 run and reported under "prefill", and the 69-layer stack (16 sequences, one
 decode token through all 69 layers as one captured HIP graph over 6.5 GiB of
 state; one layer's 32768-token prefill of the 16 sequences) under "stack".
+Beside them: the latency of one K3-shape decode step (batch 1, fp32, warm and
+with the caches flushed) under "single_step", a plain 1 GiB device copy as
+the practical bandwidth ceiling ("copy_GBps", "roofline.frac_of_copy"), and
+the fp64 oracle timed on the host (all cores and one core on the decode
+workload, all cores on the 4096-token prefill) under "cpu_baseline".
 One JSON line is printed.
 """
 from __future__ import annotations
@@ -90,6 +95,43 @@ def measured_traffic():
     if rec.get("source_digest") != source_digest(DECODE_SOURCES):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def single_step_latency(kda, workloads, torch, dev, reps=20):
+    """One decode step of the K3 shape (batch 1, 96 heads of 128x128, fp32
+    I/O, 6 MiB of state): median latency of single launches, warm (state in
+    the caches) and flushed (a 512 MiB buffer written between launches)."""
+    inp = workloads.make("k3_decode1")
+    B, T, H, dk, dv = inp.dims
+    d = {name: getattr(inp, name)[:, 0].contiguous().to(dev)
+         for name in ("q", "k", "v", "g", "beta")}
+    w = inp.conv_w.to(dev)
+    st = kda.KDAState(B, H, dk, dv, io=torch.float32, device=dev)
+    st.S.copy_(inp.S0.to(dev))
+    st.ring.copy_(inp.ring0.to(dev))
+    o = torch.empty(B, H, dv, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def once(flushed):
+        if flushed:
+            flush.fill_(1)
+        torch.cuda.synchronize()
+        ev0.record()
+        st.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], w, o)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3
+
+    for _ in range(5):
+        once(False)
+    warm = sorted(once(False) for _ in range(reps))[reps // 2]
+    cold = sorted(once(True) for _ in range(reps))[reps // 2]
+    del flush
+    return {"workload": "one decode step, batch 1, 96 heads of 128x128 fp32 state (6 MiB), "
+                        "fp32 q/k/v/o; median of single launches",
+            "latency_us_warm": warm, "latency_us_flushed": cold,
+            "tokens_per_s_warm": 1e6 / warm, "tokens_per_s_flushed": 1e6 / cold}
 
 
 def stack_bench(kda, workloads, torch, dev, args):
@@ -195,7 +237,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--calib-copy", action="store_true",
-                   help="also run a plain 1 GiB device copy (counter calibration)")
+                   help="(kept for old command lines; the copy ceiling is always measured)")
     p.add_argument("--no-stack", action="store_true",
                    help="skip the 69-layer stack measurements")
     p.add_argument("--stack-reps", type=int, default=20)
@@ -281,20 +323,22 @@ def main():
 
     stack = None if args.no_stack else stack_bench(kda, workloads, torch, dev, args)
 
-    copy_gbps = None
-    if args.calib_copy:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
+    # ---------------- one K3-shape decode step: latency, warm and flushed ---
+    single = single_step_latency(kda, workloads, torch, dev)
+
+    # ---------------- practical HBM ceiling: a plain 1 GiB device copy ----
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(5):
         dst.copy_(src)
-        torch.cuda.synchronize()
-        ev0.record()
-        for _ in range(5):
-            dst.copy_(src)
-        ev1.record()
-        torch.cuda.synchronize()
-        copy_gbps = 2 * n * 5 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
-        del src, dst
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * n * 5 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
+    del src, dst
 
     # ---------------- CPU baseline: the fp64 oracle on a bounded sample -----
     cpu = None
@@ -317,6 +361,23 @@ def main():
                "sample": f"fp64 sequential oracle, first {n} of the 256 staged decode steps "
                          f"for all {B} sequences x {H} heads ({tn:.1f} s); includes the "
                          f"conversion of the inputs to float64"}
+        # the same oracle on one core (a short sample of the same workload)
+        n1 = 2
+        t1 = time.perf_counter()
+        kda_oracle.forward(inp.q[:, :n1], inp.k[:, :n1], inp.v[:, :n1], inp.g[:, :n1],
+                           inp.beta[:, :n1], inp.conv_w, inp.S0, inp.ring0, threads=1)
+        t1 = time.perf_counter() - t1
+        cpu["one_core"] = {"value": B * n1 / t1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"first {n1} decode steps, {B} sequences x {H} heads "
+                                     f"({t1:.1f} s)"}
+        # and on the 4096-token prefill workload, all of it
+        tp0 = time.perf_counter()
+        kda_oracle.forward(pin.q, pin.k, pin.v, pin.g, pin.beta, pin.conv_w, pin.S0, pin.ring0)
+        tp0 = time.perf_counter() - tp0
+        cpu["prefill"] = {"value": pT * pB / tp0, "unit": "tokens/s",
+                          "cores": kda_oracle.max_threads(),
+                          "sample": f"the whole 4096-token prefill workload, 96 heads, "
+                                    f"sequentially per head ({tp0:.1f} s)"}
 
     line = {
         "metric": METRIC,
@@ -352,8 +413,9 @@ def main():
         "wall_s_timed_region": wall,
         "cpu_baseline": cpu,
     }
-    if copy_gbps is not None:
-        line["copy_GBps"] = copy_gbps
+    line["copy_GBps"] = copy_gbps
+    line["roofline"]["frac_of_copy"] = achieved / copy_gbps
+    line["single_step"] = single
     print(json.dumps(line))
 
 
