@@ -176,3 +176,28 @@ def test_decode_in_captured_graph_matches_eager():
         assert torch.equal(oc, oe), f"replay {rep}: o differs"
         assert torch.equal(cap.S, eager.S) and torch.equal(cap.ring, eager.ring), \
             f"replay {rep}: state differs"
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(a, b) for a in (16, 32, 64, 128) for b in (16, 32, 64, 128)])
+def test_decode_every_shape(dk, dv, io):
+    """Every supported (d_k, d_v, I/O type): 6 decode steps for 2 sequences x 2
+    heads from a random state and ring, against the oracle."""
+    dev = device()
+    inp = workloads.make("tiny", T=6, B=2, H=2, dk=dk, dv=dv, io=io, s0_random=True,
+                         ring_random=True, seed=2000 + dk + 7 * dv + (1 if io == "bf16" else 0))
+    B, T, H, dk, dv = inp.dims
+    ref_o, ref_S, ref_ring = _oracle(inp)
+    st = kda.KDAState(B, H, dk, dv, io=torch.float32 if io == "f32" else torch.bfloat16,
+                      device=dev)
+    load_state(st, inp)
+    o = run_decode(st, to_dev(inp, dev, step_major=True), T)
+    torch.cuda.synchronize()
+    got = f64(o).transpose(1, 0, 2, 3)
+    if io == "f32":
+        eo, es = abs_err(got, ref_o), abs_err(f64(st.S), ref_S)
+        assert eo <= 1e-4 and es <= 1e-4, (eo, es)
+    else:
+        eo, es = rel_err(got, ref_o), rel_err(f64(st.S), ref_S)
+        assert eo <= 2e-2 and es <= 2e-2, (eo, es)
+    np.testing.assert_array_equal(f64(st.ring), ref_ring)

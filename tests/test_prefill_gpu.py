@@ -254,3 +254,27 @@ def test_prefill_in_captured_graph_matches_eager():
         assert torch.equal(oc, oe), f"replay {rep}: o differs"
         assert torch.equal(cap.S, eager.S) and torch.equal(cap.ring, eager.ring), \
             f"replay {rep}: state differs"
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dk,dv", [(a, b) for a in (16, 32, 64, 128) for b in (16, 32, 64, 128)])
+def test_prefill_every_shape(dk, dv, chunk, io):
+    """Every supported (d_k, d_v, chunk, I/O type), 70 tokens from a random
+    state and ring: each combination of preparation kernel (general or
+    token-row) and chain kernel (generic or role-split) that the dispatch can
+    choose, against the oracle."""
+    dev = device()
+    seed = 1000 + dk + 7 * dv + 13 * chunk + (1 if io == "bf16" else 0)
+    inp = workloads.make("tiny", T=70, B=1, H=2, dk=dk, dv=dv, io=io, s0_random=True,
+                         ring_random=True, seed=seed)
+    ref_o, ref_S, ref_ring = _oracle(inp)
+    tio = torch.float32 if io == "f32" else torch.bfloat16
+    st, o = _prefill(inp, dev, chunk, tio)
+    if io == "f32":
+        eo, es = abs_err(f64(o), ref_o), abs_err(f64(st.S), ref_S)
+        assert eo <= 1e-4 and es <= 1e-4, (eo, es)
+    else:
+        eo, es = rel_err(f64(o), ref_o), rel_err(f64(st.S), ref_S)
+        assert eo <= 2e-2 and es <= 2e-2, (eo, es)
+    np.testing.assert_array_equal(f64(st.ring), ref_ring)
