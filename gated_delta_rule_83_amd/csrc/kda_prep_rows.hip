@@ -119,8 +119,13 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   const int tid = threadIdx.x, lane = tid % kWave, rb = tid / kWave;
   const int i = lane % 16, gq = lane / 16;
   const int H = a.H, T = a.T;
+  // Items run chunk-major from the last chunk to the first (all heads of a
+  // chunk together), so that the workspace blocks of the first chunks, which
+  // the chain reads first, are the most recently written ones and still sit
+  // in the memory-side cache when the chain starts.
   const int item = blockIdx.x;
-  const int cl = item % ncs, h = (item / ncs) % H, b = item / (ncs * H);
+  const int hbi = item % (H * a.B);
+  const int cl = ncs - 1 - item / (H * a.B), h = hbi % H, b = hbi / H;
   const int tstart = t0 + cl * C;
   const int n = min(C, T - tstart);
   const int r = 16 * rb + i;  // this lane's token in the chunk
