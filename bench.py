@@ -197,19 +197,22 @@ def stack_bench(kda, workloads, torch, dev, args):
     ws = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     pst = kda.KDAState(B, H, dk, dv, io=bf, device=dev)
 
+    pst.reset()
+
     def prefill():
-        pst.reset()
         pst.prefill(T, q, k, v, g, beta, ws_[0], o, chunk=64, workspace=ws)
 
-    prefill()
-    torch.cuda.synchronize()
-    reps = 3
-    ev0.record()
-    for _ in range(reps):
+    for _ in range(2):
         prefill()
-    ev1.record()
     torch.cuda.synchronize()
-    pre_s = ev0.elapsed_time(ev1) / 1e3 / reps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(5)]
+    for e0, e1 in evs:
+        e0.record()
+        prefill()
+        e1.record()
+    torch.cuda.synchronize()
+    pre_s = sorted(e0.elapsed_time(e1) for e0, e1 in evs)[len(evs) // 2] / 1e3
     assert torch.isfinite(pst.S).all().item()
     pbytes = prefill_bytes(B, T, H, dk, dv)
     del q, k, v, g, beta, o, ws, pst
@@ -232,7 +235,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=16)
-    p.add_argument("--prefill-reps", type=int, default=10)
+    p.add_argument("--prefill-reps", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -308,15 +311,21 @@ def main():
     def prefill():
         pst.prefill(pT, pd["q"], pd["k"], pd["v"], pd["g"], pd["beta"], pw, po, chunk=64)
 
-    for _ in range(2):
+    # warm-up calls, then calls bracketed one by one by events on the launch
+    # stream (back to back, no host synchronization between them); the
+    # median call is reported
+    for _ in range(10):
         prefill()
     torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.prefill_reps):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.prefill_reps)]
+    for e0, e1 in evs:
+        e0.record()
         prefill()
-    ev1.record()
+        e1.record()
     torch.cuda.synchronize()
-    pre_ms = ev0.elapsed_time(ev1) / args.prefill_reps
+    calls_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    pre_ms = calls_ms[len(calls_ms) // 2]
     pbytes = prefill_bytes(pB, pT, pH, pdk, pdv)
     pflops = prefill_flops(pB, pT, pH, pdk, pdv, 64)
     assert torch.isfinite(pst.S).all().item()
@@ -403,6 +412,7 @@ def main():
                      "bytes_per_launch": dbytes, "avg_launch_us": per_launch_s * 1e6},
         "prefill": {"workload": "chunked prefill T=4096, batch 1, 96 heads, chunk 64, bf16",
                     "tokens_per_s": pT * pB / (pre_ms / 1e3), "ms": pre_ms,
+                    "ms_min": calls_ms[0], "ms_max": calls_ms[-1], "calls": len(calls_ms),
                     "hbm_GBps": pbytes / (pre_ms / 1e3) / 1e9,
                     "hbm_frac": pbytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
                     "tflops": pflops / (pre_ms / 1e3) / 1e12,
