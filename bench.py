@@ -12,7 +12,9 @@ timed region; step i uses staged step i % 256. The chunked prefill of 4096
 tokens (batch 1, 96 heads, chunk 64, bf16) is timed separately in the same
 run and reported under "prefill", and the 69-layer stack (16 sequences, one
 decode token through all 69 layers as one captured HIP graph over 6.5 GiB of
-state; one layer's 32768-token prefill of the 16 sequences) under "stack".
+state; one layer's 32768-token prefill of the 16 sequences) under "stack", and
+the same decode and prefill workloads with one decay per token and head
+(KDA_F_SCALAR_G, the scalar-alpha Gated DeltaNet form) under "scalar_decay".
 Beside them: the latency of one K3-shape decode step (batch 1, fp32, warm and
 with the caches flushed) under "single_step", a plain 1 GiB device copy as
 the practical bandwidth ceiling ("copy_GBps", "roofline.frac_of_copy"), and
@@ -37,12 +39,12 @@ METRIC = ("KDA tokens/s: decode (B×96h×128²) + prefill T=4K; "
           "HBM GB/s & MFMA % of peak")
 
 
-def decode_bytes(B, H, dk, dv, io_bytes=2):
+def decode_bytes(B, H, dk, dv, io_bytes=2, scalar_g=False):
     """Algorithmic HBM bytes of one decode launch (all B sequences)."""
     ctot = H * (2 * dk + dv)
     state = 2 * B * H * dk * dv * 4                   # read + write of S
     tok_in = B * H * (2 * dk + dv) * io_bytes          # raw q, k, v
-    gates = B * H * dk * 4 + B * H * 4                 # g, beta
+    gates = B * H * (1 if scalar_g else dk) * 4 + B * H * 4   # g, beta
     ring = 2 * B * 3 * ctot * io_bytes                 # ring read + write
     out = B * H * dv * io_bytes                        # o
     weights = ctot * 4 * 4                             # conv weights, once
@@ -54,9 +56,10 @@ def decode_flops(B, H, dk, dv):
     return B * H * 7 * dk * dv
 
 
-def prefill_bytes(B, T, H, dk, dv, io_bytes=2):
+def prefill_bytes(B, T, H, dk, dv, io_bytes=2, scalar_g=False):
     """Compulsory HBM bytes of a T-token prefill: inputs, outputs, S in/out."""
-    return (B * T * H * ((2 * dk + dv) * io_bytes + dk * 4 + 4 + dv * io_bytes)
+    g_bytes = 4 if scalar_g else dk * 4
+    return (B * T * H * ((2 * dk + dv) * io_bytes + g_bytes + 4 + dv * io_bytes)
             + 2 * B * H * dk * dv * 4)
 
 
@@ -244,7 +247,87 @@ def parse():
     p.add_argument("--no-stack", action="store_true",
                    help="skip the 69-layer stack measurements")
     p.add_argument("--stack-reps", type=int, default=20)
+    p.add_argument("--no-gdn", action="store_true",
+                   help="skip the scalar-decay (KDA_F_SCALAR_G) measurements")
     return p.parse_args()
+
+
+def gdn_bench(kda, workloads, torch, dev, args):
+    """The scalar-decay variant (KDA_F_SCALAR_G: one decay per token and head,
+    the scalar-alpha Gated DeltaNet form) on the same two workloads: 64
+    sequences x 96 heads x 128x128 bf16 decode (same step count and warm-up as
+    the headline) and the 4096-token chunk-64 prefill (median of event-
+    bracketed calls after 10 warm-up calls)."""
+    sg = kda.KDA_F_SCALAR_G
+    inp = workloads.make("batched_decode_gdn")
+    B, T, H, dk, dv = inp.dims
+    stg = {name: getattr(inp, name).transpose(0, 1).contiguous().to(dev)
+           for name in ("q", "k", "v", "g", "beta")}
+    conv_w = inp.conv_w.to(dev)
+    st = kda.KDAState(B, H, dk, dv, io=torch.bfloat16, device=dev)
+    st.S.copy_(inp.S0.to(dev))
+    st.ring.copy_(inp.ring0.to(dev))
+    o = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        j = i % T
+        st.decode_step(stg["q"][j], stg["k"][j], stg["v"][j], stg["g"][j], stg["beta"][j],
+                       conv_w, o, flags=sg)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    per_launch = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    assert torch.isfinite(st.S).all().item() and torch.isfinite(o.float()).all().item()
+    dbytes = decode_bytes(B, H, dk, dv, scalar_g=True)
+    st.close()
+    del stg, st
+
+    pin = workloads.make("prefill_4k_gdn")
+    pB, pT, pH, pdk, pdv = pin.dims
+    pd = {name: getattr(pin, name).contiguous().to(dev) for name in ("q", "k", "v", "g", "beta")}
+    pw = pin.conv_w.to(dev)
+    pst = kda.KDAState(pB, pH, pdk, pdv, io=torch.bfloat16, device=dev)
+    pst.reset()
+    po = torch.empty(pB, pT, pH, pdv, dtype=torch.bfloat16, device=dev)
+
+    def prefill():
+        pst.prefill(pT, pd["q"], pd["k"], pd["v"], pd["g"], pd["beta"], pw, po, chunk=64,
+                    flags=sg)
+
+    for _ in range(10):
+        prefill()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.prefill_reps)]
+    for e0, e1 in evs:
+        e0.record()
+        prefill()
+        e1.record()
+    torch.cuda.synchronize()
+    calls_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    pre_ms = calls_ms[len(calls_ms) // 2]
+    assert torch.isfinite(pst.S).all().item()
+    pbytes = prefill_bytes(pB, pT, pH, pdk, pdv, scalar_g=True)
+    pst.close()
+    return {
+        "workload": "KDA_F_SCALAR_G (one decay per token and head): the decode and prefill "
+                    "workloads above with g [B,T,H]",
+        "decode": {"tokens_per_s": B / per_launch, "avg_launch_us": per_launch * 1e6,
+                   "bytes_per_launch": dbytes, "hbm_GBps": dbytes / per_launch / 1e9,
+                   "hbm_frac": dbytes / per_launch / 1e9 / HBM_PEAK_GBPS},
+        "prefill": {"tokens_per_s": pT * pB / (pre_ms / 1e3), "ms": pre_ms,
+                    "ms_min": calls_ms[0], "ms_max": calls_ms[-1], "calls": len(calls_ms),
+                    "compulsory_bytes": pbytes,
+                    "hbm_GBps": pbytes / (pre_ms / 1e3) / 1e9,
+                    "hbm_frac": pbytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBPS},
+    }
 
 
 def main():
@@ -331,6 +414,7 @@ def main():
     assert torch.isfinite(pst.S).all().item()
 
     stack = None if args.no_stack else stack_bench(kda, workloads, torch, dev, args)
+    gdn = None if args.no_gdn else gdn_bench(kda, workloads, torch, dev, args)
 
     # ---------------- one K3-shape decode step: latency, warm and flushed ---
     single = single_step_latency(kda, workloads, torch, dev)
@@ -419,6 +503,7 @@ def main():
                     "mfma_frac": pflops / (pre_ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
                     "compulsory_bytes": pbytes, "flops": pflops},
         "stack": stack,
+        "scalar_decay": gdn,
         "decode_flops_per_step": decode_flops(B, H, dk, dv),
         "wall_s_timed_region": wall,
         "cpu_baseline": cpu,

@@ -71,11 +71,15 @@ size_t ring_bytes_of(const kda_dims* d) {
   return (size_t)d->batch * 3 * ctot_of(d) * io_size(d->io);
 }
 
-kda_status check_flags(uint32_t flags) {
-  if (flags & ~(KDA_F_SKIP_CONV | KDA_F_SKIP_L2))
-    return fail(KDA_ERR_INVALID, "unknown flag bits 0x%x", flags);
+// `allowed` is the set of flag bits the entry point understands.
+kda_status check_flags(uint32_t flags, uint32_t allowed) {
+  if (flags & ~allowed)
+    return fail(KDA_ERR_INVALID, "flag bits 0x%x are not valid for this call", flags & ~allowed);
   return KDA_OK;
 }
+
+constexpr uint32_t kPrologueFlags = KDA_F_SKIP_CONV | KDA_F_SKIP_L2;
+constexpr uint32_t kStepFlags = KDA_F_SKIP_CONV | KDA_F_SKIP_L2 | KDA_F_SCALAR_G;
 
 // Token tensors, g, beta and o are accessed per element (natural alignment);
 // conv weights, S, the ring and the workspace are accessed 16 bytes at a time.
@@ -196,7 +200,7 @@ kda_status kda_conv_prologue(const kda_dims* dims, int32_t T, const void* q, con
   g_err[0] = 0;
   kda_status st = check_dims(dims);
   if (st != KDA_OK) return st;
-  if ((st = check_flags(flags)) != KDA_OK) return st;
+  if ((st = check_flags(flags, kPrologueFlags)) != KDA_OK) return st;
   if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);
   if (T == 0) return KDA_OK;
   if ((long long)dims->batch * T * dims->heads > (1LL << 31) * 3)
@@ -229,7 +233,7 @@ kda_status kda_decode_step(kda_state* stt, const void* q, const void* k, const v
                            uint32_t flags, hipStream_t stream) {
   g_err[0] = 0;
   if (!stt) return fail(KDA_ERR_INVALID, "state is NULL");
-  kda_status st = check_flags(flags);
+  kda_status st = check_flags(flags, kStepFlags);
   if (st != KDA_OK) return st;
   const kda_dims* d = &stt->dims;
   const size_t esz = io_size(d->io);
@@ -262,7 +266,7 @@ kda_status kda_chunk_prefill(kda_state* stt, int32_t T, const void* q, const voi
                              size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
   g_err[0] = 0;
   if (!stt) return fail(KDA_ERR_INVALID, "state is NULL");
-  kda_status st = check_flags(flags);
+  kda_status st = check_flags(flags, kStepFlags);
   if (st != KDA_OK) return st;
   const kda_dims* d = &stt->dims;
   if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);

@@ -59,7 +59,7 @@ struct DecodeArgs {
   const void* q;         // [B][H][dk]
   const void* k;         // [B][H][dk]
   const void* v;         // [B][H][dv]
-  const float* g;        // [B][H][dk]
+  const float* g;        // [B][H][dk], or [B][H] with KDA_F_SCALAR_G
   const float* beta;     // [B][H]
   const float* conv_w;   // [Ctot][4]
   void* o;               // [B][H][dv]
@@ -96,7 +96,7 @@ struct PrefillArgs {
   const void* q;       // [B][T][H][dk]
   const void* k;
   const void* v;       // [B][T][H][dv]
-  const float* g;      // [B][T][H][dk]
+  const float* g;      // [B][T][H][dk], or [B][T][H] with KDA_F_SCALAR_G
   const float* beta;   // [B][T][H]
   const float* conv_w; // [Ctot][4]
   void* o;             // [B][T][H][dv]

@@ -83,10 +83,16 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
   }
   constexpr int GPT = (DK + NT - 1) / NT;  // decay channels per thread
   float gval[GPT];
+  if (a.flags & KDA_F_SCALAR_G) {  // one decay for every key channel of the head
+    const float gs = a.g[bh];
 #pragma unroll
-  for (int u = 0; u < GPT; ++u) {
-    const int i = tid + u * NT;
-    gval[u] = i < DK ? a.g[bh * DK + i] : 0.0f;
+    for (int u = 0; u < GPT; ++u) gval[u] = tid + u * NT < DK ? gs : 0.0f;
+  } else {
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+      const int i = tid + u * NT;
+      gval[u] = i < DK ? a.g[bh * DK + i] : 0.0f;
+    }
   }
   const float betav = a.beta[bh];
 

@@ -227,7 +227,14 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
       const long ts = (long)H * DK;
       const int tok0 = tstart + GS * gs;
       const float* gb = a.g + ((long)b * T * H + h) * DK + gc0;
-      if (tok0 + GS - 1 < T) {
+      if (a.flags & KDA_F_SCALAR_G) {  // one decay for every key channel of the head
+        const float* gh = a.g + (long)b * T * H + h;
+#pragma unroll
+        for (int r = 0; r < GS; ++r) {
+          const float gv = gh[(long)min(tok0 + r, T - 1) * H];
+          buf[r] = f32x4{gv, gv, gv, gv};
+        }
+      } else if (tok0 + GS - 1 < T) {
         const float* p = gb + (long)tok0 * ts;
 #pragma unroll
         for (int r = 0; r < GS; ++r, p += ts) buf[r] = *reinterpret_cast<const f32x4*>(p);

@@ -87,8 +87,9 @@ struct RowsSmem {
 };
 
 // (launch bounds: C/16 waves, at least three waves per SIMD, i.e. three
-// items per CU)
-template <int C, int DK, int DV, bool CONV>
+// items per CU). CONV: the inputs are raw projections (conv + SiLU here);
+// SG: g holds one decay per (token, head), shared by all key channels.
+template <int C, int DK, int DV, bool CONV, bool SG>
 __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs a, int t0, int ncs,
                                                                   uint8_t* ws) {
   using M = MmaBf16;
@@ -172,11 +173,17 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   }
 #pragma unroll
   for (int s = 0; s < NVS; ++s) xv[s] = *reinterpret_cast<const u32x4*>(vsrc + 32 * s);
-  const float* gsrc = a.g + row * DK + 8 * gq;
+  if constexpr (SG) {  // one decay for every key channel of the head
+    const float gv = a.g[row];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    gl[s][0] = *reinterpret_cast<const f32x4*>(gsrc + 32 * s);
-    gl[s][1] = *reinterpret_cast<const f32x4*>(gsrc + 32 * s + 4);
+    for (int s = 0; s < NKS; ++s) gl[s][0] = gl[s][1] = f32x4{gv, gv, gv, gv};
+  } else {
+    const float* gsrc = a.g + row * DK + 8 * gq;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      gl[s][0] = *reinterpret_cast<const f32x4*>(gsrc + 32 * s);
+      gl[s][1] = *reinterpret_cast<const f32x4*>(gsrc + 32 * s + 4);
+    }
   }
   if constexpr (CONV) {
     if (rb == 0 && i < 3) {
@@ -525,15 +532,23 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   }
 }
 
+template <int C, int DK, int DV, bool CONV>
+void launch_conv(const PrefillArgs& a, int t0, int ncs, uint8_t* ws, hipStream_t st) {
+  const dim3 grid((unsigned)((long)ncs * a.H * a.B)), block(C * 4);
+  if (a.flags & KDA_F_SCALAR_G)
+    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, CONV, true>), grid, block, 0, st,
+                       a, t0, ncs, ws);
+  else
+    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, CONV, false>), grid, block, 0, st,
+                       a, t0, ncs, ws);
+}
+
 template <int C, int DK, int DV>
 hipError_t launch_t(const PrefillArgs& a, int t0, int ncs, uint8_t* ws, hipStream_t st) {
-  const long items = (long)ncs * a.H * a.B;
   if (a.flags & KDA_F_SKIP_CONV)
-    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, false>), dim3((unsigned)items),
-                       dim3(C * 4), 0, st, a, t0, ncs, ws);
+    launch_conv<C, DK, DV, false>(a, t0, ncs, ws, st);
   else
-    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, true>), dim3((unsigned)items),
-                       dim3(C * 4), 0, st, a, t0, ncs, ws);
+    launch_conv<C, DK, DV, true>(a, t0, ncs, ws, st);
   return hipGetLastError();
 }
 

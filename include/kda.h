@@ -74,6 +74,15 @@ typedef struct {
 #define KDA_F_SKIP_CONV 1u /* q, k, v are already convolved and activated:
                               no conv, no SiLU, the ring is neither read nor written */
 #define KDA_F_SKIP_L2 2u   /* q, k are already unit-normalised: no L2 step */
+#define KDA_F_SCALAR_G 4u  /* kda_decode_step / kda_chunk_prefill only: g holds one
+                              log-decay per (sequence, token, head), shared by every
+                              key channel of the head (the scalar alpha of Gated
+                              DeltaNet): g is [B][H] for a decode step and [B][T][H]
+                              for a prefill. Source: "为什么 Kimi K3 敢把 KV Cache
+                              扔掉？…", section 6 (Gated Delta Net: one decay per
+                              token or head) and section 7 (KDA refines it to one
+                              per channel). The result equals the per-channel call
+                              with g repeated over d_k. */
 
 /* Opaque per-layer session state: S and the conv ring for B sequences. */
 typedef struct kda_state kda_state;
@@ -126,7 +135,8 @@ kda_status kda_state_get_dims(const kda_state* st, kda_dims* out);
  *  q_out, k_out: [B][T][H][d_k] fp32; v_out: [B][T][H][d_v] fp32.
  * Writes q^, k^ (conv, SiLU, L2) and v^ (conv, SiLU). With KDA_F_SKIP_CONV
  * the inputs are copied through (conv_w and ring may be NULL); with
- * KDA_F_SKIP_L2 q and k are not normalised. T = 0 is a no-op.
+ * KDA_F_SKIP_L2 q and k are not normalised; KDA_F_SCALAR_G (no g here) is
+ * rejected with KDA_ERR_INVALID. T = 0 is a no-op.
  * Source: section "KDA 递推公式先衰减再差分" (short conv, SiLU, L2). */
 kda_status kda_conv_prologue(const kda_dims* dims, int32_t T, const void* q,
                              const void* k, const void* v, const float* conv_w,
@@ -136,7 +146,8 @@ kda_status kda_conv_prologue(const kda_dims* dims, int32_t T, const void* q,
 /* One decode token for all B sequences of the state, fused in one pass over S:
  * conv + SiLU + L2 on this token, decay, delta read, rank-1 write, readout.
  *  q, k: [B][H][d_k] raw projections (io dtype); v: [B][H][d_v].
- *  g:    [B][H][d_k] fp32 natural-log decay (-inf allowed: clears the rows).
+ *  g:    [B][H][d_k] fp32 natural-log decay (-inf allowed: clears the rows);
+ *        [B][H] with KDA_F_SCALAR_G.
  *  beta: [B][H] fp32.
  *  conv_w: [Ctot][4] fp32 (NULL allowed with KDA_F_SKIP_CONV).
  *  o:    [B][H][d_v] io dtype (written).
@@ -159,6 +170,7 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chun
  *  g:    [B][T][H][d_k] fp32; precondition: finite and <= 0, and on every key
  *        channel the sum of g over any 16 consecutive tokens is >= -80
  *        (the intra-chunk decay factors must stay inside the fp32 range).
+ *        [B][T][H] with KDA_F_SCALAR_G (same precondition).
  *  beta: [B][T][H] fp32.  conv_w: [Ctot][4] fp32.
  *  o:    [B][T][H][d_v] io dtype (written).
  *  chunk: 16, 32 or 64 (64 recommended). T need not be a multiple of chunk.

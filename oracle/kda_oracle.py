@@ -20,6 +20,12 @@ Two independent formulations live here:
   (the cumulative in-chunk decay). It exists so that the chunked and
   sequential forms can be checked against each other.
 
+The decay g is per key channel. The scalar-alpha Gated DeltaNet form (one
+decay per token and head, same page, sections 6 and 7) is the case of g equal
+on every key channel of a head, so it is checked by passing g repeated over
+d_k; that the case reproduces the Gated DeltaNet update of section 7 is a
+pin of its own in the tests.
+
 Everything is float64. bf16 inputs are upcast exactly before they get here.
 """
 from __future__ import annotations

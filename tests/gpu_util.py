@@ -51,6 +51,18 @@ def subset(inp: workloads.Inputs, seqs, heads) -> workloads.Inputs:
         meta=dict(inp.meta, seqs=seqs, heads=heads))
 
 
+def per_channel_g(inp: workloads.Inputs) -> workloads.Inputs:
+    """A scalar-decay workload (g [B, T, H]) with g repeated over the d_k key
+    channels ([B, T, H, d_k]): the per-channel form the oracle and the
+    per-channel library call take."""
+    if inp.g.dim() == 4:
+        return inp
+    dk = inp.q.shape[-1]
+    g = inp.g.unsqueeze(-1).expand(*inp.g.shape, dk).contiguous()
+    return workloads.Inputs(q=inp.q, k=inp.k, v=inp.v, g=g, beta=inp.beta, conv_w=inp.conv_w,
+                            S0=inp.S0, ring0=inp.ring0, meta=dict(inp.meta, scalar_g=False))
+
+
 def to_dev(inp: workloads.Inputs, dev, step_major=False):
     """Device copies. step_major=True lays q, k, v, g, beta out as [T, B, ...]
     so that each decode step's inputs are contiguous."""
@@ -68,7 +80,7 @@ def load_state(st, inp: workloads.Inputs):
     st.ring.copy_(inp.ring0.to(st.ring.device, st.ring.dtype))
 
 
-def run_decode(st, d, T, o_all=None):
+def run_decode(st, d, T, o_all=None, flags=0):
     """T decode steps from step-major device inputs; returns o [T, B, H, dv]."""
     B, H = d["q"].shape[1], d["q"].shape[2]
     dv = d["v"].shape[-1]
@@ -76,5 +88,5 @@ def run_decode(st, d, T, o_all=None):
         o_all = torch.empty(T, B, H, dv, dtype=st.io, device=d["q"].device)
     for t in range(T):
         st.decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t], d["conv_w"],
-                       o_all[t])
+                       o_all[t], flags=flags)
     return o_all

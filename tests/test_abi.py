@@ -119,6 +119,22 @@ def test_prefill_validation(fake_state):
     assert "below" in kda.last_error()
 
 
+def test_scalar_decay_flag_validation(fake_state):
+    """KDA_F_SCALAR_G is a flag of the decode step and the prefill only: there
+    validation goes on past it (to the NULL q here); the prologue rejects it."""
+    sg = kda.KDA_F_SCALAR_G
+    assert call_decode(fake_state, q=None, flags=sg) == K.KDA_ERR_INVALID
+    assert "q is NULL" in kda.last_error()
+    assert call_decode(fake_state, flags=sg | 8) == K.KDA_ERR_INVALID
+    assert call_prefill(fake_state, q=None, flags=sg | kda.KDA_F_SKIP_CONV) == K.KDA_ERR_INVALID
+    assert "q is NULL" in kda.last_error()
+    assert call_prefill(fake_state, T=0, flags=sg) == K.KDA_OK
+    d = kda.make_dims(1, 2, 16, 16, kda.KDA_F32)
+    assert kda.lib().kda_conv_prologue(ctypes.byref(d), 4, *([_vp(FAKE)] * 8), sg,
+                                       None) == K.KDA_ERR_INVALID
+    assert "0x4" in kda.last_error()
+
+
 def test_reset_validation(fake_state):
     arr = (ctypes.c_int32 * 2)(0, 5)
     assert kda.lib().kda_state_reset(fake_state, arr, 2, None) == K.KDA_ERR_INVALID

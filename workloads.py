@@ -10,7 +10,8 @@ workload, in a fixed order:
     q, k, v, g_raw, beta_raw, conv_w, S0 (if random), ring (if random)
 
 with q, k, v ~ N(0, 1) of shape [B, T, H, d]; g = logsigmoid(g_mu + N(0, 1))
-per key channel [B, T, H, dk]; beta = sigmoid(N(0, 1)) [B, T, H]; conv
+per key channel [B, T, H, dk] (with scalar_g, one per token and head:
+[B, T, H], the scalar-alpha Gated DeltaNet form); beta = sigmoid(N(0, 1)) [B, T, H]; conv
 weights ~ 0.5 * N(0, 1) of shape [H*(2dk+dv), 4]; S0 ~ 0.02 * N(0, 1) of
 shape [B, H, dk, dv]; ring ~ N(0, 1) of shape [B, 3, H*(2dk+dv)]. For
 bf16 workloads q, k, v and the ring are rounded to bf16 (round to nearest
@@ -41,6 +42,14 @@ WORKLOADS = {
     # Chunked prefill of 4096 tokens, chunk 64, slow decay, bf16 I/O.
     "prefill_4k": dict(B=1, T=4096, H=96, dk=128, dv=128, io="bf16", seed=3,
                        s0_random=False, ring_random=False, g_mu=2.0, chunk=64),
+    # The same two workloads with one decay per token and head (scalar-alpha
+    # Gated DeltaNet), g of shape [B, T, H].
+    "batched_decode_gdn": dict(B=64, T=256, H=96, dk=128, dv=128, io="bf16", seed=5,
+                               s0_random=True, ring_random=True, g_mu=0.0, chunk=64,
+                               scalar_g=True),
+    "prefill_4k_gdn": dict(B=1, T=4096, H=96, dk=128, dv=128, io="bf16", seed=6,
+                           s0_random=False, ring_random=False, g_mu=2.0, chunk=64,
+                           scalar_g=True),
 }
 
 
@@ -64,7 +73,7 @@ class Inputs:
 
 
 def draw(B, T, H, dk, dv, io="f32", seed=0, s0_random=False, ring_random=False,
-         g_mu=0.0, **meta) -> Inputs:
+         g_mu=0.0, scalar_g=False, **meta) -> Inputs:
     gen = torch.Generator(device="cpu").manual_seed(int(seed))
     ctot = H * (2 * dk + dv)
 
@@ -74,7 +83,8 @@ def draw(B, T, H, dk, dv, io="f32", seed=0, s0_random=False, ring_random=False,
     q = randn(B, T, H, dk)
     k = randn(B, T, H, dk)
     v = randn(B, T, H, dv)
-    g = torch.nn.functional.logsigmoid(randn(B, T, H, dk) + float(g_mu))
+    g_shape = (B, T, H) if scalar_g else (B, T, H, dk)
+    g = torch.nn.functional.logsigmoid(randn(*g_shape) + float(g_mu))
     beta = torch.sigmoid(randn(B, T, H))
     conv_w = 0.5 * randn(ctot, 4)
     S0 = 0.02 * randn(B, H, dk, dv) if s0_random else torch.zeros(B, H, dk, dv)
@@ -83,7 +93,8 @@ def draw(B, T, H, dk, dv, io="f32", seed=0, s0_random=False, ring_random=False,
         q, k, v, ring0 = (x.to(torch.bfloat16) for x in (q, k, v, ring0))
     elif io != "f32":
         raise ValueError(f"io must be 'f32' or 'bf16', not {io!r}")
-    info = dict(B=B, T=T, H=H, dk=dk, dv=dv, io=io, seed=seed, g_mu=g_mu, **meta)
+    info = dict(B=B, T=T, H=H, dk=dk, dv=dv, io=io, seed=seed, g_mu=g_mu, scalar_g=scalar_g,
+                **meta)
     return Inputs(q, k, v, g, beta, conv_w, S0, ring0, info)
 
 
