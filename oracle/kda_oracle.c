@@ -254,3 +254,32 @@ int kdao_prologue(int B, int T, int H, int dk, int dv,
   }
   return 0;
 }
+
+/* Output gate after the readout (a separate step, not part of the recurrence):
+ * a gated RMSNorm of each head's readout vector. The C engine of "KV缓存从
+ * 11.25GB缩到0.21GB：WARP中Kimi Delta Attention线性注意力原理剖析" lists a gated
+ * RMSNorm beside the KDA decode step (section "相关源码与文档导航"), and "为什么
+ * Kimi K3 敢把 KV Cache 扔掉？…" section 6 adds a gate on the output for feature
+ * scaling; neither prints the formula. The reading taken here: per row (one
+ * token of one head) of n values x with gate pre-activations z,
+ *
+ *   y[j] = x[j] / sqrt(mean_j x[j]^2 + eps) * w[j] * sigmoid(z[j]),
+ *
+ * sigmoid(z) = 1 / (1 + exp(-z)), w a weight vector of length n shared by the
+ * heads. x, z, y are [rows][n]; y may equal x. */
+int kdao_gated_rmsnorm(long rows, int n, const double *x, const double *z,
+                       const double *w, double eps, double *y) {
+  if (rows < 0 || n <= 0 || !x || !z || !w || !y) return -1;
+  for (long r = 0; r < rows; ++r) {
+    const double *xr = x + r * n, *zr = z + r * n;
+    double *yr = y + r * n;
+    double ss = 0.0;
+    for (int j = 0; j < n; ++j) ss += xr[j] * xr[j];
+    const double rms = sqrt(ss / n + eps);
+    for (int j = 0; j < n; ++j) {
+      const double gate = 1.0 / (1.0 + exp(-zr[j]));
+      yr[j] = xr[j] / rms * w[j] * gate;
+    }
+  }
+  return 0;
+}

@@ -20,6 +20,10 @@ Two independent formulations live here:
   (the cumulative in-chunk decay). It exists so that the chunked and
   sequential forms can be checked against each other.
 
+A third function, :meth:`Oracle.gated_rmsnorm`, is the output gate that
+follows the readout (a gated RMSNorm per token and head; its formula is a
+reading, stated in ``kda_oracle.c``).
+
 The decay g is per key channel. The scalar-alpha Gated DeltaNet form (one
 decay per token and head, same page, sections 6 and 7) is the case of g equal
 on every key channel of a head, so it is checked by passing g repeated over
@@ -76,6 +80,9 @@ class Oracle:
         lib.kdao_prologue.argtypes = ([ctypes.c_int] * 5 + [dp] * 8
                                       + [ctypes.c_int, ctypes.c_double, ctypes.c_int])
         lib.kdao_prologue.restype = ctypes.c_int
+        lib.kdao_gated_rmsnorm.argtypes = [ctypes.c_long, ctypes.c_int, dp, dp, dp,
+                                           ctypes.c_double, dp]
+        lib.kdao_gated_rmsnorm.restype = ctypes.c_int
         lib.kdao_max_threads.argtypes = []
         lib.kdao_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -141,6 +148,20 @@ class Oracle:
             raise RuntimeError("kdao_prologue failed")
         return qo, ko, vo, ring
 
+    def gated_rmsnorm(self, x, z, w, eps):
+        """Output gate on readout vectors: x, z [..., n] (rows of n values: one
+        token of one head), w [n]. Returns y [..., n] in float64,
+        y = x / sqrt(mean(x^2) + eps) * w * sigmoid(z) per row."""
+        x, z, w = map(_f64, (x, z, w))
+        n = x.shape[-1]
+        assert z.shape == x.shape and w.shape == (n,)
+        y = np.empty_like(x)
+        rc = self.lib.kdao_gated_rmsnorm(x.size // n, n, _ptr(x), _ptr(z), _ptr(w),
+                                         float(eps), _ptr(y))
+        if rc != 0:
+            raise RuntimeError("kdao_gated_rmsnorm failed")
+        return y
+
     def chunked_core(self, *args, **kwargs):
         return chunked_core(*args, **kwargs)
 
@@ -169,6 +190,10 @@ def core(*args, **kwargs):
 
 def prologue(*args, **kwargs):
     return default().prologue(*args, **kwargs)
+
+
+def gated_rmsnorm(*args, **kwargs):
+    return default().gated_rmsnorm(*args, **kwargs)
 
 
 def chunked_core(qh, kh, vh, g, beta, S0, chunk):

@@ -315,6 +315,59 @@ def pin_transition_product(orc):
     np.testing.assert_allclose(S[0, 0], St, atol=1e-12)
 
 
+# --------------------------------------------------------------------------
+# Output gate (gated RMSNorm after the readout; [WARP] "相关源码与文档导航"
+# names it, [K3] section 6 gates the output; the formula is a reading):
+# y = x / sqrt(mean x^2 + eps) * w * sigmoid(z) per (token, head) row.
+def pin_gated_rmsnorm_library(orc):
+    """Against torch's own RMSNorm and sigmoid (float64), several eps values."""
+    rng = np.random.default_rng(71)
+    for n, eps in ((16, 1e-6), (128, 1e-5), (32, 0.5)):
+        x = rng.standard_normal((3, 5, 2, n)) * rng.uniform(0.1, 3.0, (3, 5, 2, 1))
+        z = 2.0 * rng.standard_normal((3, 5, 2, n))
+        w = 1.0 + 0.3 * rng.standard_normal(n)
+        y = orc.gated_rmsnorm(x, z, w, eps)
+        xt, zt, wt = (torch.from_numpy(a) for a in (x, z, w))
+        want = torch.nn.functional.rms_norm(xt, (n,), wt, eps) * torch.sigmoid(zt)
+        np.testing.assert_allclose(y, want.numpy(), rtol=1e-13, atol=1e-14)
+
+
+def pin_gated_rmsnorm_closed_forms(orc):
+    rng = np.random.default_rng(72)
+    n = 24
+    x = rng.standard_normal((6, n)) * np.array([0.01, 0.1, 1, 3, 10, 100])[:, None]
+    ones = np.ones(n)
+    big = np.full_like(x, 60.0)               # sigmoid(60) = 1 - 9e-27
+    # open gate, unit weights, eps = 0: every row has mean square exactly 1
+    y = orc.gated_rmsnorm(x, big, ones, 0.0)
+    np.testing.assert_allclose((y * y).mean(-1), 1.0, rtol=1e-14)
+    # with eps > 0 the mean square is m / (m + eps), m the row's mean square
+    m = (x * x).mean(-1)
+    y = orc.gated_rmsnorm(x, big, ones, 0.25)
+    np.testing.assert_allclose((y * y).mean(-1), m / (m + 0.25), rtol=1e-13)
+    # scale invariance at eps = 0, and the row direction is kept
+    y1 = orc.gated_rmsnorm(x, big, ones, 0.0)
+    y2 = orc.gated_rmsnorm(7.5 * x, big, ones, 0.0)
+    np.testing.assert_allclose(y1, y2, rtol=1e-13)
+    np.testing.assert_allclose(y1 * np.sqrt(m)[:, None], x, rtol=1e-13)
+    # a closed gate (z = 0) halves everything; the weight scales per channel
+    w = np.linspace(0.5, 2.0, n)
+    z0 = np.zeros_like(x)
+    np.testing.assert_allclose(orc.gated_rmsnorm(x, z0, w, 0.0), 0.5 * w * y1, rtol=1e-13)
+    # gate values per channel: z -> -inf shuts a channel, the others are unchanged
+    z = big.copy()
+    z[:, 3] = -800.0
+    y = orc.gated_rmsnorm(x, z, ones, 0.0)
+    assert np.all(y[:, 3] == 0.0)
+    np.testing.assert_allclose(np.delete(y, 3, -1), np.delete(y1, 3, -1), rtol=1e-13)
+    # rows are independent: changing one row changes no other row
+    x2 = x.copy()
+    x2[2] *= -4.0
+    x2[2, 0] += 1.0
+    y = orc.gated_rmsnorm(x2, big, ones, 0.0)
+    np.testing.assert_array_equal(np.delete(y, 2, 0), np.delete(y1, 2, 0))
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_zero_decay_is_delta_rule,
@@ -328,4 +381,6 @@ ALL_PINS = [
     pin_stability_bound,
     pin_columns_and_linearity,
     pin_transition_product,
+    pin_gated_rmsnorm_library,
+    pin_gated_rmsnorm_closed_forms,
 ]

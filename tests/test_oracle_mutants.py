@@ -45,6 +45,14 @@ MUTANTS = {
     "ring_history_reversed": [("return ring_b[(long)(3 + s) * Ctot + c];",
                                "return ring_b[(long)(-1 - s) * Ctot + c];")],
     "ring_not_saved": [("ring_update(T, H, dk, dv, b, h, q, k, v, ring);\n    free", "free")],
+    # the output gate
+    "rms_sum_not_mean": [("sqrt(ss / n + eps)", "sqrt(ss + eps)")],
+    "rms_no_sqrt": [("sqrt(ss / n + eps)", "(ss / n + eps)")],
+    "rms_eps_outside_sqrt": [("sqrt(ss / n + eps)", "(sqrt(ss / n) + eps)")],
+    "gate_swish": [("yr[j] = xr[j] / rms * w[j] * gate;", "yr[j] = xr[j] / rms * w[j] * gate * zr[j];")],
+    "gate_missing": [("yr[j] = xr[j] / rms * w[j] * gate;", "yr[j] = xr[j] / rms * w[j];")],
+    "gate_sign": [("1.0 / (1.0 + exp(-zr[j]))", "1.0 / (1.0 + exp(zr[j]))")],
+    "norm_weight_missing": [("yr[j] = xr[j] / rms * w[j] * gate;", "yr[j] = xr[j] / rms * gate;")],
 }
 
 
