@@ -14,7 +14,9 @@ run and reported under "prefill", and the 69-layer stack (16 sequences, one
 decode token through all 69 layers as one captured HIP graph over 6.5 GiB of
 state; one layer's 32768-token prefill of the 16 sequences) under "stack", and
 the same decode and prefill workloads with one decay per token and head
-(KDA_F_SCALAR_G, the scalar-alpha Gated DeltaNet form) under "scalar_decay".
+(KDA_F_SCALAR_G, the scalar-alpha Gated DeltaNet form) under "scalar_decay",
+and the output gate (gated RMSNorm of the readout: fused into the decode step,
+and as its own kernel on the prefill output) under "output_gate".
 Beside them: the latency of one K3-shape decode step (batch 1, fp32, warm and
 with the caches flushed) under "single_step", a plain 1 GiB device copy as
 the practical bandwidth ceiling ("copy_GBps", "roofline.frac_of_copy"), and
@@ -381,6 +383,30 @@ def main():
     achieved = dbytes / per_launch_s / 1e9
     assert torch.isfinite(st.S).all().item() and torch.isfinite(o.float()).all().item()
 
+    # the same steps with the output gate fused into the readout (continuing
+    # from the state the timed steps left)
+    gz, gw, geps = workloads.draw_output_gate(B, T, H, dv, "bf16", seed=2)
+    gz = gz.transpose(0, 1).contiguous().to(dev)
+    gw = gw.to(dev)
+
+    def gated_step(i):
+        j = i % T
+        st.decode_step_gated(stg["q"][j], stg["k"][j], stg["v"][j], stg["g"][j],
+                             stg["beta"][j], conv_w, gz[j], gw, geps, o)
+
+    for i in range(args.warmup):
+        gated_step(i)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        gated_step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    gated_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    gated_bytes = dbytes + B * H * dv * 2 + dv * 4     # + the gate inputs and weights
+    assert torch.isfinite(o.float()).all().item()
+    del gz
+
     # ---------------- prefill: T=4096, 96 heads, chunk 64, bf16 ------------
     pin = workloads.make("prefill_4k")
     pB, pT, pH, pdk, pdv = pin.dims
@@ -412,6 +438,26 @@ def main():
     pbytes = prefill_bytes(pB, pT, pH, pdk, pdv)
     pflops = prefill_flops(pB, pT, pH, pdk, pdv, 64)
     assert torch.isfinite(pst.S).all().item()
+
+    # the output gate as its own kernel on the prefill's output (one read of
+    # o and of the gate, one write; out of place so every call sees the same
+    # input)
+    pz, pwn, peps = workloads.draw_output_gate(pB, pT, pH, pdv, "bf16", seed=3)
+    pz, pwn = pz.to(dev), pwn.to(dev)
+    py = torch.empty_like(po)
+    for _ in range(10):
+        pst.gated_rmsnorm(pT, po, pz, pwn, peps, py)
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        pst.gated_rmsnorm(pT, po, pz, pwn, peps, py)
+        e1.record()
+    torch.cuda.synchronize()
+    gate_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    gate_med = gate_ms[len(gate_ms) // 2]
+    gate_bytes = 3 * pB * pT * pH * pdv * 2 + pdv * 4
+    assert torch.isfinite(py.float()).all().item()
+    del pz, py
 
     stack = None if args.no_stack else stack_bench(kda, workloads, torch, dev, args)
     gdn = None if args.no_gdn else gdn_bench(kda, workloads, torch, dev, args)
@@ -504,6 +550,20 @@ def main():
                     "compulsory_bytes": pbytes, "flops": pflops},
         "stack": stack,
         "scalar_decay": gdn,
+        "output_gate": {
+            "workload": "gated RMSNorm of each head's readout (sigmoid gate, shared weight, "
+                        "eps 1e-5): fused into the decode step (64 sequences, same steps), "
+                        "and as its own kernel on the 4096-token prefill output",
+            "decode_tokens_per_s": B / gated_launch_s,
+            "decode_avg_launch_us": gated_launch_s * 1e6,
+            "decode_hbm_frac": gated_bytes / gated_launch_s / 1e9 / HBM_PEAK_GBPS,
+            "epilogue_kernel": "gated_rmsnorm_kernel<128,bf16>",
+            "epilogue_us": gate_med * 1e3, "epilogue_us_min": gate_ms[0] * 1e3,
+            "epilogue_bytes": gate_bytes,
+            "epilogue_GBps": gate_bytes / (gate_med / 1e3) / 1e9,
+            "epilogue_hbm_frac": gate_bytes / (gate_med / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "prefill_with_gate_tokens_per_s": pT * pB / ((pre_ms + gate_med) / 1e3),
+        },
         "decode_flops_per_step": decode_flops(B, H, dk, dv),
         "wall_s_timed_region": wall,
         "cpu_baseline": cpu,

@@ -1,6 +1,7 @@
 // C ABI of the KDA library: argument validation, state handles, dispatch.
 // Every entry point validates fully before it enqueues anything, returns a
 // kda_status, and never lets a C++ exception escape.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -91,6 +92,33 @@ constexpr uint32_t kStepFlags = KDA_F_SKIP_CONV | KDA_F_SKIP_L2 | KDA_F_SCALAR_G
   } while (0)
 
 constexpr size_t kDefaultWsCap = (size_t)2 << 30;  // 2 GiB
+
+kda_status check_eps(float eps) {
+  if (!(eps > 0.0f) || !(eps < INFINITY))
+    return fail(KDA_ERR_INVALID, "eps = %g must be finite and > 0", (double)eps);
+  return KDA_OK;
+}
+
+// Shared by kda_decode_step and kda_decode_step_gated (gate == NULL: plain).
+kda_status decode_common(kda_state* stt, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* conv_w,
+                         const void* gate, const float* norm_w, float eps, void* o,
+                         uint32_t flags, hipStream_t stream) {
+  const kda_dims* d = &stt->dims;
+  const size_t esz = io_size(d->io);
+  KDA_REQUIRE_PTR(q, "q", esz);
+  KDA_REQUIRE_PTR(k, "k", esz);
+  KDA_REQUIRE_PTR(v, "v", esz);
+  KDA_REQUIRE_PTR(g, "g", 4);
+  KDA_REQUIRE_PTR(beta, "beta", 4);
+  KDA_REQUIRE_PTR(o, "o", esz);
+  if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
+  kda::DecodeArgs a{stt->S, stt->ring, q, k, v, g, beta, conv_w, o,
+                    d->batch, d->heads, d->d_k, d->d_v, flags, gate, norm_w, eps};
+  hipError_t e = kda::launch_decode(a, d->io, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return KDA_OK;
+}
 
 }  // namespace
 
@@ -235,19 +263,47 @@ kda_status kda_decode_step(kda_state* stt, const void* q, const void* k, const v
   if (!stt) return fail(KDA_ERR_INVALID, "state is NULL");
   kda_status st = check_flags(flags, kStepFlags);
   if (st != KDA_OK) return st;
-  const kda_dims* d = &stt->dims;
-  const size_t esz = io_size(d->io);
-  KDA_REQUIRE_PTR(q, "q", esz);
-  KDA_REQUIRE_PTR(k, "k", esz);
-  KDA_REQUIRE_PTR(v, "v", esz);
-  KDA_REQUIRE_PTR(g, "g", 4);
-  KDA_REQUIRE_PTR(beta, "beta", 4);
-  KDA_REQUIRE_PTR(o, "o", esz);
-  if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
-  kda::DecodeArgs a{stt->S, stt->ring, q, k, v, g, beta, conv_w, o,
-                    d->batch, d->heads, d->d_k, d->d_v, flags};
-  hipError_t e = kda::launch_decode(a, d->io, stream);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return decode_common(stt, q, k, v, g, beta, conv_w, nullptr, nullptr, 0.0f, o, flags,
+                       stream);
+}
+
+kda_status kda_decode_step_gated(kda_state* stt, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* conv_w,
+                                 const void* gate, const float* norm_w, float eps, void* o,
+                                 uint32_t flags, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!stt) return fail(KDA_ERR_INVALID, "state is NULL");
+  kda_status st = check_flags(flags, kStepFlags);
+  if (st != KDA_OK) return st;
+  if ((st = check_eps(eps)) != KDA_OK) return st;
+  KDA_REQUIRE_PTR(gate, "gate", io_size(stt->dims.io));
+  KDA_REQUIRE_PTR(norm_w, "norm_w", 4);
+  return decode_common(stt, q, k, v, g, beta, conv_w, gate, norm_w, eps, o, flags, stream);
+}
+
+kda_status kda_gated_rmsnorm(const kda_dims* dims, int32_t T, const void* x, const void* gate,
+                             const float* norm_w, float eps, void* out, hipStream_t stream) {
+  g_err[0] = 0;
+  kda_status st = check_dims(dims);
+  if (st != KDA_OK) return st;
+  if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);
+  if ((st = check_eps(eps)) != KDA_OK) return st;
+  if (T == 0) return KDA_OK;
+  KDA_REQUIRE_PTR(x, "x", 16);
+  KDA_REQUIRE_PTR(gate, "gate", 16);
+  KDA_REQUIRE_PTR(norm_w, "norm_w", 16);
+  KDA_REQUIRE_PTR(out, "out", 16);
+  const long rows = (long)dims->batch * T * dims->heads;
+  const size_t bytes = (size_t)rows * dims->d_v * io_size(dims->io);
+  const uintptr_t xo = reinterpret_cast<uintptr_t>(x), oo = reinterpret_cast<uintptr_t>(out),
+                  go = reinterpret_cast<uintptr_t>(gate);
+  if (oo != xo && oo < xo + bytes && xo < oo + bytes)
+    return fail(KDA_ERR_INVALID, "out overlaps x without being x");
+  if (oo < go + bytes && go < oo + bytes)
+    return fail(KDA_ERR_INVALID, "out overlaps gate");
+  hipError_t e = kda::launch_gated_rmsnorm(x, gate, norm_w, eps, out, rows, dims->d_v, dims->io,
+                                           stream);
+  if (e != hipSuccess) return hip_fail(e, "gated rmsnorm launch");
   return KDA_OK;
 }
 

@@ -65,8 +65,16 @@ struct DecodeArgs {
   void* o;               // [B][H][dv]
   int B, H, dk, dv;
   uint32_t flags;
+  // output gate fused into the readout (NULL gate: plain readout)
+  const void* gate;      // [B][H][dv] io dtype, gate pre-activations
+  const float* norm_w;   // [dv]
+  float norm_eps;
 };
 hipError_t launch_decode(const DecodeArgs& a, kda_dtype io, hipStream_t stream);
+
+// Gated RMSNorm of rows of dv values: y = x / sqrt(mean x^2 + eps) * w * sigmoid(z).
+hipError_t launch_gated_rmsnorm(const void* x, const void* z, const float* w, float eps,
+                                void* y, long rows, int dv, kda_dtype io, hipStream_t stream);
 
 struct PrologueArgs {
   const void* q;  // [B][T][H][dk]

@@ -25,8 +25,9 @@ namespace {
 
 // NTH: stream S with non-temporal loads and stores (it is read once and
 // written once per step; keeping it out of the caches leaves them to the
-// small per-token inputs).
-template <int DK, int DV, int NT, typename IO, bool NTH>
+// small per-token inputs). GATE: o receives the gated RMSNorm of the readout,
+// o = r / sqrt(mean r^2 + eps) * w * sigmoid(z) over the head's dv values.
+template <int DK, int DV, int NT, typename IO, bool NTH, bool GATE>
 __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
   constexpr int LPR = DV / 4;         // lanes per state row
   constexpr int RPP = NT / LPR;       // state rows per load pass
@@ -40,6 +41,8 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
   __shared__ float sq[DK], sk[DK], sv[DV], sdec[DK], sdel[DV];
   __shared__ float sred[NW][LPR][8];
   __shared__ float snorm[3];
+  constexpr int NWD = (DV + kWave - 1) / kWave;  // waves that hold readout values
+  __shared__ float sgate[NWD];
 
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int H = a.H;
@@ -95,6 +98,13 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
     }
   }
   const float betav = a.beta[bh];
+  float zg = 0.f, wg = 0.f;  // gate pre-activation and norm weight of column tid
+  if constexpr (GATE) {
+    if (tid < DV) {
+      zg = to_f32(static_cast<const IO*>(a.gate)[bh * DV + tid]);
+      wg = a.norm_w[tid];
+    }
+  }
 
   // ---- 2. the state: J float4 per thread, rows rg + RPP*jj ---------------
   float* Sbh = a.S + bh * DK * DV + 4 * c4;
@@ -182,6 +192,7 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
   __syncthreads();
 
   // ---- 6. per column: delta and the readout -----------------------------
+  float ov = 0.f;
   if (tid < DV) {
     const int cc = tid / 4, e = tid % 4;
     float rk = 0.f, rq = 0.f;
@@ -192,9 +203,26 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
     }
     const float del = betav * (sv[tid] - rk);
     sdel[tid] = del;
-    static_cast<IO*>(a.o)[bh * DV + tid] = from_f32<IO>(rq + qk * del);
+    ov = rq + qk * del;
+    if constexpr (!GATE) static_cast<IO*>(a.o)[bh * DV + tid] = from_f32<IO>(ov);
+  }
+  if constexpr (GATE) {
+    if (wv < NWD) {  // wave-uniform: every lane of these waves takes part
+      const float ss = wave_sum(tid < DV ? ov * ov : 0.f);
+      if (lane == 0) sgate[wv] = ss;
+    }
   }
   __syncthreads();
+  if constexpr (GATE) {
+    if (tid < DV) {
+      float ss = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWD; ++w) ss += sgate[w];
+      const float inv = 1.0f / sqrtf(ss * (1.0f / DV) + a.norm_eps);
+      const float sig = 1.0f / (1.0f + __expf(-zg));
+      static_cast<IO*>(a.o)[bh * DV + tid] = from_f32<IO>(ov * inv * wg * sig);
+    }
+  }
 
   // ---- 7. rank-1 write and store -----------------------------------------
   const f32x4 dl = *reinterpret_cast<const f32x4*>(&sdel[4 * c4]);
@@ -222,7 +250,12 @@ template <int DK, int DV, typename IO>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NT = decode_threads<DK, DV>();
   dim3 grid(a.H, a.B);
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, NT, IO, true>), grid, dim3(NT), 0, stream, a);
+  if (a.gate)
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, NT, IO, true, true>), grid, dim3(NT), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, NT, IO, true, false>), grid, dim3(NT), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,127 @@
+// Output gate after the readout: a gated RMSNorm of every (token, head) row
+// of dv readout values,
+//   y = x / sqrt(mean x^2 + eps) * w * sigmoid(z),
+// with z the gate pre-activations and w a weight vector of length dv shared by
+// the heads. The WARP engine lists a gated RMSNorm beside its KDA decode step
+// ("KV缓存从11.25GB缩到0.21GB：WARP中Kimi Delta Attention线性注意力原理剖析",
+// section "相关源码与文档导航") and "为什么 Kimi K3 敢把 KV Cache 扔掉？…" section 6
+// gates the output for feature scaling; neither prints the formula, and this
+// is the plain reading of the two.
+//
+// HBM-bound streaming: per row x and z are read once and y is written once
+// (3 * dv * sizeof(io) bytes). A row is covered by LPR = dv / VEC lanes, each
+// holding VEC = 16 / sizeof(io) consecutive values (one 16-byte load of x, one
+// of z, one 16-byte store of y); the row's sum of squares is reduced over its
+// LPR lanes with xor shuffles. Each thread takes UR rows, spaced by the rows
+// of one block pass, and issues all their loads before any arithmetic.
+#include "kda_common.h"
+
+namespace kda {
+namespace {
+
+template <typename IO> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  using T = f32x4;
+};
+template <> struct Vec16<bf16> {
+  static constexpr int N = 8;
+  using T = bf16x8;
+};
+
+constexpr int kGateNT = 256;
+constexpr int kGateUR = 4;
+
+// x and y may be the same buffer (in place): every element is read and then
+// written by the same thread.
+template <int DV, typename IO>
+__global__ __launch_bounds__(kGateNT) void gated_rmsnorm_kernel(const IO* x, const IO* z,
+                                                               const float* __restrict__ w,
+                                                               float eps, IO* y, long rows) {
+  using V = typename Vec16<IO>::T;
+  constexpr int VEC = Vec16<IO>::N;
+  constexpr int LPR = DV / VEC;            // lanes per row
+  constexpr int RPP = kGateNT / LPR;       // rows per block pass
+  static_assert(DV % VEC == 0 && LPR >= 1 && LPR <= kWave, "unsupported dv");
+  const int tid = threadIdx.x, c = tid % LPR;
+  const long row0 = (long)blockIdx.x * RPP * kGateUR + tid / LPR;
+
+  V xv[kGateUR], zv[kGateUR];
+#pragma unroll
+  for (int u = 0; u < kGateUR; ++u) {
+    const long row = row0 + (long)u * RPP;
+    if (row < rows) {
+      xv[u] = *reinterpret_cast<const V*>(x + row * DV + c * VEC);
+      zv[u] = *reinterpret_cast<const V*>(z + row * DV + c * VEC);
+    } else {
+      xv[u] = V{};
+      zv[u] = V{};
+    }
+  }
+  float wr[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; e += 4) {
+    const f32x4 w4 = *reinterpret_cast<const f32x4*>(w + c * VEC + e);
+    wr[e] = w4.x;
+    wr[e + 1] = w4.y;
+    wr[e + 2] = w4.z;
+    wr[e + 3] = w4.w;
+  }
+
+#pragma unroll
+  for (int u = 0; u < kGateUR; ++u) {
+    float xf[VEC];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      xf[e] = to_f32(xv[u][e]);
+      ss += xf[e] * xf[e];
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
+    V out;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float sig = 1.0f / (1.0f + __expf(-to_f32(zv[u][e])));
+      out[e] = from_f32<IO>(xf[e] * inv * wr[e] * sig);
+    }
+    const long row = row0 + (long)u * RPP;
+    if (row < rows) *reinterpret_cast<V*>(y + row * DV + c * VEC) = out;
+  }
+}
+
+template <int DV, typename IO>
+hipError_t launch_t(const void* x, const void* z, const float* w, float eps, void* y, long rows,
+                    hipStream_t stream) {
+  constexpr int rows_per_block = kGateNT / (DV / Vec16<IO>::N) * kGateUR;
+  const long blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gated_rmsnorm_kernel<DV, IO>), dim3((unsigned)blocks), dim3(kGateNT), 0,
+                     stream, static_cast<const IO*>(x), static_cast<const IO*>(z), w, eps,
+                     static_cast<IO*>(y), rows);
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_io(const void* x, const void* z, const float* w, float eps, void* y, long rows,
+                     int dv, hipStream_t stream) {
+  switch (dv) {
+    case 16: return launch_t<16, IO>(x, z, w, eps, y, rows, stream);
+    case 32: return launch_t<32, IO>(x, z, w, eps, y, rows, stream);
+    case 64: return launch_t<64, IO>(x, z, w, eps, y, rows, stream);
+    case 128: return launch_t<128, IO>(x, z, w, eps, y, rows, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gated_rmsnorm(const void* x, const void* z, const float* w, float eps,
+                                void* y, long rows, int dv, kda_dtype io, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  return io == KDA_BF16 ? launch_io<bf16>(x, z, w, eps, y, rows, dv, stream)
+                        : launch_io<float>(x, z, w, eps, y, rows, dv, stream);
+}
+
+}  // namespace kda

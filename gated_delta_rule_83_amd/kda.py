@@ -23,7 +23,7 @@ EXPORTED = [
     "kda_state_bytes", "kda_state_alloc", "kda_state_reset", "kda_state_free",
     "kda_state_S", "kda_state_ring", "kda_state_get_dims", "kda_conv_prologue",
     "kda_decode_step", "kda_prefill_workspace_bytes", "kda_chunk_prefill",
-    "kda_last_error", "kda_version",
+    "kda_gated_rmsnorm", "kda_decode_step_gated", "kda_last_error", "kda_version",
 ]
 
 
@@ -52,6 +52,7 @@ def lib():
                           "`python -c 'import __graft_entry__ as g; g.build()'`")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    f32 = ctypes.c_float
     dp = ctypes.POINTER(kda_dims)
     sig = {
         "kda_state_bytes": (sz, [dp, ctypes.POINTER(sz)]),
@@ -66,6 +67,9 @@ def lib():
         "kda_prefill_workspace_bytes": (sz, [dp, i32, i32]),
         "kda_chunk_prefill": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz,
                                              u32, vp]),
+        "kda_gated_rmsnorm": (ctypes.c_int, [dp, i32, vp, vp, vp, f32, vp, vp]),
+        "kda_decode_step_gated": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
+                                                 u32, vp]),
         "kda_last_error": (ctypes.c_char_p, []),
         "kda_version": (ctypes.c_char_p, []),
     }
@@ -181,6 +185,25 @@ def kda_decode_step(handle, q, k, v, g, beta, conv_w, o, flags=0, stream=None, i
         _ptr(conv_w, "conv_w", torch.float32), _ptr(o, "o", io), int(flags), _stream(stream)))
 
 
+def kda_decode_step_gated(handle, q, k, v, g, beta, conv_w, gate, norm_w, eps, o, flags=0,
+                          stream=None, io=None):
+    io = io or io_dtype(kda_state_get_dims(handle))
+    _check(lib().kda_decode_step_gated(
+        handle, _ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io),
+        _ptr(g, "g", torch.float32), _ptr(beta, "beta", torch.float32),
+        _ptr(conv_w, "conv_w", torch.float32), _ptr(gate, "gate", io),
+        _ptr(norm_w, "norm_w", torch.float32), ctypes.c_float(eps), _ptr(o, "o", io),
+        int(flags), _stream(stream)))
+
+
+def kda_gated_rmsnorm(dims, T, x, gate, norm_w, eps, out, stream=None):
+    io = io_dtype(dims)
+    _check(lib().kda_gated_rmsnorm(
+        ctypes.byref(dims), int(T), _ptr(x, "x", io), _ptr(gate, "gate", io),
+        _ptr(norm_w, "norm_w", torch.float32), ctypes.c_float(eps), _ptr(out, "out", io),
+        _stream(stream)))
+
+
 def kda_prefill_workspace_bytes(dims, T, chunk=64) -> int:
     return int(lib().kda_prefill_workspace_bytes(ctypes.byref(dims), int(T), int(chunk)))
 
@@ -222,6 +245,15 @@ class KDAState:
 
     def decode_step(self, q, k, v, g, beta, conv_w, o, flags=0, stream=None):
         kda_decode_step(self.handle, q, k, v, g, beta, conv_w, o, flags, stream, io=self.io)
+
+    def decode_step_gated(self, q, k, v, g, beta, conv_w, gate, norm_w, eps, o, flags=0,
+                          stream=None):
+        kda_decode_step_gated(self.handle, q, k, v, g, beta, conv_w, gate, norm_w, eps, o,
+                              flags, stream, io=self.io)
+
+    def gated_rmsnorm(self, T, x, gate, norm_w, eps, out, stream=None):
+        """The output gate on T tokens of this state's dims ([B,T,H,dv] tensors)."""
+        kda_gated_rmsnorm(self.dims, T, x, gate, norm_w, eps, out, stream)
 
     def prefill(self, T, q, k, v, g, beta, conv_w, o, chunk=64, workspace=None, flags=0,
                 stream=None):

@@ -187,6 +187,37 @@ kda_status kda_chunk_prefill(kda_state* st, int32_t T, const void* q,
                              int32_t chunk, void* workspace, size_t workspace_bytes,
                              uint32_t flags, hipStream_t stream);
 
+/* Output gate after the readout: a gated RMSNorm of each (sequence, token,
+ * head) row of d_v readout values,
+ *   out = x / sqrt(mean over d_v of x^2 + eps) * norm_w * sigmoid(gate).
+ *  x:      [B][T][H][d_v] io dtype (e.g. the o of kda_chunk_prefill).
+ *  gate:   [B][T][H][d_v] io dtype, the gate pre-activations.
+ *  norm_w: [d_v] fp32, one weight vector shared by all heads.
+ *  eps:    finite and > 0.
+ *  out:    [B][T][H][d_v] io dtype; may be x itself (in place), must not
+ *          otherwise overlap x or gate.
+ * x, gate, out and norm_w must be 16-byte aligned. T = 0 is a no-op. Only the
+ * dims' batch, heads, d_v and io are used.
+ * Source: the WARP engine lists a gated RMSNorm beside its KDA decode step
+ * ("KV缓存从11.25GB缩到0.21GB：…", section "相关源码与文档导航"), and "为什么 Kimi
+ * K3 敢把 KV Cache 扔掉？…" section 6 gates the output for feature scaling;
+ * neither prints the formula: this is the plain reading of the two (per-head
+ * RMSNorm over d_v, sigmoid gate).
+ * Errors: KDA_ERR_INVALID (NULL or misaligned pointer, T < 0, eps),
+ * KDA_ERR_UNSUPPORTED (dims). */
+kda_status kda_gated_rmsnorm(const kda_dims* dims, int32_t T, const void* x, const void* gate,
+                             const float* norm_w, float eps, void* out, hipStream_t stream);
+
+/* kda_decode_step with the output gate of kda_gated_rmsnorm fused into the
+ * readout: o receives the gated RMSNorm of S^T q^ (computed from the fp32
+ * readout, before any rounding to the io dtype).
+ *  gate:   [B][H][d_v] io dtype; norm_w: [d_v] fp32; eps finite and > 0.
+ * Everything else as kda_decode_step. */
+kda_status kda_decode_step_gated(kda_state* st, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta,
+                                 const float* conv_w, const void* gate, const float* norm_w,
+                                 float eps, void* o, uint32_t flags, hipStream_t stream);
+
 /* Description of the last error on the calling thread ("" if none). */
 const char* kda_last_error(void);
 

@@ -135,6 +135,46 @@ def test_scalar_decay_flag_validation(fake_state):
     assert "0x4" in kda.last_error()
 
 
+def test_output_gate_validation(fake_state):
+    """Argument checks of the output gate entry points (every case fails before
+    anything is enqueued)."""
+    L = kda.lib()
+    d = kda.make_dims(1, 2, 16, 16, kda.KDA_F32)
+    f = ctypes.c_float
+
+    def gate(T=4, x=FAKE, z=2 * FAKE, w=3 * FAKE, eps=1e-5, out=FAKE):
+        return L.kda_gated_rmsnorm(ctypes.byref(d), T, _vp(x), _vp(z), _vp(w), f(eps), _vp(out),
+                                   None)
+
+    assert gate(T=0) == K.KDA_OK
+    assert gate(T=-1) == K.KDA_ERR_INVALID
+    for bad in (0.0, -1e-5, float("inf"), float("nan")):
+        assert gate(eps=bad) == K.KDA_ERR_INVALID
+        assert "eps" in kda.last_error()
+    assert gate(x=None) == K.KDA_ERR_INVALID
+    assert gate(w=3 * FAKE + 4) == K.KDA_ERR_INVALID
+    assert "norm_w is not 16-byte aligned" in kda.last_error()
+    assert gate(out=FAKE + 64) == K.KDA_ERR_INVALID          # partly overlaps x
+    assert "overlaps x" in kda.last_error()
+    assert gate(out=2 * FAKE) == K.KDA_ERR_INVALID           # is the gate
+    assert "overlaps gate" in kda.last_error()
+
+    def dec(gate_p=4 * FAKE, w=3 * FAKE, eps=1e-5, q=FAKE, flags=0):
+        return L.kda_decode_step_gated(fake_state, _vp(q), _vp(FAKE), _vp(FAKE), _vp(FAKE),
+                                       _vp(FAKE), _vp(FAKE), _vp(gate_p), _vp(w), f(eps),
+                                       _vp(FAKE), flags, None)
+
+    assert dec(gate_p=None) == K.KDA_ERR_INVALID
+    assert "gate is NULL" in kda.last_error()
+    assert dec(w=None) == K.KDA_ERR_INVALID
+    assert dec(eps=0.0) == K.KDA_ERR_INVALID
+    assert dec(q=None) == K.KDA_ERR_INVALID
+    assert "q is NULL" in kda.last_error()
+    assert dec(flags=8) == K.KDA_ERR_INVALID
+    assert L.kda_decode_step_gated(None, *([_vp(FAKE)] * 8), f(1e-5), _vp(FAKE), 0,
+                                   None) == K.KDA_ERR_INVALID
+
+
 def test_reset_validation(fake_state):
     arr = (ctypes.c_int32 * 2)(0, 5)
     assert kda.lib().kda_state_reset(fake_state, arr, 2, None) == K.KDA_ERR_INVALID

@@ -98,6 +98,20 @@ def draw(B, T, H, dk, dv, io="f32", seed=0, s0_random=False, ring_random=False,
     return Inputs(q, k, v, g, beta, conv_w, S0, ring0, info)
 
 
+def draw_output_gate(B, T, H, dv, io="f32", seed=0):
+    """Inputs of the output gate that follows the readout, from a generator of
+    their own (seed + 500,000, so the recurrence's draws are unchanged): gate
+    pre-activations z ~ N(0, 1) [B, T, H, dv] (rounded to bf16 for bf16
+    workloads) and a norm weight w = 1 + 0.1 * N(0, 1) [dv] (fp32), with
+    eps = 1e-5. Returns (z, w, eps)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed) + 500_000)
+    z = torch.randn(B, T, H, dv, generator=gen, dtype=torch.float32)
+    w = 1.0 + 0.1 * torch.randn(dv, generator=gen, dtype=torch.float32)
+    if io == "bf16":
+        z = z.to(torch.bfloat16)
+    return z, w, 1e-5
+
+
 def make(name: str, **overrides) -> Inputs:
     """Draw the named workload; keyword overrides replace its parameters
     (e.g. a smaller T for a quick check)."""
