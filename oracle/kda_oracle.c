@@ -283,3 +283,21 @@ int kdao_gated_rmsnorm(long rows, int n, const double *x, const double *z,
   }
   return 0;
 }
+
+/* Gates from raw projections (a separate step before the recurrence): the
+ * Alpha/Beta projection of "为什么 Kimi K3 敢把 KV Cache 扔掉？…" section 6 sets
+ * the forgetting strength alpha in [0, 1] and the update strength beta; the
+ * squashing into (0, 1) by a logistic sigmoid is a reading (no formula is
+ * printed). With alpha = sigmoid(a) the log-space decay the recurrence takes
+ * is g = log(sigmoid(a)) = -log(1 + exp(-a)), and beta = sigmoid(b).
+ * a, g: n_g values; b, beta: n_b values. */
+int kdao_gates_from_raw(long n_g, const double *a, double *g, long n_b, const double *b,
+                        double *beta) {
+  if (n_g < 0 || n_b < 0 || (n_g && (!a || !g)) || (n_b && (!b || !beta))) return -1;
+  for (long i = 0; i < n_g; ++i) {
+    /* -log(1 + e^{-a}) written so that neither branch overflows */
+    g[i] = a[i] >= 0.0 ? -log1p(exp(-a[i])) : a[i] - log1p(exp(a[i]));
+  }
+  for (long i = 0; i < n_b; ++i) beta[i] = 1.0 / (1.0 + exp(-b[i]));
+  return 0;
+}

@@ -20,9 +20,11 @@ Two independent formulations live here:
   (the cumulative in-chunk decay). It exists so that the chunked and
   sequential forms can be checked against each other.
 
-A third function, :meth:`Oracle.gated_rmsnorm`, is the output gate that
-follows the readout (a gated RMSNorm per token and head; its formula is a
-reading, stated in ``kda_oracle.c``).
+Two more steps around the recurrence, each a reading stated in
+``kda_oracle.c``: :meth:`Oracle.gated_rmsnorm`, the output gate that follows
+the readout (a gated RMSNorm per token and head), and
+:meth:`Oracle.gates_from_raw`, the decay and beta formed from raw projections
+(log-sigmoid and sigmoid).
 
 The decay g is per key channel. The scalar-alpha Gated DeltaNet form (one
 decay per token and head, same page, sections 6 and 7) is the case of g equal
@@ -83,6 +85,8 @@ class Oracle:
         lib.kdao_gated_rmsnorm.argtypes = [ctypes.c_long, ctypes.c_int, dp, dp, dp,
                                            ctypes.c_double, dp]
         lib.kdao_gated_rmsnorm.restype = ctypes.c_int
+        lib.kdao_gates_from_raw.argtypes = [ctypes.c_long, dp, dp, ctypes.c_long, dp, dp]
+        lib.kdao_gates_from_raw.restype = ctypes.c_int
         lib.kdao_max_threads.argtypes = []
         lib.kdao_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -162,6 +166,16 @@ class Oracle:
             raise RuntimeError("kdao_gated_rmsnorm failed")
         return y
 
+    def gates_from_raw(self, a, b):
+        """Gates from raw projections: g = log(sigmoid(a)) (any shape) and
+        beta = sigmoid(b). Returns (g, beta) in float64."""
+        a, b = _f64(a), _f64(b)
+        g, beta = np.empty_like(a), np.empty_like(b)
+        rc = self.lib.kdao_gates_from_raw(a.size, _ptr(a), _ptr(g), b.size, _ptr(b), _ptr(beta))
+        if rc != 0:
+            raise RuntimeError("kdao_gates_from_raw failed")
+        return g, beta
+
     def chunked_core(self, *args, **kwargs):
         return chunked_core(*args, **kwargs)
 
@@ -194,6 +208,10 @@ def prologue(*args, **kwargs):
 
 def gated_rmsnorm(*args, **kwargs):
     return default().gated_rmsnorm(*args, **kwargs)
+
+
+def gates_from_raw(*args, **kwargs):
+    return default().gates_from_raw(*args, **kwargs)
 
 
 def chunked_core(qh, kh, vh, g, beta, S0, chunk):

@@ -368,6 +368,32 @@ def pin_gated_rmsnorm_closed_forms(orc):
     np.testing.assert_array_equal(np.delete(y, 2, 0), np.delete(y1, 2, 0))
 
 
+# --------------------------------------------------------------------------
+# Gates from raw projections ([K3] section 6: the Alpha/Beta projection sets
+# the forgetting and update strengths; the sigmoid squashing is a reading):
+# g = log(sigmoid(a)), beta = sigmoid(b).
+def pin_gates_from_raw(orc):
+    rng = np.random.default_rng(81)
+    a = np.concatenate([4.0 * rng.standard_normal(200), [0.0, -700.0, 700.0, -40.0, 40.0]])
+    b = 3.0 * rng.standard_normal(50)
+    g, beta = orc.gates_from_raw(a, b)
+    # torch's own log-sigmoid and sigmoid in float64
+    at, bt = torch.from_numpy(a), torch.from_numpy(b)
+    np.testing.assert_allclose(g, torch.nn.functional.logsigmoid(at).numpy(), rtol=1e-14,
+                               atol=1e-300)
+    np.testing.assert_allclose(beta, torch.sigmoid(bt).numpy(), rtol=1e-14)
+    # closed forms: alpha = e^g = sigmoid(a) in (0, 1], g(0) = -ln 2, and
+    # log sigmoid(a) - log sigmoid(-a) = a; sigmoid(b) + sigmoid(-b) = 1
+    assert np.all(g <= 0.0)
+    np.testing.assert_allclose(np.exp(g[:200]), 1.0 / (1.0 + np.exp(-a[:200])), rtol=1e-14)
+    assert g[200] == -np.log(2.0)
+    assert g[201] == -700.0                                   # a -> -inf: g ~ a
+    np.testing.assert_allclose(g[202], -np.exp(-700.0), rtol=1e-14)  # a -> inf: g ~ -e^-a
+    g_neg, beta_neg = orc.gates_from_raw(-a[:200], -b)
+    np.testing.assert_allclose(g[:200] - g_neg, a[:200], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(beta + beta_neg, 1.0, rtol=1e-15)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_zero_decay_is_delta_rule,
@@ -383,4 +409,5 @@ ALL_PINS = [
     pin_transition_product,
     pin_gated_rmsnorm_library,
     pin_gated_rmsnorm_closed_forms,
+    pin_gates_from_raw,
 ]

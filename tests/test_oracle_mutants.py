@@ -53,6 +53,13 @@ MUTANTS = {
     "gate_missing": [("yr[j] = xr[j] / rms * w[j] * gate;", "yr[j] = xr[j] / rms * w[j];")],
     "gate_sign": [("1.0 / (1.0 + exp(-zr[j]))", "1.0 / (1.0 + exp(zr[j]))")],
     "norm_weight_missing": [("yr[j] = xr[j] / rms * w[j] * gate;", "yr[j] = xr[j] / rms * gate;")],
+    # gates from raw projections
+    "decay_is_sigmoid": [("-log1p(exp(-a[i])) : a[i] - log1p(exp(a[i]))",
+                          "1.0 / (1.0 + exp(-a[i])) : 1.0 / (1.0 + exp(-a[i]))")],
+    "decay_branch_swapped": [("a[i] >= 0.0 ? -log1p", "a[i] < 0.0 ? -log1p")],
+    "decay_sign_of_a": [("-log1p(exp(-a[i])) : a[i] - log1p(exp(a[i]))",
+                         "-log1p(exp(a[i])) : -a[i] - log1p(exp(-a[i]))")],
+    "beta_not_squashed": [("beta[i] = 1.0 / (1.0 + exp(-b[i]));", "beta[i] = b[i];")],
 }
 
 
