@@ -15,6 +15,8 @@ decode token through all 69 layers as one captured HIP graph over 6.5 GiB of
 state; one layer's 32768-token prefill of the 16 sequences) under "stack", and
 the same decode and prefill workloads with one decay per token and head
 (KDA_F_SCALAR_G, the scalar-alpha Gated DeltaNet form) under "scalar_decay",
+the same with the gates formed in the kernels from raw projections
+(KDA_F_RAW_GATES) under "raw_gates",
 and the output gate (gated RMSNorm of the readout: fused into the decode step,
 and as its own kernel on the prefill output) under "output_gate".
 Beside them: the latency of one K3-shape decode step (batch 1, fp32, warm and
@@ -250,18 +252,18 @@ def parse():
                    help="skip the 69-layer stack measurements")
     p.add_argument("--stack-reps", type=int, default=20)
     p.add_argument("--no-gdn", action="store_true",
-                   help="skip the scalar-decay (KDA_F_SCALAR_G) measurements")
+                   help="skip the flag variants (KDA_F_SCALAR_G, KDA_F_RAW_GATES)")
     return p.parse_args()
 
 
-def gdn_bench(kda, workloads, torch, dev, args):
-    """The scalar-decay variant (KDA_F_SCALAR_G: one decay per token and head,
-    the scalar-alpha Gated DeltaNet form) on the same two workloads: 64
-    sequences x 96 heads x 128x128 bf16 decode (same step count and warm-up as
-    the headline) and the 4096-token chunk-64 prefill (median of event-
-    bracketed calls after 10 warm-up calls)."""
-    sg = kda.KDA_F_SCALAR_G
-    inp = workloads.make("batched_decode_gdn")
+def variant_bench(kda, workloads, torch, dev, args, decode_name, prefill_name, flags, what,
+                  **overrides):
+    """A flag variant on the two workloads of the headline: 64 sequences x 96
+    heads x 128x128 bf16 decode (same step count and warm-up as the headline)
+    and the 4096-token chunk-64 prefill (median of event-bracketed calls after
+    10 warm-up calls)."""
+    scalar_g = bool(flags & kda.KDA_F_SCALAR_G)
+    inp = workloads.make(decode_name, **overrides)
     B, T, H, dk, dv = inp.dims
     stg = {name: getattr(inp, name).transpose(0, 1).contiguous().to(dev)
            for name in ("q", "k", "v", "g", "beta")}
@@ -274,7 +276,7 @@ def gdn_bench(kda, workloads, torch, dev, args):
     def step(i):
         j = i % T
         st.decode_step(stg["q"][j], stg["k"][j], stg["v"][j], stg["g"][j], stg["beta"][j],
-                       conv_w, o, flags=sg)
+                       conv_w, o, flags=flags)
 
     for i in range(args.warmup):
         step(i)
@@ -287,11 +289,11 @@ def gdn_bench(kda, workloads, torch, dev, args):
     torch.cuda.synchronize()
     per_launch = ev0.elapsed_time(ev1) / 1e3 / args.steps
     assert torch.isfinite(st.S).all().item() and torch.isfinite(o.float()).all().item()
-    dbytes = decode_bytes(B, H, dk, dv, scalar_g=True)
+    dbytes = decode_bytes(B, H, dk, dv, scalar_g=scalar_g)
     st.close()
     del stg, st
 
-    pin = workloads.make("prefill_4k_gdn")
+    pin = workloads.make(prefill_name, **overrides)
     pB, pT, pH, pdk, pdv = pin.dims
     pd = {name: getattr(pin, name).contiguous().to(dev) for name in ("q", "k", "v", "g", "beta")}
     pw = pin.conv_w.to(dev)
@@ -301,7 +303,7 @@ def gdn_bench(kda, workloads, torch, dev, args):
 
     def prefill():
         pst.prefill(pT, pd["q"], pd["k"], pd["v"], pd["g"], pd["beta"], pw, po, chunk=64,
-                    flags=sg)
+                    flags=flags)
 
     for _ in range(10):
         prefill()
@@ -316,11 +318,10 @@ def gdn_bench(kda, workloads, torch, dev, args):
     calls_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     pre_ms = calls_ms[len(calls_ms) // 2]
     assert torch.isfinite(pst.S).all().item()
-    pbytes = prefill_bytes(pB, pT, pH, pdk, pdv, scalar_g=True)
+    pbytes = prefill_bytes(pB, pT, pH, pdk, pdv, scalar_g=scalar_g)
     pst.close()
     return {
-        "workload": "KDA_F_SCALAR_G (one decay per token and head): the decode and prefill "
-                    "workloads above with g [B,T,H]",
+        "workload": what,
         "decode": {"tokens_per_s": B / per_launch, "avg_launch_us": per_launch * 1e6,
                    "bytes_per_launch": dbytes, "hbm_GBps": dbytes / per_launch / 1e9,
                    "hbm_frac": dbytes / per_launch / 1e9 / HBM_PEAK_GBPS},
@@ -460,7 +461,14 @@ def main():
     del pz, py
 
     stack = None if args.no_stack else stack_bench(kda, workloads, torch, dev, args)
-    gdn = None if args.no_gdn else gdn_bench(kda, workloads, torch, dev, args)
+    gdn = None if args.no_gdn else variant_bench(
+        kda, workloads, torch, dev, args, "batched_decode_gdn", "prefill_4k_gdn",
+        kda.KDA_F_SCALAR_G, "KDA_F_SCALAR_G (one decay per token and head): the decode and "
+        "prefill workloads above with g [B,T,H]")
+    raw = None if args.no_gdn else variant_bench(
+        kda, workloads, torch, dev, args, "batched_decode", "prefill_4k", kda.KDA_F_RAW_GATES,
+        "KDA_F_RAW_GATES (the decay and beta formed in the kernels from raw projections): the "
+        "decode and prefill workloads above drawn as pre-activations", raw_gates=True)
 
     # ---------------- one K3-shape decode step: latency, warm and flushed ---
     single = single_step_latency(kda, workloads, torch, dev)
@@ -550,6 +558,7 @@ def main():
                     "compulsory_bytes": pbytes, "flops": pflops},
         "stack": stack,
         "scalar_decay": gdn,
+        "raw_gates": raw,
         "output_gate": {
             "workload": "gated RMSNorm of each head's readout (sigmoid gate, shared weight, "
                         "eps 1e-5): fused into the decode step (64 sequences, same steps), "

@@ -80,7 +80,8 @@ kda_status check_flags(uint32_t flags, uint32_t allowed) {
 }
 
 constexpr uint32_t kPrologueFlags = KDA_F_SKIP_CONV | KDA_F_SKIP_L2;
-constexpr uint32_t kStepFlags = KDA_F_SKIP_CONV | KDA_F_SKIP_L2 | KDA_F_SCALAR_G;
+constexpr uint32_t kStepFlags =
+    KDA_F_SKIP_CONV | KDA_F_SKIP_L2 | KDA_F_SCALAR_G | KDA_F_RAW_GATES;
 
 // Token tensors, g, beta and o are accessed per element (natural alignment);
 // conv weights, S, the ring and the workspace are accessed 16 bytes at a time.

@@ -44,6 +44,15 @@ __device__ __forceinline__ float silu(float y) {
   return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
 }
 
+// The gates formed from raw projections (KDA_F_RAW_GATES): the log-decay
+// log(sigmoid(x)) = min(x, 0) - log(1 + e^{-|x|}), which does not overflow,
+// with the hardware exp2/log2 (the log's argument lies in (1, 2], so the
+// result is within about 1e-7 absolute), and the update strength sigmoid(x).
+__device__ __forceinline__ float log_sigmoid(float x) {
+  return fminf(x, 0.0f) - __logf(1.0f + __expf(-fabsf(x)));
+}
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
 // Sum over the 64 lanes of a wave; every lane receives the total.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

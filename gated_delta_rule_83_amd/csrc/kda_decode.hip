@@ -97,7 +97,12 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
       gval[u] = i < DK ? a.g[bh * DK + i] : 0.0f;
     }
   }
-  const float betav = a.beta[bh];
+  float betav = a.beta[bh];
+  if (a.flags & KDA_F_RAW_GATES) {  // raw projections: form the gates here
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) gval[u] = log_sigmoid(gval[u]);
+    betav = sigmoid(betav);
+  }
   float zg = 0.f, wg = 0.f;  // gate pre-activation and norm weight of column tid
   if constexpr (GATE) {
     if (tid < DV) {

@@ -269,6 +269,10 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
 #pragma unroll
         for (int r = 0; r < QS; ++r)
           bv[r] = a.beta[((long)b * T + min(tstart + qr0 + r, T - 1)) * H + h];
+        if (a.flags & KDA_F_RAW_GATES) {  // raw projection: beta formed here
+#pragma unroll
+          for (int r = 0; r < QS; ++r) bv[r] = sigmoid(bv[r]);
+        }
       }
 #pragma unroll
       for (int r = 0; r < QS; ++r) {
@@ -309,6 +313,12 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
     } else if (role == 3) {
       // strip-local inclusive prefix sums of g, parked in the R region
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (a.flags & KDA_F_RAW_GATES) {  // raw projections: the log-decay formed here
+#pragma unroll
+        for (int r = 0; r < GS; ++r)
+          buf[r] = f32x4{log_sigmoid(buf[r].x), log_sigmoid(buf[r].y), log_sigmoid(buf[r].z),
+                         log_sigmoid(buf[r].w)};
+      }
 #pragma unroll
       for (int r = 0; r < GS; ++r) {
         const bool valid = GS * gs + r < n;

@@ -89,7 +89,8 @@ struct RowsSmem {
 // (launch bounds: C/16 waves, at least three waves per SIMD, i.e. three
 // items per CU). CONV: the inputs are raw projections (conv + SiLU here);
 // SG: g holds one decay per (token, head), shared by all key channels.
-template <int C, int DK, int DV, bool CONV, bool SG>
+// RAW: g and beta are raw projections; the gates are formed on load.
+template <int C, int DK, int DV, bool CONV, bool SG, bool RAW>
 __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs a, int t0, int ncs,
                                                                   uint8_t* ws) {
   using M = MmaBf16;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
       }
     }
   }
-  const float betav = valid ? a.beta[row] : 0.f;
+  float betav = valid ? a.beta[row] : 0.f;
   const bf16* qsrc = static_cast<const bf16*>(a.q) + row * DK + 8 * gq;
   const bf16* ksrc = static_cast<const bf16*>(a.k) + row * DK + 8 * gq;
   const bf16* vsrc = static_cast<const bf16*>(a.v) + row * DV + 8 * gq;
@@ -233,17 +234,31 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   // ---- 1a. g: in-block prefix sums (row scan) and R = e^{Gam_r - Gam_m},
   //          m = the block's first token; block first values and sums of
   //          the rest to LDS ------------------------------------------------
+  if constexpr (RAW) betav = sigmoid(betav);  // raw projection: beta formed here
   float R[NKS][8];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
     float p[8];
+    if constexpr (RAW) {  // raw projections: the log-decay formed here
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float gv = valid ? gl[s][e / 4][e % 4] : 0.f;
-      p[e] = i == 0 ? 0.f : gv;
-      if (e % 4 == 3 && i == 0)
-        *reinterpret_cast<f32x4*>(&sFirst[rb][32 * s + 8 * gq + e - 3]) =
-            valid ? gl[s][e / 4] : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 8; ++e) {
+        const float gv = valid ? log_sigmoid(gl[s][e / 4][e % 4]) : 0.f;
+        gl[s][e / 4][e % 4] = gv;
+        p[e] = i == 0 ? 0.f : gv;
+      }
+      if (i == 0) {
+        *reinterpret_cast<f32x4*>(&sFirst[rb][32 * s + 8 * gq]) = gl[s][0];
+        *reinterpret_cast<f32x4*>(&sFirst[rb][32 * s + 8 * gq + 4]) = gl[s][1];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gv = valid ? gl[s][e / 4][e % 4] : 0.f;
+        p[e] = i == 0 ? 0.f : gv;
+        if (e % 4 == 3 && i == 0)
+          *reinterpret_cast<f32x4*>(&sFirst[rb][32 * s + 8 * gq + e - 3]) =
+              valid ? gl[s][e / 4] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -532,15 +547,23 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   }
 }
 
+template <int C, int DK, int DV, bool CONV, bool SG>
+void launch_sg(const PrefillArgs& a, int t0, int ncs, uint8_t* ws, hipStream_t st) {
+  const dim3 grid((unsigned)((long)ncs * a.H * a.B)), block(C * 4);
+  if (a.flags & KDA_F_RAW_GATES)
+    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, CONV, SG, true>), grid, block, 0,
+                       st, a, t0, ncs, ws);
+  else
+    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, CONV, SG, false>), grid, block, 0,
+                       st, a, t0, ncs, ws);
+}
+
 template <int C, int DK, int DV, bool CONV>
 void launch_conv(const PrefillArgs& a, int t0, int ncs, uint8_t* ws, hipStream_t st) {
-  const dim3 grid((unsigned)((long)ncs * a.H * a.B)), block(C * 4);
   if (a.flags & KDA_F_SCALAR_G)
-    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, CONV, true>), grid, block, 0, st,
-                       a, t0, ncs, ws);
+    launch_sg<C, DK, DV, CONV, true>(a, t0, ncs, ws, st);
   else
-    hipLaunchKernelGGL((prefill_prep_rows_kernel<C, DK, DV, CONV, false>), grid, block, 0, st,
-                       a, t0, ncs, ws);
+    launch_sg<C, DK, DV, CONV, false>(a, t0, ncs, ws, st);
 }
 
 template <int C, int DK, int DV>

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_OOM = 0, -1, -2, -3, -4
 KDA_F32, KDA_BF16 = 0, 1
-KDA_F_SKIP_CONV, KDA_F_SKIP_L2, KDA_F_SCALAR_G = 1, 2, 4
+KDA_F_SKIP_CONV, KDA_F_SKIP_L2, KDA_F_SCALAR_G, KDA_F_RAW_GATES = 1, 2, 4, 8
 
 EXPORTED = [
     "kda_state_bytes", "kda_state_alloc", "kda_state_reset", "kda_state_free",

@@ -83,6 +83,15 @@ typedef struct {
                               token or head) and section 7 (KDA refines it to one
                               per channel). The result equals the per-channel call
                               with g repeated over d_k. */
+#define KDA_F_RAW_GATES 8u /* kda_decode_step / kda_chunk_prefill only: g and beta hold
+                              the raw gate projections a and b (any real values) and
+                              the kernels form the decay g = log(sigmoid(a)) (alpha =
+                              sigmoid(a) in (0, 1)) and beta = sigmoid(b) themselves.
+                              Combines with KDA_F_SCALAR_G (then a is [B][T][H]).
+                              Source: "为什么 Kimi K3 敢把 KV Cache 扔掉？…", section 6:
+                              the Alpha/Beta projection sets the forgetting and update
+                              strengths, alpha in [0, 1]; the squashing by a sigmoid
+                              is a reading (no formula is printed). */
 
 /* Opaque per-layer session state: S and the conv ring for B sequences. */
 typedef struct kda_state kda_state;

@@ -105,7 +105,7 @@ def test_decode_validation(fake_state):
     assert "4-byte aligned" in kda.last_error()
     assert call_decode(fake_state, w=FAKE + 4) == K.KDA_ERR_INVALID
     assert "conv_w is not 16-byte aligned" in kda.last_error()
-    assert call_decode(fake_state, flags=8) == K.KDA_ERR_INVALID
+    assert call_decode(fake_state, flags=16) == K.KDA_ERR_INVALID
     assert call_decode(fake_state, w=None) == K.KDA_ERR_INVALID
     assert "conv_w" in kda.last_error()
 
@@ -120,12 +120,13 @@ def test_prefill_validation(fake_state):
 
 
 def test_scalar_decay_flag_validation(fake_state):
-    """KDA_F_SCALAR_G is a flag of the decode step and the prefill only: there
-    validation goes on past it (to the NULL q here); the prologue rejects it."""
+    """KDA_F_SCALAR_G and KDA_F_RAW_GATES are flags of the decode step and the
+    prefill only: there validation goes on past them (to the NULL q here); the
+    prologue rejects them."""
     sg = kda.KDA_F_SCALAR_G
     assert call_decode(fake_state, q=None, flags=sg) == K.KDA_ERR_INVALID
     assert "q is NULL" in kda.last_error()
-    assert call_decode(fake_state, flags=sg | 8) == K.KDA_ERR_INVALID
+    assert call_decode(fake_state, flags=sg | 16) == K.KDA_ERR_INVALID
     assert call_prefill(fake_state, q=None, flags=sg | kda.KDA_F_SKIP_CONV) == K.KDA_ERR_INVALID
     assert "q is NULL" in kda.last_error()
     assert call_prefill(fake_state, T=0, flags=sg) == K.KDA_OK
@@ -133,6 +134,14 @@ def test_scalar_decay_flag_validation(fake_state):
     assert kda.lib().kda_conv_prologue(ctypes.byref(d), 4, *([_vp(FAKE)] * 8), sg,
                                        None) == K.KDA_ERR_INVALID
     assert "0x4" in kda.last_error()
+    raw = kda.KDA_F_RAW_GATES
+    assert call_decode(fake_state, q=None, flags=raw | sg) == K.KDA_ERR_INVALID
+    assert "q is NULL" in kda.last_error()
+    assert call_prefill(fake_state, q=None, flags=raw) == K.KDA_ERR_INVALID
+    assert "q is NULL" in kda.last_error()
+    assert kda.lib().kda_conv_prologue(ctypes.byref(d), 4, *([_vp(FAKE)] * 8), raw,
+                                       None) == K.KDA_ERR_INVALID
+    assert "0x8" in kda.last_error()
 
 
 def test_output_gate_validation(fake_state):
@@ -170,7 +179,7 @@ def test_output_gate_validation(fake_state):
     assert dec(eps=0.0) == K.KDA_ERR_INVALID
     assert dec(q=None) == K.KDA_ERR_INVALID
     assert "q is NULL" in kda.last_error()
-    assert dec(flags=8) == K.KDA_ERR_INVALID
+    assert dec(flags=16) == K.KDA_ERR_INVALID
     assert L.kda_decode_step_gated(None, *([_vp(FAKE)] * 8), f(1e-5), _vp(FAKE), 0,
                                    None) == K.KDA_ERR_INVALID
 

@@ -11,7 +11,9 @@ workload, in a fixed order:
 
 with q, k, v ~ N(0, 1) of shape [B, T, H, d]; g = logsigmoid(g_mu + N(0, 1))
 per key channel [B, T, H, dk] (with scalar_g, one per token and head:
-[B, T, H], the scalar-alpha Gated DeltaNet form); beta = sigmoid(N(0, 1)) [B, T, H]; conv
+[B, T, H], the scalar-alpha Gated DeltaNet form); beta = sigmoid(N(0, 1)) [B, T, H]
+(with raw_gates, g and beta hold the pre-activations g_mu + N(0, 1) and
+N(0, 1) themselves, drawn from the same stream); conv
 weights ~ 0.5 * N(0, 1) of shape [H*(2dk+dv), 4]; S0 ~ 0.02 * N(0, 1) of
 shape [B, H, dk, dv]; ring ~ N(0, 1) of shape [B, 3, H*(2dk+dv)]. For
 bf16 workloads q, k, v and the ring are rounded to bf16 (round to nearest
@@ -73,7 +75,7 @@ class Inputs:
 
 
 def draw(B, T, H, dk, dv, io="f32", seed=0, s0_random=False, ring_random=False,
-         g_mu=0.0, scalar_g=False, **meta) -> Inputs:
+         g_mu=0.0, scalar_g=False, raw_gates=False, **meta) -> Inputs:
     gen = torch.Generator(device="cpu").manual_seed(int(seed))
     ctot = H * (2 * dk + dv)
 
@@ -84,8 +86,11 @@ def draw(B, T, H, dk, dv, io="f32", seed=0, s0_random=False, ring_random=False,
     k = randn(B, T, H, dk)
     v = randn(B, T, H, dv)
     g_shape = (B, T, H) if scalar_g else (B, T, H, dk)
-    g = torch.nn.functional.logsigmoid(randn(*g_shape) + float(g_mu))
-    beta = torch.sigmoid(randn(B, T, H))
+    g = randn(*g_shape) + float(g_mu)
+    beta = randn(B, T, H)
+    if not raw_gates:  # with raw_gates g and beta stay the pre-activations
+        g = torch.nn.functional.logsigmoid(g)
+        beta = torch.sigmoid(beta)
     conv_w = 0.5 * randn(ctot, 4)
     S0 = 0.02 * randn(B, H, dk, dv) if s0_random else torch.zeros(B, H, dk, dv)
     ring0 = randn(B, 3, ctot) if ring_random else torch.zeros(B, 3, ctot)
@@ -94,7 +99,7 @@ def draw(B, T, H, dk, dv, io="f32", seed=0, s0_random=False, ring_random=False,
     elif io != "f32":
         raise ValueError(f"io must be 'f32' or 'bf16', not {io!r}")
     info = dict(B=B, T=T, H=H, dk=dk, dv=dv, io=io, seed=seed, g_mu=g_mu, scalar_g=scalar_g,
-                **meta)
+                raw_gates=raw_gates, **meta)
     return Inputs(q, k, v, g, beta, conv_w, S0, ring0, info)
 
 
