@@ -13,7 +13,10 @@
 // holding VEC = 16 / sizeof(io) consecutive values (one 16-byte load of x, one
 // of z, one 16-byte store of y); the row's sum of squares is reduced over its
 // LPR lanes with xor shuffles. Each thread takes UR rows, spaced by the rows
-// of one block pass, and issues all their loads before any arithmetic.
+// of one block pass, and issues all their loads before any arithmetic. x, z
+// and y are streamed with non-temporal loads and stores (each byte is touched
+// once; measured on MI355X over 393,216 rows of 128 bf16: 50 us against 59 us
+// with ordinary ones).
 #include "kda_common.h"
 
 namespace kda {
@@ -51,8 +54,8 @@ __global__ __launch_bounds__(kGateNT) void gated_rmsnorm_kernel(const IO* x, con
   for (int u = 0; u < kGateUR; ++u) {
     const long row = row0 + (long)u * RPP;
     if (row < rows) {
-      xv[u] = *reinterpret_cast<const V*>(x + row * DV + c * VEC);
-      zv[u] = *reinterpret_cast<const V*>(z + row * DV + c * VEC);
+      xv[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(x + row * DV + c * VEC));
+      zv[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(z + row * DV + c * VEC));
     } else {
       xv[u] = V{};
       zv[u] = V{};
@@ -87,7 +90,8 @@ __global__ __launch_bounds__(kGateNT) void gated_rmsnorm_kernel(const IO* x, con
       out[e] = from_f32<IO>(xf[e] * inv * wr[e] * sig);
     }
     const long row = row0 + (long)u * RPP;
-    if (row < rows) *reinterpret_cast<V*>(y + row * DV + c * VEC) = out;
+    if (row < rows)
+      __builtin_nontemporal_store(out, reinterpret_cast<V*>(y + row * DV + c * VEC));
   }
 }
 

@@ -11,8 +11,7 @@ import torch
 import gated_delta_rule_83_amd as kda
 import workloads
 from oracle import kda_oracle
-from tests.gpu_util import (abs_err, device, f64, load_state, rel_err, run_decode, subset,
-                            to_dev)
+from tests.gpu_util import abs_err, device, f64, load_state, rel_err, subset, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -146,3 +145,48 @@ def test_prefill_4k_then_gate_in_place():
     ref_y = kda_oracle.gated_rmsnorm(ref_o, z[:, :, heads], w, eps)
     ey = _check(f64(o[:, :, heads]), ref_y, "bf16")
     print(f"prefill_4k + gate: rel err {ey:.2e}")
+
+
+def test_gated_paths_in_captured_graph_match_eager():
+    """Gated decode steps from raw gate projections, then the standalone gate
+    kernel on their outputs, captured in one HIP graph: every replay (with
+    eager work and synchronizations between replays) equals the same launches
+    issued eagerly, bit for bit."""
+    dev = device()
+    inp = workloads.make("tiny", T=3, B=2, H=4, dk=64, dv=128, io="bf16", s0_random=True,
+                         ring_random=True, raw_gates=True, seed=960)
+    B, T, H, dk, dv = inp.dims
+    z, w, eps = workloads.draw_output_gate(B, T, H, dv, "bf16", seed=960)
+    d = to_dev(inp, dev, step_major=True)
+    zd, wd = z.transpose(0, 1).contiguous().to(dev), w.to(dev)
+    eager = kda.KDAState(B, H, dk, dv, io=torch.bfloat16, device=dev)
+    cap = kda.KDAState(B, H, dk, dv, io=torch.bfloat16, device=dev)
+    for st in (eager, cap):
+        load_state(st, inp)
+    oe = torch.empty(T, B, H, dv, dtype=torch.bfloat16, device=dev)
+    oc, ye, yc = torch.empty_like(oe), torch.empty_like(oe), torch.empty_like(oe)
+    raw = kda.KDA_F_RAW_GATES
+
+    def run(st, o, y):
+        for t in range(T):
+            st.decode_step_gated(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t],
+                                 d["conv_w"], zd[t], wd, eps, o[t], flags=raw)
+        # the plain gate kernel over all T steps' outputs ([T*B] rows of H heads)
+        kda.kda_gated_rmsnorm(kda.make_dims(T * B, H, dk, dv), 1, o, zd, wd, eps, y)
+
+    run(cap, oc, yc)
+    torch.cuda.synchronize()
+    load_state(cap, inp)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(cap, oc, yc)
+    load_state(cap, inp)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        run(eager, oe, ye)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oc, oe) and torch.equal(yc, ye), f"replay {rep}: outputs differ"
+        assert torch.equal(cap.S, eager.S) and torch.equal(cap.ring, eager.ring), \
+            f"replay {rep}: state differs"
