@@ -256,6 +256,19 @@ def parse():
     return p.parse_args()
 
 
+def back_to_back_ms(torch, call, n):
+    """Average duration of n calls issued back to back between one pair of
+    events (steady-state throughput: no event between the calls)."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def variant_bench(kda, workloads, torch, dev, args, decode_name, prefill_name, flags, what,
                   **overrides):
     """A flag variant on the two workloads of the headline: 64 sequences x 96
@@ -317,6 +330,7 @@ def variant_bench(kda, workloads, torch, dev, args, decode_name, prefill_name, f
     torch.cuda.synchronize()
     calls_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     pre_ms = calls_ms[len(calls_ms) // 2]
+    b2b_ms = back_to_back_ms(torch, prefill, args.prefill_reps)
     assert torch.isfinite(pst.S).all().item()
     pbytes = prefill_bytes(pB, pT, pH, pdk, pdv, scalar_g=scalar_g)
     pst.close()
@@ -327,6 +341,8 @@ def variant_bench(kda, workloads, torch, dev, args, decode_name, prefill_name, f
                    "hbm_frac": dbytes / per_launch / 1e9 / HBM_PEAK_GBPS},
         "prefill": {"tokens_per_s": pT * pB / (pre_ms / 1e3), "ms": pre_ms,
                     "ms_min": calls_ms[0], "ms_max": calls_ms[-1], "calls": len(calls_ms),
+                    "ms_back_to_back": b2b_ms,
+                    "tokens_per_s_back_to_back": pT * pB / (b2b_ms / 1e3),
                     "compulsory_bytes": pbytes,
                     "hbm_GBps": pbytes / (pre_ms / 1e3) / 1e9,
                     "hbm_frac": pbytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBPS},
@@ -436,6 +452,7 @@ def main():
     torch.cuda.synchronize()
     calls_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     pre_ms = calls_ms[len(calls_ms) // 2]
+    b2b_ms = back_to_back_ms(torch, prefill, args.prefill_reps)
     pbytes = prefill_bytes(pB, pT, pH, pdk, pdv)
     pflops = prefill_flops(pB, pT, pH, pdk, pdv, 64)
     assert torch.isfinite(pst.S).all().item()
@@ -551,6 +568,8 @@ def main():
         "prefill": {"workload": "chunked prefill T=4096, batch 1, 96 heads, chunk 64, bf16",
                     "tokens_per_s": pT * pB / (pre_ms / 1e3), "ms": pre_ms,
                     "ms_min": calls_ms[0], "ms_max": calls_ms[-1], "calls": len(calls_ms),
+                    "ms_back_to_back": b2b_ms,
+                    "tokens_per_s_back_to_back": pT * pB / (b2b_ms / 1e3),
                     "hbm_GBps": pbytes / (pre_ms / 1e3) / 1e9,
                     "hbm_frac": pbytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
                     "tflops": pflops / (pre_ms / 1e3) / 1e12,
