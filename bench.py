@@ -354,7 +354,7 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KDA state of every (sequence, head) is "
               "independent, so more GPUs would each run this same kernel on their own "
-              "share; multi-GPU runs are not part of this build.", file=sys.stderr)
+              "share; this benchmark runs on one GPU only.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
