@@ -135,10 +135,16 @@ def single_step_latency(kda, workloads, torch, dev, reps=20):
     warm = sorted(once(False) for _ in range(reps))[reps // 2]
     cold = sorted(once(True) for _ in range(reps))[reps // 2]
     del flush
+    # consecutive steps issued back to back (one token after another of the
+    # same sequence, no event between them)
+    n = 200
+    b2b = back_to_back_ms(
+        torch, lambda: st.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], w, o), n) * 1e3
     return {"workload": "one decode step, batch 1, 96 heads of 128x128 fp32 state (6 MiB), "
                         "fp32 q/k/v/o; median of single launches",
             "latency_us_warm": warm, "latency_us_flushed": cold,
-            "tokens_per_s_warm": 1e6 / warm, "tokens_per_s_flushed": 1e6 / cold}
+            "tokens_per_s_warm": 1e6 / warm, "tokens_per_s_flushed": 1e6 / cold,
+            "us_per_step_back_to_back": b2b}
 
 
 def stack_bench(kda, workloads, torch, dev, args):

@@ -88,6 +88,9 @@ typedef struct {
                               the kernels form the decay g = log(sigmoid(a)) (alpha =
                               sigmoid(a) in (0, 1)) and beta = sigmoid(b) themselves.
                               Combines with KDA_F_SCALAR_G (then a is [B][T][H]).
+                              For kda_chunk_prefill the decay so formed must meet
+                              that call's precondition on g (a of -5 or more per
+                              token always does).
                               Source: "为什么 Kimi K3 敢把 KV Cache 扔掉？…", section 6:
                               the Alpha/Beta projection sets the forgetting and update
                               strengths, alpha in [0, 1]; the squashing by a sigmoid
