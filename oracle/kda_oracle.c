@@ -301,3 +301,107 @@ int kdao_gates_from_raw(long n_g, const double *a, double *g, long n_b, const do
   for (long i = 0; i < n_b; ++i) beta[i] = 1.0 / (1.0 + exp(-b[i]));
   return 0;
 }
+
+/* Gradient of the recurrence (steps 3-6) for training: given the activations
+ * q^, k^, v^ [B][T][H][d], g [B][T][H][dk], beta [B][T][H], the entering state
+ * S0 [B][H][dk][dv] and the gradients dO [B][T][H][dv] of the readouts and
+ * dST [B][H][dk][dv] of the final state, returns dq, dk [B][T][H][dk], dv
+ * [B][T][H][dv], dg [B][T][H][dk], dbeta [B][T][H] and dS0 [B][H][dk][dv].
+ *
+ * Written from the update of section "KDA 递推公式先衰减再差分" by reverse-mode
+ * differentiation, token by token from the last one. With S' = Diag(e^g) S_{t-1},
+ * r = S'^T k, delta = beta (v - r), S_t = S' + k delta^T, o_t = S_t^T q and
+ * G = dL/dS_t (the readouts of tokens t and later, and dST):
+ *   G       += q do^T                  (o_t = S_t^T q)
+ *   dq       = S_t do
+ *   ddelta   = G^T k,  dk += G delta    (S_t = S' + k delta^T)
+ *   dv       = beta ddelta,  dbeta = ddelta . (v - r),  dr = -beta ddelta
+ *   dS'      = G + k dr^T,  dk += S' dr (r = S'^T k)
+ *   dg[i]    = sum_j dS'[i][j] S'[i][j]
+ *   G        = Diag(e^g) dS'           (dL/dS_{t-1})
+ * and dS0 is the last G. The states S_t are kept from a forward pass, so this
+ * is for small inputs only. Returns 0, or -1 on bad arguments. */
+int kdao_core_backward(int B, int T, int H, int dk, int dv,
+                       const double *q, const double *k, const double *v,
+                       const double *g, const double *beta, const double *S0,
+                       const double *dO, const double *dST,
+                       double *dq, double *dk_out, double *dv_out, double *dg,
+                       double *dbeta, double *dS0) {
+  if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  const long BH = (long)B * H, SS = (long)dk * dv;
+  double *states = malloc(sizeof(double) * SS * (T + 1));
+  double *G = malloc(sizeof(double) * SS);
+  double *Sp = malloc(sizeof(double) * SS);
+  double *r = malloc(sizeof(double) * dv);
+  double *del = malloc(sizeof(double) * dv);
+  double *dd = malloc(sizeof(double) * dv);
+  int bad = !states || !G || !Sp || !r || !del || !dd;
+  for (long bh = 0; bh < BH && !bad; ++bh) {
+    const int b = (int)(bh / H), h = (int)(bh % H);
+#define TOK(t) (((long)b * T + (t)) * H + h)
+    /* forward, keeping S_0 .. S_T */
+    memcpy(states, S0 + bh * SS, sizeof(double) * SS);
+    for (int t = 0; t < T; ++t) {
+      const double *kt = k + TOK(t) * dk, *vt = v + TOK(t) * dv, *gt = g + TOK(t) * dk;
+      const double bt = beta[TOK(t)];
+      double *Sn = states + (long)(t + 1) * SS;
+      const double *Sc = states + (long)t * SS;
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) Sn[(long)i * dv + j] = exp(gt[i]) * Sc[(long)i * dv + j];
+      for (int j = 0; j < dv; ++j) {
+        r[j] = 0.0;
+        for (int i = 0; i < dk; ++i) r[j] += Sn[(long)i * dv + j] * kt[i];
+      }
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) Sn[(long)i * dv + j] += bt * kt[i] * (vt[j] - r[j]);
+    }
+    /* backward */
+    memcpy(G, dST + bh * SS, sizeof(double) * SS);
+    for (int t = T - 1; t >= 0; --t) {
+      const double *qt = q + TOK(t) * dk, *kt = k + TOK(t) * dk, *vt = v + TOK(t) * dv;
+      const double *gt = g + TOK(t) * dk, *dot = dO + TOK(t) * dv;
+      const double bt = beta[TOK(t)];
+      const double *Sprev = states + (long)t * SS, *St = states + (long)(t + 1) * SS;
+      double *dqt = dq + TOK(t) * dk, *dkt = dk_out + TOK(t) * dk, *dvt = dv_out + TOK(t) * dv;
+      double *dgt = dg + TOK(t) * dk;
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) {
+          G[(long)i * dv + j] += qt[i] * dot[j];
+          Sp[(long)i * dv + j] = exp(gt[i]) * Sprev[(long)i * dv + j];
+        }
+      for (int j = 0; j < dv; ++j) {
+        r[j] = 0.0;
+        dd[j] = 0.0;
+        for (int i = 0; i < dk; ++i) {
+          r[j] += Sp[(long)i * dv + j] * kt[i];
+          dd[j] += G[(long)i * dv + j] * kt[i];
+        }
+        del[j] = bt * (vt[j] - r[j]);
+      }
+      double db = 0.0;
+      for (int j = 0; j < dv; ++j) {
+        dvt[j] = bt * dd[j];
+        db += dd[j] * (vt[j] - r[j]);
+      }
+      dbeta[TOK(t)] = db;
+      for (int i = 0; i < dk; ++i) {
+        double aq = 0.0, ak = 0.0, ag = 0.0;
+        for (int j = 0; j < dv; ++j) {
+          const double drj = -bt * dd[j];
+          aq += St[(long)i * dv + j] * dot[j];
+          ak += G[(long)i * dv + j] * del[j] + Sp[(long)i * dv + j] * drj;
+          const double dsp = G[(long)i * dv + j] + kt[i] * drj;
+          ag += dsp * Sp[(long)i * dv + j];
+          G[(long)i * dv + j] = exp(gt[i]) * dsp;
+        }
+        dqt[i] = aq;
+        dkt[i] = ak;
+        dgt[i] = ag;
+      }
+    }
+    memcpy(dS0 + bh * SS, G, sizeof(double) * SS);
+#undef TOK
+  }
+  free(states); free(G); free(Sp); free(r); free(del); free(dd);
+  return bad ? -1 : 0;
+}

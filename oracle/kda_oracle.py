@@ -24,7 +24,8 @@ Two more steps around the recurrence, each a reading stated in
 ``kda_oracle.c``: :meth:`Oracle.gated_rmsnorm`, the output gate that follows
 the readout (a gated RMSNorm per token and head), and
 :meth:`Oracle.gates_from_raw`, the decay and beta formed from raw projections
-(log-sigmoid and sigmoid).
+(log-sigmoid and sigmoid). :meth:`Oracle.core_backward` is the gradient of
+the recurrence for training, by reverse-mode differentiation token by token.
 
 The decay g is per key channel. The scalar-alpha Gated DeltaNet form (one
 decay per token and head, same page, sections 6 and 7) is the case of g equal
@@ -87,6 +88,8 @@ class Oracle:
         lib.kdao_gated_rmsnorm.restype = ctypes.c_int
         lib.kdao_gates_from_raw.argtypes = [ctypes.c_long, dp, dp, ctypes.c_long, dp, dp]
         lib.kdao_gates_from_raw.restype = ctypes.c_int
+        lib.kdao_core_backward.argtypes = [ctypes.c_int] * 5 + [dp] * 14
+        lib.kdao_core_backward.restype = ctypes.c_int
         lib.kdao_max_threads.argtypes = []
         lib.kdao_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -175,6 +178,25 @@ class Oracle:
         if rc != 0:
             raise RuntimeError("kdao_gates_from_raw failed")
         return g, beta
+
+    def core_backward(self, qh, kh, vh, g, beta, S0, dO, dST):
+        """Gradient of the recurrence (decay, delta read, rank-1 write,
+        readout) for the linear functional sum(dO * o) + sum(dST * S_T):
+        returns dq, dk, dv, dg, dbeta, dS0 (float64, shapes of the inputs).
+        Keeps every state of a forward pass: small inputs only."""
+        qh, kh, vh, g, beta, S0, dO, dST = map(_f64, (qh, kh, vh, g, beta, S0, dO, dST))
+        B, T, H, dk = qh.shape
+        dv = vh.shape[-1]
+        assert kh.shape == qh.shape and g.shape == qh.shape and beta.shape == (B, T, H)
+        assert vh.shape == dO.shape == (B, T, H, dv) and S0.shape == dST.shape == (B, H, dk, dv)
+        out = [np.zeros_like(qh), np.zeros_like(kh), np.zeros_like(vh), np.zeros_like(g),
+               np.zeros_like(beta), np.zeros_like(S0)]
+        rc = self.lib.kdao_core_backward(B, T, H, dk, dv, _ptr(qh), _ptr(kh), _ptr(vh), _ptr(g),
+                                         _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dST),
+                                         *[_ptr(x) for x in out])
+        if rc != 0:
+            raise RuntimeError("kdao_core_backward failed")
+        return tuple(out)
 
     def chunked_core(self, *args, **kwargs):
         return chunked_core(*args, **kwargs)

@@ -394,6 +394,38 @@ def pin_gates_from_raw(orc):
     np.testing.assert_allclose(beta + beta_neg, 1.0, rtol=1e-15)
 
 
+# --------------------------------------------------------------------------
+# Gradient of the recurrence (for training): the hand-derived reverse pass
+# against central finite differences of the forward oracle itself, for every
+# element of every input, on a linear functional of o and the final state.
+def pin_core_backward_finite_differences(orc):
+    q, k, v, g, beta, w, S0, ring = _rand_case(91, T=6, dk=3, dv=4)
+    rng = np.random.default_rng(92)
+    dO = rng.standard_normal(v.shape)
+    dST = rng.standard_normal(S0.shape)
+    args = dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0)
+
+    def loss(a):
+        o, S = orc.core(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"])
+        return float((o * dO).sum() + (S * dST).sum())
+
+    grads = orc.core_backward(q, k, v, g, beta, S0, dO, dST)
+    h = 1e-6
+    for name, grad in zip(("q", "k", "v", "g", "beta", "S0"), grads):
+        x = args[name]
+        assert grad.shape == x.shape
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            saved = x[idx]
+            x[idx] = saved + h
+            lp = loss(args)
+            x[idx] = saved - h
+            lm = loss(args)
+            x[idx] = saved
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg=f"d{name}")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_zero_decay_is_delta_rule,
@@ -410,4 +442,5 @@ ALL_PINS = [
     pin_gated_rmsnorm_library,
     pin_gated_rmsnorm_closed_forms,
     pin_gates_from_raw,
+    pin_core_backward_finite_differences,
 ]

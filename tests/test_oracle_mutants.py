@@ -60,6 +60,15 @@ MUTANTS = {
     "decay_sign_of_a": [("-log1p(exp(-a[i])) : a[i] - log1p(exp(a[i]))",
                          "-log1p(exp(a[i])) : -a[i] - log1p(exp(-a[i]))")],
     "beta_not_squashed": [("beta[i] = 1.0 / (1.0 + exp(-b[i]));", "beta[i] = b[i];")],
+    # the gradient of the recurrence
+    "bwd_no_decay_carry": [("G[(long)i * dv + j] = exp(gt[i]) * dsp;", "G[(long)i * dv + j] = dsp;")],
+    "bwd_dk_misses_read": [("ak += G[(long)i * dv + j] * del[j] + Sp[(long)i * dv + j] * drj;",
+                            "ak += G[(long)i * dv + j] * del[j];")],
+    "bwd_dq_from_old_state": [("aq += St[(long)i * dv + j] * dot[j];",
+                               "aq += Sp[(long)i * dv + j] * dot[j];")],
+    "bwd_dbeta_without_read": [("db += dd[j] * (vt[j] - r[j]);", "db += dd[j] * vt[j];")],
+    "bwd_readout_added_late": [("          G[(long)i * dv + j] += qt[i] * dot[j];\n", ""),
+                               ("        dgt[i] = ag;\n", "        dgt[i] = ag;\n        (void)qt;\n")],
 }
 
 
