@@ -5,8 +5,8 @@
 // the heads. The WARP engine lists a gated RMSNorm beside its KDA decode step
 // ("KV缓存从11.25GB缩到0.21GB：WARP中Kimi Delta Attention线性注意力原理剖析",
 // section "相关源码与文档导航") and "为什么 Kimi K3 敢把 KV Cache 扔掉？…" section 6
-// gates the output for feature scaling; neither prints the formula, and this
-// is the plain reading of the two.
+// puts a gate on the output that rescales features; neither prints the
+// formula, and this is the plain reading of the two.
 //
 // HBM-bound streaming: per row x and z are read once and y is written once
 // (3 * dv * sizeof(io) bytes). A row is covered by LPR = dv / VEC lanes, each

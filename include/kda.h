@@ -212,9 +212,9 @@ kda_status kda_chunk_prefill(kda_state* st, int32_t T, const void* q,
  * dims' batch, heads, d_v and io are used.
  * Source: the WARP engine lists a gated RMSNorm beside its KDA decode step
  * ("KV缓存从11.25GB缩到0.21GB：…", section "相关源码与文档导航"), and "为什么 Kimi
- * K3 敢把 KV Cache 扔掉？…" section 6 gates the output for feature scaling;
- * neither prints the formula: this is the plain reading of the two (per-head
- * RMSNorm over d_v, sigmoid gate).
+ * K3 敢把 KV Cache 扔掉？…" section 6 puts a gate on the output that rescales
+ * features; neither prints the formula: this is the plain reading of the two
+ * (per-head RMSNorm over d_v, sigmoid gate).
  * Errors: KDA_ERR_INVALID (NULL or misaligned pointer, T < 0, eps),
  * KDA_ERR_UNSUPPORTED (dims). */
 kda_status kda_gated_rmsnorm(const kda_dims* dims, int32_t T, const void* x, const void* gate,

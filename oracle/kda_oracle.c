@@ -259,8 +259,8 @@ int kdao_prologue(int B, int T, int H, int dk, int dv,
  * a gated RMSNorm of each head's readout vector. The C engine of "KV缓存从
  * 11.25GB缩到0.21GB：WARP中Kimi Delta Attention线性注意力原理剖析" lists a gated
  * RMSNorm beside the KDA decode step (section "相关源码与文档导航"), and "为什么
- * Kimi K3 敢把 KV Cache 扔掉？…" section 6 adds a gate on the output for feature
- * scaling; neither prints the formula. The reading taken here: per row (one
+ * Kimi K3 敢把 KV Cache 扔掉？…" section 6 puts a gate on the output that
+ * rescales features; neither prints the formula. The reading taken here: per row (one
  * token of one head) of n values x with gate pre-activations z,
  *
  *   y[j] = x[j] / sqrt(mean_j x[j]^2 + eps) * w[j] * sigmoid(z[j]),
