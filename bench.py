@@ -249,6 +249,8 @@ def parse():
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--prefill-reps", type=int, default=20)
+    p.add_argument("--prefill-warmup", type=int, default=100,
+                   help="untimed prefill calls before the timed ones")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -280,7 +282,7 @@ def variant_bench(kda, workloads, torch, dev, args, decode_name, prefill_name, f
     """A flag variant on the two workloads of the headline: 64 sequences x 96
     heads x 128x128 bf16 decode (same step count and warm-up as the headline)
     and the 4096-token chunk-64 prefill (median of event-bracketed calls after
-    10 warm-up calls)."""
+    the warm-up calls)."""
     scalar_g = bool(flags & kda.KDA_F_SCALAR_G)
     inp = workloads.make(decode_name, **overrides)
     B, T, H, dk, dv = inp.dims
@@ -324,7 +326,7 @@ def variant_bench(kda, workloads, torch, dev, args, decode_name, prefill_name, f
         pst.prefill(pT, pd["q"], pd["k"], pd["v"], pd["g"], pd["beta"], pw, po, chunk=64,
                     flags=flags)
 
-    for _ in range(10):
+    for _ in range(args.prefill_warmup):
         prefill()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -443,10 +445,12 @@ def main():
     def prefill():
         pst.prefill(pT, pd["q"], pd["k"], pd["v"], pd["g"], pd["beta"], pw, po, chunk=64)
 
-    # warm-up calls, then calls bracketed one by one by events on the launch
-    # stream (back to back, no host synchronization between them); the
-    # median call is reported
-    for _ in range(10):
+    # warm-up calls (the prefill kernels take 60-80 calls, about 25 ms of
+    # sustained load, to settle: the first calls run up to 25 % longer), then
+    # calls bracketed one by one by events on the launch stream (back to
+    # back, no host synchronization between them); the median call is
+    # reported
+    for _ in range(args.prefill_warmup):
         prefill()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
