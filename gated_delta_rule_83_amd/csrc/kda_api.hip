@@ -375,4 +375,57 @@ kda_status kda_chunk_prefill(kda_state* stt, int32_t T, const void* q, const voi
   return KDA_OK;
 }
 
+size_t kda_backward_workspace_bytes(const kda_dims* d, int32_t T, int32_t chunk) {
+  if (check_dims(d) != KDA_OK || T < 0 || (chunk != 16 && chunk != 32 && chunk != 64)) return 0;
+  return kda::backward_ws_bytes(d->batch, T, d->heads, d->d_k, d->d_v, chunk);
+}
+
+kda_status kda_chunk_backward(const kda_dims* d, int32_t T, const void* q, const void* k,
+                              const void* v, const float* g, const float* beta, const float* S0,
+                              const void* dO, const float* dST, void* dq, void* dk, void* dv,
+                              float* dg, float* dbeta, float* dS0, int32_t chunk,
+                              void* workspace, size_t workspace_bytes, uint32_t flags,
+                              hipStream_t stream) {
+  g_err[0] = 0;
+  kda_status st = check_dims(d);
+  if (st != KDA_OK) return st;
+  if (flags != 0) return fail(KDA_ERR_INVALID, "kda_chunk_backward takes no flags (got 0x%x)", flags);
+  if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);
+  if (chunk != 16 && chunk != 32 && chunk != 64)
+    return fail(KDA_ERR_UNSUPPORTED, "chunk = %d: supported chunks are 16, 32, 64", chunk);
+  const size_t nc = ((size_t)T + chunk - 1) / chunk;
+  if (nc * (size_t)d->batch * d->heads > 0x7fffffffu)
+    return fail(KDA_ERR_UNSUPPORTED, "T = %d: too many (chunk, sequence, head) items", T);
+  if (S0 && !aligned16(S0)) return fail(KDA_ERR_INVALID, "S0 is not 16-byte aligned");
+  if (dST && !aligned16(dST)) return fail(KDA_ERR_INVALID, "dST is not 16-byte aligned");
+  if (dS0 && !aligned16(dS0)) return fail(KDA_ERR_INVALID, "dS0 is not 16-byte aligned");
+  const size_t need = kda::backward_ws_bytes(d->batch, T, d->heads, d->d_k, d->d_v, chunk);
+  if (T > 0) {
+    const size_t esz = io_size(d->io);
+    KDA_REQUIRE_PTR(q, "q", esz);
+    KDA_REQUIRE_PTR(k, "k", esz);
+    KDA_REQUIRE_PTR(v, "v", esz);
+    KDA_REQUIRE_PTR(g, "g", 4);
+    KDA_REQUIRE_PTR(beta, "beta", 4);
+    KDA_REQUIRE_PTR(dO, "dO", esz);
+    KDA_REQUIRE_PTR(dq, "dq", esz);
+    KDA_REQUIRE_PTR(dk, "dk", esz);
+    KDA_REQUIRE_PTR(dv, "dv", esz);
+    KDA_REQUIRE_PTR(dg, "dg", 4);
+    KDA_REQUIRE_PTR(dbeta, "dbeta", 4);
+    KDA_REQUIRE_PTR(workspace, "workspace", 16);
+    if (workspace_bytes < need)
+      return fail(KDA_ERR_INVALID, "workspace of %zu bytes is below the %zu bytes needed",
+                  workspace_bytes, need);
+  } else if (!dS0) {
+    return KDA_OK;  // nothing to compute
+  }
+  kda::BackwardArgs a{q,  k,  v,     g,   beta,       S0,         dO,         dST,
+                      dq, dk, dv,    dg,  dbeta,      dS0,        d->batch,   T,
+                      d->heads, d->d_k, d->d_v, chunk, nullptr, nullptr, nullptr};
+  hipError_t e = kda::launch_backward(a, d->io, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return KDA_OK;
+}
+
 }  // extern "C"

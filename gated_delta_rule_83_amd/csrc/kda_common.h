@@ -124,4 +124,28 @@ size_t prefill_ws_bytes_per_chunk(int H, int B, int dk, int dv, int chunk, kda_d
 hipError_t launch_prefill(const PrefillArgs& a, kda_dtype io, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+struct BackwardArgs {
+  const void* q;        // [B][T][H][dk] q^ (io dtype), after conv, SiLU and L2
+  const void* k;        // [B][T][H][dk] k^
+  const void* v;        // [B][T][H][dv] v^
+  const float* g;       // [B][T][H][dk]
+  const float* beta;    // [B][T][H]
+  const float* S0;      // [B][H][dk][dv] entering state, or NULL (zero)
+  const void* dO;       // [B][T][H][dv] (io dtype)
+  const float* dST;     // [B][H][dk][dv], or NULL (zero)
+  void* dq;             // [B][T][H][dk] (io dtype)
+  void* dk;
+  void* dv;             // [B][T][H][dv] (io dtype)
+  float* dg;            // [B][T][H][dk]
+  float* dbeta;         // [B][T][H]
+  float* dS0;           // [B][H][dk][dv], or NULL (not written)
+  int B, T, H, dkw, dvw, chunk;  // widths d_k, d_v
+  // workspace regions, set by launch_backward
+  float* scratch;       // per (chunk, sequence, head) blocks
+  float* S0s;           // entering state of every chunk [nc][B][H][dk][dv]
+  float* dS1s;          // gradient reaching every chunk's leaving state
+};
+size_t backward_ws_bytes(int B, int T, int H, int dk, int dv, int chunk);
+hipError_t launch_backward(BackwardArgs a, kda_dtype io, void* ws, hipStream_t stream);
+
 }  // namespace kda

@@ -23,7 +23,8 @@ EXPORTED = [
     "kda_state_bytes", "kda_state_alloc", "kda_state_reset", "kda_state_free",
     "kda_state_S", "kda_state_ring", "kda_state_get_dims", "kda_conv_prologue",
     "kda_decode_step", "kda_prefill_workspace_bytes", "kda_chunk_prefill",
-    "kda_gated_rmsnorm", "kda_decode_step_gated", "kda_last_error", "kda_version",
+    "kda_gated_rmsnorm", "kda_decode_step_gated", "kda_backward_workspace_bytes",
+    "kda_chunk_backward", "kda_last_error", "kda_version",
 ]
 
 
@@ -70,6 +71,9 @@ def lib():
         "kda_gated_rmsnorm": (ctypes.c_int, [dp, i32, vp, vp, vp, f32, vp, vp]),
         "kda_decode_step_gated": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
                                                  u32, vp]),
+        "kda_backward_workspace_bytes": (sz, [dp, i32, i32]),
+        "kda_chunk_backward": (ctypes.c_int, [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, vp, i32, vp, sz, u32, vp]),
         "kda_last_error": (ctypes.c_char_p, []),
         "kda_version": (ctypes.c_char_p, []),
     }
@@ -218,6 +222,31 @@ def kda_chunk_prefill(handle, T, q, k, v, g, beta, conv_w, o, chunk=64, workspac
         handle, int(T), _ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io),
         _ptr(g, "g", torch.float32), _ptr(beta, "beta", torch.float32),
         _ptr(conv_w, "conv_w", torch.float32), _ptr(o, "o", io), int(chunk),
+        _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes), int(flags), _stream(stream)))
+
+
+def kda_backward_workspace_bytes(dims, T, chunk=64) -> int:
+    return int(lib().kda_backward_workspace_bytes(ctypes.byref(dims), int(T), int(chunk)))
+
+
+def kda_chunk_backward(dims, T, q, k, v, g, beta, S0, dO, dST, dq, dk, dv, dg, dbeta, dS0,
+                       chunk=64, workspace=None, flags=0, stream=None):
+    """Gradients of the recurrence for T tokens (include/kda.h). S0, dST and
+    dS0 may be None. `workspace` is a device tensor of at least
+    kda_backward_workspace_bytes(dims, T, chunk) bytes; if None, one is taken
+    from torch's allocator for this call."""
+    io = io_dtype(dims)
+    need = kda_backward_workspace_bytes(dims, T, chunk)
+    if workspace is None and need > 0:
+        dev = next(t.device for t in (q, dO, dS0) if isinstance(t, torch.Tensor))
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    f32 = torch.float32
+    _check(lib().kda_chunk_backward(
+        ctypes.byref(dims), int(T), _ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io),
+        _ptr(g, "g", f32), _ptr(beta, "beta", f32), _ptr(S0, "S0", f32), _ptr(dO, "dO", io),
+        _ptr(dST, "dST", f32), _ptr(dq, "dq", io), _ptr(dk, "dk", io), _ptr(dv, "dv", io),
+        _ptr(dg, "dg", f32), _ptr(dbeta, "dbeta", f32), _ptr(dS0, "dS0", f32), int(chunk),
         _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes), int(flags), _stream(stream)))
 
 

@@ -230,6 +230,50 @@ kda_status kda_decode_step_gated(kda_state* st, const void* q, const void* k,
                                  const float* conv_w, const void* gate, const float* norm_w,
                                  float eps, void* o, uint32_t flags, hipStream_t stream);
 
+/* Device workspace that kda_chunk_backward needs for T tokens and `chunk`
+ * (0 if the arguments are invalid): per (chunk, sequence, head) a scratch
+ * block of the chunk's intermediate products, plus the entering state and the
+ * leaving-state gradient of every chunk, all fp32. About 3.5 GB for B = 1,
+ * T = 4096, 96 heads of 128 x 128, chunk 64. */
+size_t kda_backward_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chunk);
+
+/* Gradient of the recurrence (decay, delta read, rank-1 write, readout) for
+ * training, chunkwise: for the forward pass that kda_chunk_prefill runs with
+ * KDA_F_SKIP_CONV | KDA_F_SKIP_L2 from the entering state S0, and the loss
+ * gradients dO of its readouts and dST of its final state, returns the
+ * gradients of its activations, decay, beta and entering state. The
+ * prologue (conv, SiLU, L2) is not part of it.
+ *  q, k:  [B][T][H][d_k] q^, k^ as the recurrence consumes them (io dtype);
+ *  v:     [B][T][H][d_v] v^;
+ *  g:     [B][T][H][d_k] fp32 log-decay, finite and <= 0 (any such value:
+ *         the decay factors are exponentials of non-positive differences);
+ *  beta:  [B][T][H] fp32;
+ *  S0:    [B][H][d_k][d_v] fp32 entering state, or NULL for zero;
+ *  dO:    [B][T][H][d_v] io dtype;  dST: [B][H][d_k][d_v] fp32, or NULL for zero;
+ *  dq, dk: [B][T][H][d_k] io dtype; dv: [B][T][H][d_v] io dtype;
+ *  dg:    [B][T][H][d_k] fp32;  dbeta: [B][T][H] fp32;
+ *  dS0:   [B][H][d_k][d_v] fp32, or NULL (not written).
+ * S0, dST and dS0 must be 16-byte aligned. workspace: device buffer of
+ * kda_backward_workspace_bytes (16-byte aligned, contents on entry ignored).
+ * flags must be 0. chunk: 16, 32 or 64; T need not be a multiple of it.
+ * T = 0 writes dS0 = dST (zero if dST is NULL). All arithmetic is fp32.
+ * The forward pass is recomputed inside (the entering state of every chunk
+ * is kept in the workspace), so the call needs no saved activations beyond
+ * its inputs. Outputs must not overlap the inputs.
+ * Source: "为什么 Kimi K3 敢把 KV Cache 扔掉？…", section 5: chunking is how
+ * the recurrence is trained in parallel (the state handed from chunk to
+ * chunk, the WY representation inside a chunk); section 6 (cumulative
+ * in-chunk decay). The gradient formulas are derived by reverse-mode
+ * differentiation of that chunked form; the pages print none.
+ * Errors: KDA_ERR_INVALID (NULL or misaligned pointer, T < 0, flags, small
+ * workspace), KDA_ERR_UNSUPPORTED (dims, chunk). */
+kda_status kda_chunk_backward(const kda_dims* dims, int32_t T, const void* q,
+                              const void* k, const void* v, const float* g,
+                              const float* beta, const float* S0, const void* dO,
+                              const float* dST, void* dq, void* dk, void* dv, float* dg,
+                              float* dbeta, float* dS0, int32_t chunk, void* workspace,
+                              size_t workspace_bytes, uint32_t flags, hipStream_t stream);
+
 /* Description of the last error on the calling thread ("" if none). */
 const char* kda_last_error(void);
 

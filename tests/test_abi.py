@@ -210,3 +210,51 @@ def test_workspace_size():
     assert kda.kda_prefill_workspace_bytes(d, 4096, 64) == 64 * one
     assert kda.kda_prefill_workspace_bytes(d, 4097, 64) == 65 * one
     assert kda.kda_prefill_workspace_bytes(d, 64, 48) == 0
+
+
+def call_backward(d, T=8, chunk=16, ws_bytes=None, flags=0, S0=None, dST=None, dS0=None,
+                  **ptrs):
+    names = ["q", "k", "v", "g", "beta", "dO", "dq", "dk", "dv", "dg", "dbeta", "ws"]
+    p = {n: ptrs.get(n, FAKE) for n in names}
+    if ws_bytes is None:
+        ws_bytes = kda.kda_backward_workspace_bytes(d, max(T, 0), chunk)
+    L = kda.lib()
+    return L.kda_chunk_backward(
+        ctypes.byref(d), T, _vp(p["q"]), _vp(p["k"]), _vp(p["v"]), _vp(p["g"]), _vp(p["beta"]),
+        _vp(S0), _vp(p["dO"]), _vp(dST), _vp(p["dq"]), _vp(p["dk"]), _vp(p["dv"]),
+        _vp(p["dg"]), _vp(p["dbeta"]), _vp(dS0), chunk, _vp(p["ws"]), ws_bytes, flags, None)
+
+
+def test_backward_workspace_size():
+    d = kda.make_dims(1, 96, 128, 128, kda.KDA_F32)
+    one = kda.kda_backward_workspace_bytes(d, 64, 64)
+    # per chunk-head: 9 [64 x 128] and 2 [64 x 128] token arrays, 5 [64 x 64],
+    # e^{Gam_n} [128], plus the entering state and its gradient [128 x 128]
+    assert one == 96 * 4 * (11 * 64 * 128 + 5 * 64 * 64 + 128 + 2 * 128 * 128)
+    assert kda.kda_backward_workspace_bytes(d, 4096, 64) == 64 * one
+    assert kda.kda_backward_workspace_bytes(d, 4097, 64) == 65 * one
+    assert kda.kda_backward_workspace_bytes(d, 0, 64) == 0
+    assert kda.kda_backward_workspace_bytes(d, 64, 48) == 0
+    assert kda.kda_backward_workspace_bytes(d, -1, 64) == 0
+
+
+def test_backward_validation():
+    d = kda.make_dims(2, 3, 16, 32, kda.KDA_F32)
+    assert call_backward(d, T=-1) == K.KDA_ERR_INVALID
+    assert call_backward(d, chunk=48) == K.KDA_ERR_UNSUPPORTED
+    assert call_backward(d, flags=kda.KDA_F_SKIP_CONV) == K.KDA_ERR_INVALID
+    for name in ["q", "k", "v", "g", "beta", "dO", "dq", "dk", "dv", "dg", "dbeta", "ws"]:
+        assert call_backward(d, **{name: None}) == K.KDA_ERR_INVALID, name
+        assert {"ws": "workspace"}.get(name, name) in kda.last_error()
+    assert call_backward(d, q=FAKE + 2) == K.KDA_ERR_INVALID       # fp32 needs 4 bytes
+    assert call_backward(d, ws=FAKE + 4) == K.KDA_ERR_INVALID      # 16-byte workspace
+    assert call_backward(d, S0=FAKE + 4) == K.KDA_ERR_INVALID
+    assert call_backward(d, dST=FAKE + 4) == K.KDA_ERR_INVALID
+    assert call_backward(d, dS0=FAKE + 4) == K.KDA_ERR_INVALID
+    need = kda.kda_backward_workspace_bytes(d, 8, 16)
+    assert call_backward(d, ws_bytes=need - 1) == K.KDA_ERR_INVALID
+    assert "workspace" in kda.last_error()
+    # T = 0 with no dS0 asked for: nothing to do, nothing enqueued
+    assert call_backward(d, T=0, ws_bytes=0, ws=None, q=None, dO=None) == K.KDA_OK
+    bad = kda.make_dims(1, 1, 24, 32, kda.KDA_F32)
+    assert call_backward(bad, ws_bytes=0) == K.KDA_ERR_UNSUPPORTED

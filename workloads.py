@@ -117,6 +117,19 @@ def draw_output_gate(B, T, H, dv, io="f32", seed=0):
     return z, w, 1e-5
 
 
+def draw_backward_grads(B, T, H, dk, dv, io="f32", seed=0):
+    """Loss gradients for a backward pass, from a generator of their own
+    (seed + 600,000, so the forward draws are unchanged): dO ~ N(0, 1)
+    [B, T, H, dv] (rounded to bf16 for bf16 workloads) and dST ~ N(0, 1)
+    [B, H, dk, dv] (fp32). Returns (dO, dST)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed) + 600_000)
+    dO = torch.randn(B, T, H, dv, generator=gen, dtype=torch.float32)
+    dST = torch.randn(B, H, dk, dv, generator=gen, dtype=torch.float32)
+    if io == "bf16":
+        dO = dO.to(torch.bfloat16)
+    return dO, dST
+
+
 def make(name: str, **overrides) -> Inputs:
     """Draw the named workload; keyword overrides replace its parameters
     (e.g. a smaller T for a quick check)."""
