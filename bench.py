@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_DENSE_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_VECTOR_TFLOPS = 157.3      # MI355X fp32 vector (and fp32 MFMA)
 METRIC = ("KDA tokens/s: decode (B×96h×128²) + prefill T=4K; "
           "HBM GB/s & MFMA % of peak")
 
@@ -74,6 +75,29 @@ def prefill_flops(B, T, H, dk, dv, C):
     and P U (C dv), plus the triangular solve (C^2/3 per column pair)."""
     per = 6 * dk * dv + 2 * C * dk + C * (dk + dv) + C * dv + (C * C) // 3
     return B * T * H * per
+
+
+def backward_flops(B, T, H, dk, dv, C):
+    """Algorithmic FLOPs of the chunked backward per token-head, as its kernels
+    compute it: the forward recomputed (A and P: 2 C dk; W and U': C (dk+dv);
+    U = U' - W S and the state update: 4 dk dv; the inverse C^2/3), the
+    reverse chain (P^T dO: C dv; K^d dS, Q~^T dO, W^T dU: 6 dk dv), the dense
+    gradients (dO S0^T, dU S0^T, U dS1^T: 6 dk dv; dP: C dv), the solve
+    gradients (X^T dW, X^T dU: C (dk+dv); dX: 2 C (dk+dv); T1 and dM: 2 C^2/3)
+    and the decayed-Gram gradients (row and column side: 4 C dk)."""
+    per = (2 * C * dk + C * (dk + dv) + 4 * dk * dv + (C * C) // 3 +
+           C * dv + 6 * dk * dv +
+           6 * dk * dv + C * dv +
+           3 * C * (dk + dv) + 2 * (C * C) // 3 +
+           4 * C * dk)
+    return B * T * H * per
+
+
+def backward_bytes(B, T, H, dk, dv, io_bytes=2):
+    """Compulsory bytes of one backward call: q^, k^, v^, dO and dq, dk, dv in
+    the I/O type, g and dg fp32, beta and dbeta fp32, plus S0, dST and dS0."""
+    per_tok = 2 * ((2 * dk + dv) + dv) * io_bytes + 2 * dk * 4 + 2 * 4
+    return B * T * H * per_tok + 3 * B * H * dk * dv * 4
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
@@ -243,6 +267,65 @@ def stack_bench(kda, workloads, torch, dev, args):
     }
 
 
+def backward_bench(kda, workloads, torch, dev, args):
+    """The chunked backward on the 4096-token, 96-head, 128x128 bf16 workload
+    (random entering state): q^, k^, v^ made on the device by kda_conv_prologue
+    from the raw draws (rounded to bf16), dO and dST from
+    workloads.draw_backward_grads; median of event-bracketed calls after
+    warm-up calls."""
+    inp = workloads.make("prefill_4k", s0_random=True)
+    B, T, H, dk, dv = inp.dims
+    dims = kda.make_dims(B, H, dk, dv, torch.bfloat16)
+    conv_w = inp.conv_w.to(dev)
+    ring = torch.zeros(B, 3, H * (2 * dk + dv), dtype=torch.bfloat16, device=dev)
+    acts = [torch.empty(B, T, H, d, device=dev) for d in (dk, dk, dv)]
+    kda.kda_conv_prologue(dims, T, inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), conv_w, ring,
+                          *acts)
+    qh, kh, vh = (x.to(torch.bfloat16) for x in acts)
+    del acts
+    g, beta, S0 = inp.g.to(dev), inp.beta.to(dev), inp.S0.to(dev)
+    dO, dST = workloads.draw_backward_grads(B, T, H, dk, dv, io="bf16", seed=3)
+    dO, dST = dO.to(dev), dST.to(dev)
+    out = [torch.empty(B, T, H, dk, dtype=torch.bfloat16, device=dev),
+           torch.empty(B, T, H, dk, dtype=torch.bfloat16, device=dev),
+           torch.empty(B, T, H, dv, dtype=torch.bfloat16, device=dev),
+           torch.empty(B, T, H, dk, device=dev), torch.empty(B, T, H, device=dev),
+           torch.empty(B, H, dk, dv, device=dev)]
+    ws = torch.empty(kda.kda_backward_workspace_bytes(dims, T, 64), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        kda.kda_chunk_backward(dims, T, qh, kh, vh, g, beta, S0, dO, dST, *out, chunk=64,
+                               workspace=ws)
+
+    for _ in range(args.backward_warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.backward_reps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    med = ms[len(ms) // 2]
+    assert all(torch.isfinite(t.float()).all().item() for t in out)
+    flops = backward_flops(B, T, H, dk, dv, 64)
+    nbytes = backward_bytes(B, T, H, dk, dv)
+    res = {"workload": "chunked backward (gradients of q^, k^, v^, g, beta, S0) of the "
+                       "4096-token prefill, batch 1, 96 heads of 128x128, chunk 64, bf16 I/O, "
+                       "fp32 arithmetic",
+           "tokens_per_s": B * T / (med / 1e3), "ms": med, "ms_min": ms[0], "ms_max": ms[-1],
+           "calls": len(ms), "flops": flops, "tflops": flops / (med / 1e3) / 1e12,
+           "fp32_frac": flops / (med / 1e3) / 1e12 / FP32_VECTOR_TFLOPS,
+           "compulsory_bytes": nbytes, "hbm_GBps": nbytes / (med / 1e3) / 1e9,
+           "hbm_frac": nbytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS,
+           "workspace_bytes": ws.numel()}
+    del ws, out
+    return res
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -259,6 +342,10 @@ def parse():
     p.add_argument("--no-stack", action="store_true",
                    help="skip the 69-layer stack measurements")
     p.add_argument("--stack-reps", type=int, default=20)
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip the chunked backward measurement")
+    p.add_argument("--backward-reps", type=int, default=10)
+    p.add_argument("--backward-warmup", type=int, default=5)
     p.add_argument("--no-gdn", action="store_true",
                    help="skip the flag variants (KDA_F_SCALAR_G, KDA_F_RAW_GATES)")
     return p.parse_args()
@@ -497,6 +584,8 @@ def main():
         "KDA_F_RAW_GATES (the decay and beta formed in the kernels from raw projections): the "
         "decode and prefill workloads above drawn as pre-activations", raw_gates=True)
 
+    bwd = None if args.no_backward else backward_bench(kda, workloads, torch, dev, args)
+
     # ---------------- one K3-shape decode step: latency, warm and flushed ---
     single = single_step_latency(kda, workloads, torch, dev)
 
@@ -544,6 +633,20 @@ def main():
         cpu["one_core"] = {"value": B * n1 / t1, "unit": "tokens/s", "cores": 1,
                            "sample": f"first {n1} decode steps, {B} sequences x {H} heads "
                                      f"({t1:.1f} s)"}
+        # the gradient oracle (sequential fp64, one thread) on one head of the
+        # 4096-token workload, scaled to its 96 heads
+        bq = workloads.make("prefill_4k", s0_random=True)
+        qb, kb, vb = kda_oracle.prologue(bq.q, bq.k, bq.v, bq.conv_w, bq.ring0)[:3]
+        dOb, dSTb = workloads.draw_backward_grads(1, pT, pH, pdk, pdv, io="bf16", seed=3)
+        tb = time.perf_counter()
+        kda_oracle.default().core_backward(qb[:, :, :1], kb[:, :, :1], vb[:, :, :1],
+                                           bq.g[:, :, :1], bq.beta[:, :, :1], bq.S0[:, :1],
+                                           dOb[:, :, :1], dSTb[:, :1])
+        tb = time.perf_counter() - tb
+        cpu["backward"] = {"value": pT / (tb * pH), "unit": "tokens/s", "cores": 1,
+                           "sample": f"gradient of the recurrence for head 0 of the "
+                                     f"4096-token workload ({tb:.1f} s), scaled to 96 heads"}
+        del bq, qb, kb, vb, dOb, dSTb
         # and on the 4096-token prefill workload, all of it
         tp0 = time.perf_counter()
         kda_oracle.forward(pin.q, pin.k, pin.v, pin.g, pin.beta, pin.conv_w, pin.S0, pin.ring0)
@@ -586,6 +689,7 @@ def main():
                     "mfma_frac": pflops / (pre_ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
                     "compulsory_bytes": pbytes, "flops": pflops},
         "stack": stack,
+        "backward": bwd,
         "scalar_decay": gdn,
         "raw_gates": raw,
         "output_gate": {

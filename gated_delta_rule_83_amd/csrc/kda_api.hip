@@ -402,12 +402,13 @@ kda_status kda_chunk_backward(const kda_dims* d, int32_t T, const void* q, const
   const size_t need = kda::backward_ws_bytes(d->batch, T, d->heads, d->d_k, d->d_v, chunk);
   if (T > 0) {
     const size_t esz = io_size(d->io);
-    KDA_REQUIRE_PTR(q, "q", esz);
-    KDA_REQUIRE_PTR(k, "k", esz);
-    KDA_REQUIRE_PTR(v, "v", esz);
-    KDA_REQUIRE_PTR(g, "g", 4);
+    // q, k, v, g and dO are read 16 bytes (or 8 for bf16) at a time
+    KDA_REQUIRE_PTR(q, "q", 16);
+    KDA_REQUIRE_PTR(k, "k", 16);
+    KDA_REQUIRE_PTR(v, "v", 16);
+    KDA_REQUIRE_PTR(g, "g", 16);
     KDA_REQUIRE_PTR(beta, "beta", 4);
-    KDA_REQUIRE_PTR(dO, "dO", esz);
+    KDA_REQUIRE_PTR(dO, "dO", 16);
     KDA_REQUIRE_PTR(dq, "dq", esz);
     KDA_REQUIRE_PTR(dk, "dk", esz);
     KDA_REQUIRE_PTR(dv, "dv", esz);

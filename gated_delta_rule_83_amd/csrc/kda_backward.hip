@@ -31,6 +31,8 @@
 // -> decayed-Gram gradients and dg (per chunk-head). The decay factors are
 // formed as exponentials of non-positive differences, so any finite g <= 0
 // is accepted.
+#include <type_traits>
+
 #include "kda_common.h"
 
 namespace kda {
@@ -83,29 +85,80 @@ __device__ __forceinline__ Item item_of(const BackwardArgs& a, long it) {
   return r;
 }
 
+// 16 x 16 tile on fp32 MFMA (v_mfma_f32_16x16x4_f32): acc += A B over k in
+// [0, K), K a multiple of 4, with a(i, k) = A[tile row i][k] and
+// b(k, j) = B[k][tile column j]. Lane l supplies A[l % 16][k + l / 16] and
+// B[k + l / 16][l % 16]; element e of the result is tile row 4 (l / 16) + e,
+// column l % 16.
+template <class FA, class FB>
+__device__ __forceinline__ f32x4 mma_tile(f32x4 acc, int K, FA&& a, FB&& b) {
+  const int l = threadIdx.x % kWave, i = l % 16, kk = l / 16;
+#pragma unroll 4
+  for (int k = 0; k < K; k += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(i, k + kk), b(k + kk, i), acc, 0, 0, 0);
+  return acc;
+}
+
+// Sum over the 16 lanes of a row group (lanes with equal l / 16).
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
+
+// Four consecutive elements as fp32 (one 16- or 8-byte load).
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4f(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// Stages ROWS x COLS values into LDS (row stride LD floats, 16-byte aligned
+// rows): ld4(r, c) gives row r, columns c..c+3 for r < live; rows at or past
+// `live` are zeros. Every load of a thread is issued before its stores.
+template <int NT, int ROWS, int COLS, int LD, class F>
+__device__ __forceinline__ void stage_rows(float* dst, int live, F&& ld4) {
+  static_assert(COLS % 4 == 0 && LD % 4 == 0, "16-byte pieces");
+  constexpr int Q = COLS / 4, TOT = ROWS * Q, PER = (TOT + NT - 1) / NT;
+  f32x4 buf[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int i = (int)threadIdx.x + p * NT, r = i / Q, c = 4 * (i % Q);
+    buf[p] = (i < TOT && r < live) ? ld4(r, c) : kZero4;
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int i = (int)threadIdx.x + p * NT, r = i / Q, c = 4 * (i % Q);
+    if (i < TOT) *reinterpret_cast<f32x4*>(dst + r * LD + c) = buf[p];
+  }
+}
+constexpr int kBP = 1024;  // threads of the per-chunk kernels with scalar loops
+
 // ---- 1. per chunk-head: Gam, A, P, X, Q~, K~, K^d, W, U' --------------------
 template <int DK, int DV, typename IO>
-__global__ __launch_bounds__(kBT) void bw_prep_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kBP) void bw_prep_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  constexpr int PK = DK + 1;
-  __shared__ float sK[CM][PK], sQ[CM][PK], sG[CM][PK];
-  __shared__ float sM[CM][CM + 1], sX[CM][CM + 1];
-  __shared__ float sb[CM];
+  constexpr int PK = DK + 4, PKV = (DK > DV ? DK : DV) + 4;
+  constexpr int NW = kBP / kWave;
+  __shared__ __attribute__((aligned(16))) float sK[CM][PKV], sQ[CM][PK], sG[CM][PK];
+  __shared__ __attribute__((aligned(16))) float sM[CM][CM + 1], sX[CM][CM + 4];
+  __shared__ float sb[CM];  // sK later holds beta V^
   const Item it = item_of(a, blockIdx.x);
-  const int n = it.n;
+  const int n = it.n, n4 = (n + 3) & ~3;
   float* blk = a.scratch + (long)blockIdx.x * L::n;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l16 = lane % 16, r4 = 4 * (lane / 16);
   const IO* q = static_cast<const IO*>(a.q);
   const IO* k = static_cast<const IO*>(a.k);
   const IO* v = static_cast<const IO*>(a.v);
-  for (int i = tid; i < n * DK; i += kBT) {
-    const int r = i / DK, cc = i % DK;
-    const long off = tok(a, it.b, it.t0 + r, it.h) * DK + cc;
-    sK[r][cc] = to_f32(k[off]);
-    sQ[r][cc] = to_f32(q[off]);
-    sG[r][cc] = a.g[off];
-  }
-  if (tid < n) sb[tid] = a.beta[tok(a, it.b, it.t0 + tid, it.h)];
+  const long row0 = tok(a, it.b, it.t0, it.h), rs = (long)a.H;  // token row r: row0 + r * rs
+  stage_rows<kBP, CM, DK, PKV>(&sK[0][0], n, [&](int r, int c) { return ld4f(k + (row0 + r * rs) * DK + c); });
+  stage_rows<kBP, CM, DK, PK>(&sQ[0][0], n, [&](int r, int c) { return ld4f(q + (row0 + r * rs) * DK + c); });
+  stage_rows<kBP, CM, DK, PK>(&sG[0][0], n, [&](int r, int c) { return ld4f(a.g + (row0 + r * rs) * DK + c); });
+  for (int i = tid; i < CM * CM; i += kBP) sX[i / CM][i % CM] = 0.f;
+  if (tid < CM) sb[tid] = tid < n ? a.beta[row0 + tid * rs] : 0.f;
   __syncthreads();
   if (tid < DK) {
     float s = 0.f;
@@ -115,12 +168,13 @@ __global__ __launch_bounds__(kBT) void bw_prep_kernel(BackwardArgs a) {
     }
   }
   __syncthreads();
-  // A (strictly lower) and P (lower): wave w takes rows w, w+4, ..., lane j
+  // A (strictly lower) and P (lower): wave w takes rows w, w+NW, ..., lane j
   // the column; every exponent Gam_r - Gam_j (j <= r) is <= 0.
-  for (int r = wv; r < n; r += 4) {
+  for (int r = wv; r < n; r += NW) {
     const int j = lane;
     float accA = 0.f, accP = 0.f;
     if (j <= r) {
+#pragma unroll 4
       for (int cc = 0; cc < DK; ++cc) {
         const float kj = sK[j][cc] * __expf(sG[r][cc] - sG[j][cc]);
         accA += sK[r][cc] * kj;
@@ -133,43 +187,64 @@ __global__ __launch_bounds__(kBT) void bw_prep_kernel(BackwardArgs a) {
   }
   __syncthreads();
   // X = (I + diag(beta) A)^-1, unit lower triangular, by forward
-  // substitution: lane j of wave 0 owns column j.
-  if (wv == 0) {
-    const int j = lane;
+  // substitution: waves 0-3 own 16 columns each, four lanes per column split
+  // each row's dot product (rows >= n stay zero). A row's new value is
+  // written by lane group 0 and read by the other groups of the same wave in
+  // the next row (LDS accesses of one wave complete in order).
+  if (wv < 4) {
+    const int j = 16 * wv + l16, p = lane / 16;
     for (int r = 0; r < n; ++r) {
       float acc = 0.f;
-      for (int m = 0; m < r; ++m) acc += sM[r][m] * sX[m][j];
-      sX[r][j] = r > j ? -acc : (r == j ? 1.f : 0.f);
+      for (int m = p; m < r; m += 4) acc += sM[r][m] * sX[m][j];
+      acc += __shfl_xor(acc, 16, kWave);
+      acc += __shfl_xor(acc, 32, kWave);
+      if (p == 0) sX[r][j] = r > j ? -acc : (r == j ? 1.f : 0.f);
     }
   }
   __syncthreads();
-  for (int i = tid; i < n * CM; i += kBT) {
-    const int r = i / CM, j = i % CM;
-    blk[L::oX + i] = j < n ? sX[r][j] : 0.f;
-  }
-  for (int i = tid; i < n * DK; i += kBT) {
+  for (int i = tid; i < n * CM; i += kBP) blk[L::oX + i] = sX[i / CM][i % CM];
+  for (int i = tid; i < n * DK; i += kBP) {
     const int r = i / DK, cc = i % DK;
     const float G = sG[r][cc], eg = __expf(G), kt = eg * sK[r][cc];
     blk[L::oQt + i] = eg * sQ[r][cc];
     blk[L::oKt + i] = kt;
     blk[L::oKd + i] = __expf(sG[n - 1][cc] - G) * sK[r][cc];
     blk[L::oG + i] = G;
-    sQ[r][cc] = sb[r] * kt;  // beta K~ for W (each element read by its writer only)
+    sQ[r][cc] = sb[r] * kt;  // beta K~ (each element read by its writer only)
   }
+  for (int i = n * DK + tid; i < CM * DK; i += kBP) sQ[i / DK][i % DK] = 0.f;
   if (tid < DK) blk[L::oEn + tid] = __expf(sG[n - 1][tid]);
   __syncthreads();
-  for (int i = tid; i < n * DK; i += kBT) {  // W = X (beta K~)
-    const int r = i / DK, cc = i % DK;
-    float acc = 0.f;
-    for (int j = 0; j <= r; ++j) acc += sX[r][j] * sQ[j][cc];
-    blk[L::oW + i] = acc;
+  // beta V^ over the (now unused) k rows
+  stage_rows<kBP, CM, DV, PKV>(&sK[0][0], n, [&](int r, int c) {
+    return sb[r] * ld4f(v + (row0 + r * rs) * DV + c);
+  });
+  // W = X (beta K~): 16 x 16 tiles over the waves
+  constexpr int TW = (CM / 16) * (DK / 16);
+  for (int t = wv; t < TW; t += NW) {
+    const int rt = t / (DK / 16), ct = t % (DK / 16);
+    if (16 * rt >= n) continue;
+    const f32x4 acc = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[16 * rt + i][kx]; },
+                               [&](int kx, int j) { return sQ[kx][16 * ct + j]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e;
+      if (row < n) blk[L::oW + (long)row * DK + 16 * ct + l16] = acc[e];
+    }
   }
-  for (int i = tid; i < n * DV; i += kBT) {  // U' = X (beta V^)
-    const int r = i / DV, l = i % DV;
-    float acc = 0.f;
-    for (int j = 0; j <= r; ++j)
-      acc += sX[r][j] * sb[j] * to_f32(v[tok(a, it.b, it.t0 + j, it.h) * DV + l]);
-    blk[L::oU + i] = acc;
+  __syncthreads();
+  // U' = X (beta V^)
+  constexpr int TU = (CM / 16) * (DV / 16);
+  for (int t = wv; t < TU; t += NW) {
+    const int rt = t / (DV / 16), ct = t % (DV / 16);
+    if (16 * rt >= n) continue;
+    const f32x4 acc = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[16 * rt + i][kx]; },
+                               [&](int kx, int j) { return sK[kx][16 * ct + j]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e;
+      if (row < n) blk[L::oU + (long)row * DV + 16 * ct + l16] = acc[e];
+    }
   }
 }
 
@@ -178,274 +253,468 @@ constexpr int bw_dvb() {
   return DV < 32 ? DV : 32;
 }
 
+// Tiling shared by the two chains: a workgroup holds a DK x DVB block of the
+// state (or of its gradient) as 16 x 16 MFMA accumulators, tile t = w + 4 m
+// of wave w; the token-row blocks (U, dU, dO) are CM x DVB.
+template <int DK, int DV>
+struct ChainTiles {
+  static constexpr int DVB = bw_dvb<DV>(), NB = DV / DVB, NCT = DVB / 16;
+  static constexpr int SPB = DVB + 4, SPO = (DK > CM ? DK : CM) + 4;
+  static constexpr int NST = (DK / 16) * NCT, SPW = (NST + 3) / 4;
+  static constexpr int NUT = (CM / 16) * NCT, UPW = (NUT + 3) / 4;
+};
+
 // ---- 2. forward state chain: entering state of every chunk, U ---------------
-// One workgroup per (32-column block, head, sequence); the S block lives in
-// LDS. Per chunk: keep S, U = U' - W S (over U' in the scratch), then
-// S = Diag(e^{Gam_n}) S + K^d^T U.
+// One workgroup per (32-column block, head, sequence). Per chunk: keep S,
+// U = U' - W S (over U' in the scratch), S = Diag(e^{Gam_n}) S + K^d^T U.
 template <int DK, int DV>
 __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  constexpr int DVB = bw_dvb<DV>(), NB = DV / DVB;
-  __shared__ float sS[DK][DVB];
-  __shared__ float sU[CM][DVB];
-  __shared__ float sO[CM][DK + 1];
-  const int cbk = blockIdx.x % NB, bh = blockIdx.x / NB, cb0 = cbk * DVB;
+  using CT = ChainTiles<DK, DV>;
+  constexpr int NCT = CT::NCT, SPW = CT::SPW, UPW = CT::UPW, NST = CT::NST, NUT = CT::NUT;
+  __shared__ float sS[DK][CT::SPB];
+  __shared__ float sU[CM][CT::SPB];
+  __shared__ __attribute__((aligned(16))) float sO[CM][CT::SPO];
+  __shared__ __attribute__((aligned(16))) float sEn[DK];
+  const int cbk = blockIdx.x % CT::NB, bh = blockIdx.x / CT::NB, cb0 = cbk * CT::DVB;
   const int BH = a.B * a.H, nc = (a.T + a.chunk - 1) / a.chunk;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < DK * DVB; i += kBT) {
-    const int r = i / DVB, j = i % DVB;
-    sS[r][j] = a.S0 ? a.S0[((long)bh * DK + r) * DV + cb0 + j] : 0.f;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l16 = lane % 16, r4 = 4 * (lane / 16);
+  f32x4 accS[SPW];
+#pragma unroll
+  for (int m = 0; m < SPW; ++m) {
+    const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      accS[m][e] = (t < NST && a.S0)
+                       ? a.S0[((long)bh * DK + 16 * rt + r4 + e) * DV + cb0 + 16 * ct + l16]
+                       : 0.f;
   }
   for (int c = 0; c < nc; ++c) {
-    const int n = min(a.chunk, a.T - c * a.chunk);
+    const int n = min(a.chunk, a.T - c * a.chunk), n4 = (n + 3) & ~3;
     const long item = (long)c * BH + bh;
     float* blk = a.scratch + item * L::n;
     float* Sk = a.S0s + item * DK * DV;
-    __syncthreads();  // S of this chunk complete
-    for (int i = tid; i < DK * DVB; i += kBT) {
-      const int r = i / DVB, j = i % DVB;
-      Sk[(long)r * DV + cb0 + j] = sS[r][j];
+    __syncthreads();  // the previous chunk is done with sS, sU, sO
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      if (t < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * rt + r4 + e, col = 16 * ct + l16;
+          Sk[(long)row * DV + cb0 + col] = accS[m][e];
+          sS[row][col] = accS[m][e];
+        }
+      }
     }
-    for (int i = tid; i < n * DK; i += kBT) sO[i / DK][i % DK] = blk[L::oW + i];
+    stage_rows<kBT, CM, DK, CT::SPO>(&sO[0][0], n,
+                                     [&](int r, int cx) { return ld4f(blk + L::oW + r * DK + cx); });
+    stage_rows<kBT, 1, DK, DK>(sEn, 1, [&](int, int cx) { return ld4f(blk + L::oEn + cx); });
     __syncthreads();
-    for (int i = tid; i < n * DVB; i += kBT) {
-      const int r = i / DVB, j = i % DVB;
-      float acc = blk[L::oU + (long)r * DV + cb0 + j];
-      for (int cc = 0; cc < DK; ++cc) acc -= sO[r][cc] * sS[cc][j];
-      sU[r][j] = acc;
-      blk[L::oU + (long)r * DV + cb0 + j] = acc;
+#pragma unroll
+    for (int m = 0; m < UPW; ++m) {  // U = U' - W S
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      if (t < NUT) {
+        const f32x4 ws = mma_tile(kZero4, DK, [&](int i, int kx) { return sO[16 * rt + i][kx]; },
+                                  [&](int kx, int j) { return sS[kx][16 * ct + j]; });
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * rt + r4 + e, col = 16 * ct + l16;
+          float u = 0.f;
+          if (row < n) {
+            float* pu = blk + L::oU + (long)row * DV + cb0 + col;
+            u = *pu - ws[e];
+            *pu = u;
+          }
+          sU[row][col] = u;
+        }
+      }
     }
     __syncthreads();
-    for (int i = tid; i < n * DK; i += kBT) sO[i / DK][i % DK] = blk[L::oKd + i];
+    stage_rows<kBT, CM, DK, CT::SPO>(&sO[0][0], n,
+                                     [&](int r, int cx) { return ld4f(blk + L::oKd + r * DK + cx); });
     __syncthreads();
-    for (int i = tid; i < DK * DVB; i += kBT) {
-      const int cc = i / DVB, j = i % DVB;
-      float acc = blk[L::oEn + cc] * sS[cc][j];
-      for (int r = 0; r < n; ++r) acc += sO[r][cc] * sU[r][j];
-      sS[cc][j] = acc;
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {  // S = Diag(e^{Gam_n}) S + K^d^T U
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      if (t < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accS[m][e] *= sEn[16 * rt + r4 + e];
+        accS[m] = mma_tile(accS[m], n4, [&](int i, int kx) { return sO[kx][16 * rt + i]; },
+                           [&](int kx, int j) { return sU[kx][16 * ct + j]; });
+      }
     }
   }
 }
 
 // ---- 3. reverse chain: dS1 of every chunk, dU, and dS0 ----------------------
-// Same grid as the state chain; chunks from the last to the first. The dS
-// block lives in LDS; each thread keeps its elements of the update in
-// registers across the two operand stages.
+// Same grid and tiling as the state chain, chunks from the last to the
+// first; one staging buffer holds P, K^d, Q~ and W in turn.
 template <int DK, int DV, typename IO>
 __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  constexpr int DVB = bw_dvb<DV>(), NB = DV / DVB, PER = DK * DVB / kBT;
-  static_assert(DK * DVB % kBT == 0, "dS block per thread");
-  __shared__ float sdS[DK][DVB];
-  __shared__ float sdO[CM][DVB];
-  __shared__ float sdU[CM][DVB];
-  __shared__ float sO[CM][DK + 1];
-  const int cbk = blockIdx.x % NB, bh = blockIdx.x / NB, cb0 = cbk * DVB;
+  using CT = ChainTiles<DK, DV>;
+  constexpr int NCT = CT::NCT, SPW = CT::SPW, UPW = CT::UPW, NST = CT::NST, NUT = CT::NUT;
+  constexpr int DVB = CT::DVB;
+  __shared__ float sdS[DK][CT::SPB];
+  __shared__ __attribute__((aligned(16))) float sdO[CM][CT::SPB];
+  __shared__ float sdU[CM][CT::SPB];
+  __shared__ __attribute__((aligned(16))) float sO[CM][CT::SPO];
+  __shared__ __attribute__((aligned(16))) float sEn[DK];
+  const int cbk = blockIdx.x % CT::NB, bh = blockIdx.x / CT::NB, cb0 = cbk * DVB;
   const int b = bh / a.H, h = bh % a.H;
   const int BH = a.B * a.H, nc = (a.T + a.chunk - 1) / a.chunk;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l16 = lane % 16, r4 = 4 * (lane / 16);
   const IO* dO = static_cast<const IO*>(a.dO);
-  for (int i = tid; i < DK * DVB; i += kBT) {
-    const int r = i / DVB, j = i % DVB;
-    sdS[r][j] = a.dST ? a.dST[((long)bh * DK + r) * DV + cb0 + j] : 0.f;
+  f32x4 accS[SPW];
+#pragma unroll
+  for (int m = 0; m < SPW; ++m) {
+    const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      accS[m][e] = (t < NST && a.dST)
+                       ? a.dST[((long)bh * DK + 16 * rt + r4 + e) * DV + cb0 + 16 * ct + l16]
+                       : 0.f;
   }
+  // rows at or past the chunk's last token are zeroed (P is zero right of
+  // its diagonal, so its columns past the last token are zero as stored)
+  int cur_n = 0;
+  auto stage = [&](const float* src, auto cols) {
+    constexpr int COLS = decltype(cols)::value;
+    stage_rows<kBT, CM, COLS, CT::SPO>(&sO[0][0], cur_n,
+                                       [&](int r, int cx) { return ld4f(src + r * COLS + cx); });
+  };
   for (int c = nc - 1; c >= 0; --c) {
-    const int t0 = c * a.chunk, n = min(a.chunk, a.T - t0);
+    const int t0 = c * a.chunk, n = min(a.chunk, a.T - t0), n4 = (n + 3) & ~3;
     const long item = (long)c * BH + bh;
     float* blk = a.scratch + item * L::n;
     float* dSk = a.dS1s + item * DK * DV;
-    __syncthreads();  // dS of this chunk complete
-    for (int i = tid; i < DK * DVB; i += kBT) {
-      const int r = i / DVB, j = i % DVB;
-      dSk[(long)r * DV + cb0 + j] = sdS[r][j];
-    }
-    for (int i = tid; i < n * DVB; i += kBT) {
-      const int r = i / DVB, j = i % DVB;
-      sdO[r][j] = to_f32(dO[tok(a, b, t0 + r, h) * DV + cb0 + j]);
-    }
-    for (int i = tid; i < n * DK; i += kBT) sO[i / DK][i % DK] = blk[L::oKd + i];
-    __syncthreads();
-    const float* P = blk + L::oP;
-    for (int i = tid; i < n * DVB; i += kBT) {  // dU = P^T dO + K^d dS
-      const int r = i / DVB, j = i % DVB;
-      float acc = 0.f;
-      for (int i2 = r; i2 < n; ++i2) acc += P[i2 * CM + r] * sdO[i2][j];
-      for (int cc = 0; cc < DK; ++cc) acc += sO[r][cc] * sdS[cc][j];
-      sdU[r][j] = acc;
-      blk[L::odU + (long)r * DV + cb0 + j] = acc;
-    }
-    __syncthreads();
-    for (int i = tid; i < n * DK; i += kBT) sO[i / DK][i % DK] = blk[L::oQt + i];
-    __syncthreads();
-    float acc[PER];
+    __syncthreads();  // the previous chunk is done with every buffer
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {  // Diag(e^{Gam_n}) dS + Q~^T dO
-      const int i = tid + p * kBT, cc = i / DVB, j = i % DVB;
-      float s = blk[L::oEn + cc] * sdS[cc][j];
-      for (int r = 0; r < n; ++r) s += sO[r][cc] * sdO[r][j];
-      acc[p] = s;
+    for (int m = 0; m < SPW; ++m) {
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      if (t < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * rt + r4 + e, col = 16 * ct + l16;
+          dSk[(long)row * DV + cb0 + col] = accS[m][e];
+          sdS[row][col] = accS[m][e];
+        }
+      }
+    }
+    cur_n = n;
+    const long drow0 = tok(a, b, t0, h);
+    stage_rows<kBT, CM, DVB, CT::SPB>(&sdO[0][0], n, [&](int r, int cx) {
+      return ld4f(dO + (drow0 + (long)r * a.H) * DV + cb0 + cx);
+    });
+    stage_rows<kBT, 1, DK, DK>(sEn, 1, [&](int, int cx) { return ld4f(blk + L::oEn + cx); });
+    stage(blk + L::oP, std::integral_constant<int, CM>());
+    __syncthreads();
+    f32x4 accU[UPW];
+#pragma unroll
+    for (int m = 0; m < UPW; ++m) {  // P^T dO
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      accU[m] = kZero4;
+      if (t < NUT)
+        accU[m] = mma_tile(kZero4, n4, [&](int i, int kx) { return sO[kx][16 * rt + i]; },
+                           [&](int kx, int j) { return sdO[kx][16 * ct + j]; });
     }
     __syncthreads();
-    for (int i = tid; i < n * DK; i += kBT) sO[i / DK][i % DK] = blk[L::oW + i];
+    stage(blk + L::oKd, std::integral_constant<int, DK>());
     __syncthreads();
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {  // - W^T dU
-      const int i = tid + p * kBT, cc = i / DVB, j = i % DVB;
-      float s = acc[p];
-      for (int r = 0; r < n; ++r) s -= sO[r][cc] * sdU[r][j];
-      sdS[cc][j] = s;
+    for (int m = 0; m < UPW; ++m) {  // + K^d dS
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      if (t < NUT) {
+        accU[m] = mma_tile(accU[m], DK, [&](int i, int kx) { return sO[16 * rt + i][kx]; },
+                           [&](int kx, int j) { return sdS[kx][16 * ct + j]; });
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * rt + r4 + e, col = 16 * ct + l16;
+          const float u = row < n ? accU[m][e] : 0.f;
+          sdU[row][col] = u;
+          if (row < n) blk[L::odU + (long)row * DV + cb0 + col] = u;
+        }
+      }
+    }
+    __syncthreads();
+    stage(blk + L::oQt, std::integral_constant<int, DK>());
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {  // dS = Diag(e^{Gam_n}) dS + Q~^T dO
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      if (t < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accS[m][e] *= sEn[16 * rt + r4 + e];
+        accS[m] = mma_tile(accS[m], n4, [&](int i, int kx) { return sO[kx][16 * rt + i]; },
+                           [&](int kx, int j) { return sdO[kx][16 * ct + j]; });
+      }
+    }
+    __syncthreads();
+    stage(blk + L::oW, std::integral_constant<int, DK>());
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {  // - W^T dU
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      if (t < NST)
+        accS[m] = mma_tile(accS[m], n4, [&](int i, int kx) { return -sO[kx][16 * rt + i]; },
+                           [&](int kx, int j) { return sdU[kx][16 * ct + j]; });
     }
   }
-  __syncthreads();
   if (a.dS0) {
-    for (int i = tid; i < DK * DVB; i += kBT) {
-      const int r = i / DVB, j = i % DVB;
-      a.dS0[((long)bh * DK + r) * DV + cb0 + j] = sdS[r][j];
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      if (t < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a.dS0[((long)bh * DK + 16 * rt + r4 + e) * DV + cb0 + 16 * ct + l16] = accS[m][e];
+      }
     }
   }
 }
 
 // ---- 4. per chunk-head: the products with S0 and dS1, and dP -----------------
-// Wave w takes channels w, w+4, ...; lane r is the token row, so the rows of
-// S0 and dS1 are read as wave-uniform vectors.
+// Contractions over d_v in slabs of 32 columns staged in LDS; wave w owns the
+// column tiles w, w+4, ... of dQ~, dW and dK^d (all row tiles) and column
+// tile w of dP.
 template <int DK, int DV, typename IO>
 __global__ __launch_bounds__(kBT) void bw_grad_dense_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  constexpr int PV = DV + 1;
-  __shared__ float sdO[CM][PV], sdU[CM][PV], sU[CM][PV];
+  constexpr int SL = DV < 32 ? DV : 32, SLP = SL + 4;
+  constexpr int CTN = DK / 16, CPW = (CTN + 3) / 4, RT = CM / 16;
+  __shared__ __attribute__((aligned(16))) float sS0[DK][SLP], sdS1[DK][SLP];
+  __shared__ __attribute__((aligned(16))) float sdO[CM][SLP], sdU[CM][SLP], sU[CM][SLP];
+  __shared__ float sdD[DK];
   const Item it = item_of(a, blockIdx.x);
   const int n = it.n;
   float* blk = a.scratch + (long)blockIdx.x * L::n;
   const float* S0 = a.S0s + (long)blockIdx.x * DK * DV;
   const float* dS1 = a.dS1s + (long)blockIdx.x * DK * DV;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l16 = lane % 16, r4 = 4 * (lane / 16);
   const IO* dO = static_cast<const IO*>(a.dO);
-  for (int i = tid; i < n * DV; i += kBT) {
-    const int r = i / DV, l = i % DV;
-    sdO[r][l] = to_f32(dO[tok(a, it.b, it.t0 + r, it.h) * DV + l]);
-    sdU[r][l] = blk[L::odU + i];
-    sU[r][l] = blk[L::oU + i];
-  }
-  __syncthreads();
-  const int r = lane;
-  const bool live = r < n;
-  for (int cc = wv; cc < DK; cc += 4) {
-    float dq = 0.f, dw = 0.f, dkd = 0.f, dd = 0.f;
-    if (live) {
-      for (int l = 0; l < DV; l += 4) {
-        const f32x4 s = *reinterpret_cast<const f32x4*>(S0 + (long)cc * DV + l);
-        const f32x4 ds = *reinterpret_cast<const f32x4*>(dS1 + (long)cc * DV + l);
+  const long row0 = tok(a, it.b, it.t0, it.h);
+  f32x4 aQ[CPW][RT], aW[CPW][RT], aK[CPW][RT], aP[RT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dq += sdO[r][l + e] * s[e];
-          dw += sdU[r][l + e] * s[e];
-          dkd += sU[r][l + e] * ds[e];
-          dd += ds[e] * s[e];
+  for (int m = 0; m < CPW; ++m)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) aQ[m][rt] = aW[m][rt] = aK[m][rt] = kZero4;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) aP[rt] = kZero4;
+  float dd = 0.f;
+  for (int l0 = 0; l0 < DV; l0 += SL) {
+    __syncthreads();
+    stage_rows<kBT, DK, SL, SLP>(&sS0[0][0], DK,
+                                 [&](int r, int c) { return ld4f(S0 + (long)r * DV + l0 + c); });
+    stage_rows<kBT, DK, SL, SLP>(&sdS1[0][0], DK,
+                                 [&](int r, int c) { return ld4f(dS1 + (long)r * DV + l0 + c); });
+    stage_rows<kBT, CM, SL, SLP>(&sdO[0][0], n, [&](int r, int c) {
+      return ld4f(dO + (row0 + (long)r * a.H) * DV + l0 + c);
+    });
+    stage_rows<kBT, CM, SL, SLP>(&sdU[0][0], n,
+                                 [&](int r, int c) { return ld4f(blk + L::odU + r * DV + l0 + c); });
+    stage_rows<kBT, CM, SL, SLP>(&sU[0][0], n,
+                                 [&](int r, int c) { return ld4f(blk + L::oU + r * DV + l0 + c); });
+    __syncthreads();
+    if (tid < DK)
+      for (int j = 0; j < SL; ++j) dd += sS0[tid][j] * sdS1[tid][j];
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+      const int ct = wv + 4 * m;
+      if (ct < CTN) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          auto s0t = [&](int kx, int j) { return sS0[16 * ct + j][kx]; };
+          aQ[m][rt] = mma_tile(aQ[m][rt], SL, [&](int i, int kx) { return sdO[16 * rt + i][kx]; },
+                               s0t);
+          aW[m][rt] = mma_tile(aW[m][rt], SL, [&](int i, int kx) { return sdU[16 * rt + i][kx]; },
+                               s0t);
+          aK[m][rt] = mma_tile(aK[m][rt], SL, [&](int i, int kx) { return sU[16 * rt + i][kx]; },
+                               [&](int kx, int j) { return sdS1[16 * ct + j][kx]; });
         }
       }
     }
-    const long i = (long)r * DK + cc;
-    float kd = 0.f, G = 0.f, qt = 0.f;
-    if (live) {
-      kd = blk[L::oKd + i];
-      G = blk[L::oG + i];
-      qt = blk[L::oQt + i];
-    }
-    const float col = wave_sum(kd * dkd);  // sum over rows of K^d * dK^d
-    if (live) {
-      const float Gn = blk[L::oG + (long)(n - 1) * DK + cc];
-      float dG = qt * dq - kd * dkd;
-      if (r == n - 1) dG += col + blk[L::oEn + cc] * dd;
-      blk[L::odq + i] = __expf(G) * dq;
-      blk[L::odk + i] = __expf(Gn - G) * dkd;
-      blk[L::odG + i] = dG;
-      blk[L::odW + i] = -dw;
-    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+      aP[rt] = mma_tile(aP[rt], SL, [&](int i, int kx) { return sdO[16 * rt + i][kx]; },
+                        [&](int kx, int j) { return sU[16 * wv + j][kx]; });
   }
-  // dP = (dO U^T) on j <= r: wave w takes rows w, w+4, ..., lane j the column
-  for (int r2 = wv; r2 < n; r2 += 4) {
-    const int j = lane;
-    float acc = 0.f;
-    if (j <= r2)
-      for (int l = 0; l < DV; ++l) acc += sdO[r2][l] * sU[j][l];
-    blk[L::odP + r2 * CM + j] = j <= r2 ? acc : 0.f;
+  if (tid < DK) sdD[tid] = dd;
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < CPW; ++m) {
+    const int ct = wv + 4 * m;
+    if (ct >= CTN) continue;
+    const int cc = 16 * ct + l16;
+    float col = 0.f;  // sum over the rows of K^d * dK^d in this column
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + r4 + e;
+        if (row < n) col += blk[L::oKd + (long)row * DK + cc] * aK[m][rt][e];
+      }
+    col += __shfl_xor(col, 16, kWave);
+    col += __shfl_xor(col, 32, kWave);
+    const float Gn = blk[L::oG + (long)(n - 1) * DK + cc];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + r4 + e;
+        if (row >= n) continue;
+        const long i = (long)row * DK + cc;
+        const float G = blk[L::oG + i], kd = blk[L::oKd + i], qt = blk[L::oQt + i];
+        const float dq = aQ[m][rt][e], dkd = aK[m][rt][e];
+        float dG = qt * dq - kd * dkd;
+        if (row == n - 1) dG += col + blk[L::oEn + cc] * sdD[cc];
+        blk[L::odq + i] = __expf(G) * dq;
+        blk[L::odk + i] = __expf(Gn - G) * dkd;
+        blk[L::odG + i] = dG;
+        blk[L::odW + i] = -aW[m][rt][e];
+      }
   }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)  // dP = (dO U^T) on j <= r
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, j = 16 * wv + l16;
+      if (row < n) blk[L::odP + row * CM + j] = j <= row ? aP[rt][e] : 0.f;
+    }
 }
 
 // ---- 5. per chunk-head: through W, U' and the inverse; dv and dbeta --------
+// LDS holds X and, in a first phase, dW, dU, K~, V^; in a second phase the
+// same space holds dX and T1 = dX X^T.
 template <int DK, int DV, typename IO>
 __global__ __launch_bounds__(kBT) void bw_grad_solve_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  __shared__ float sX[CM][CM + 1], sKt[CM][DK + 1], sV[CM][DV + 1];
-  __shared__ float sdX[CM][CM + 1], sT[CM][CM + 1];
+  constexpr int PX = CM + 4, PK = DK + 4, PV = DV + 4, RT = CM / 16;
+  constexpr int PH1 = 2 * CM * PK + 2 * CM * PV, PH2 = 2 * CM * PX;
+  __shared__ __attribute__((aligned(16))) float sX[CM][PX];
+  __shared__ __attribute__((aligned(16))) float sBuf[PH1 > PH2 ? PH1 : PH2];
   __shared__ float sbt[CM], sdb[CM];
+  float(*sdW)[PK] = reinterpret_cast<float(*)[PK]>(sBuf);
+  float(*sKt)[PK] = reinterpret_cast<float(*)[PK]>(sBuf + CM * PK);
+  float(*sdU)[PV] = reinterpret_cast<float(*)[PV]>(sBuf + 2 * CM * PK);
+  float(*sV)[PV] = reinterpret_cast<float(*)[PV]>(sBuf + 2 * CM * PK + CM * PV);
+  float(*sdX)[PX] = reinterpret_cast<float(*)[PX]>(sBuf);
+  float(*sT)[PX] = reinterpret_cast<float(*)[PX]>(sBuf + CM * PX);
   const Item it = item_of(a, blockIdx.x);
-  const int n = it.n;
+  const int n = it.n, n4 = (n + 3) & ~3;
   float* blk = a.scratch + (long)blockIdx.x * L::n;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l16 = lane % 16, r4 = 4 * (lane / 16);
   const IO* v = static_cast<const IO*>(a.v);
   IO* dv = static_cast<IO*>(a.dv);
-  for (int i = tid; i < n * CM; i += kBT) sX[i / CM][i % CM] = blk[L::oX + i];
-  for (int i = tid; i < n * DK; i += kBT) sKt[i / DK][i % DK] = blk[L::oKt + i];
-  for (int i = tid; i < n * DV; i += kBT) {
-    const int r = i / DV, l = i % DV;
-    sV[r][l] = to_f32(v[tok(a, it.b, it.t0 + r, it.h) * DV + l]);
-  }
-  if (tid < n) sbt[tid] = a.beta[tok(a, it.b, it.t0 + tid, it.h)];
-  __syncthreads();
-  // Y = X^T dW and Z = X^T dU, row r per wave, channels across the lanes
-  for (int r = wv; r < n; r += 4) {
-    const float br = sbt[r];
-    float db = 0.f;
-    for (int cc = lane; cc < DK; cc += kWave) {
-      float y = 0.f;
-      for (int i = r; i < n; ++i) y += sX[i][r] * blk[L::odW + (long)i * DK + cc];
-      db += sKt[r][cc] * y;
-      const long o = (long)r * DK + cc;
-      blk[L::odk + o] += __expf(blk[L::oG + o]) * br * y;
-      blk[L::odG + o] += sKt[r][cc] * br * y;
-    }
-    for (int l = lane; l < DV; l += kWave) {
-      float z = 0.f;
-      for (int i = r; i < n; ++i) z += sX[i][r] * blk[L::odU + (long)i * DV + l];
-      db += sV[r][l] * z;
-      dv[tok(a, it.b, it.t0 + r, it.h) * DV + l] = from_f32<IO>(br * z);
-    }
-    db = wave_sum(db);
-    if (lane == 0) sdb[r] = db;
-  }
-  // dX, strictly lower: dX[a][b] = beta_b (dW[a] . K~[b] + dU[a] . V^[b])
-  for (int r = wv; r < n; r += 4) {
-    const int j = lane;
-    float acc = 0.f;
-    if (j < r) {
-      for (int cc = 0; cc < DK; ++cc) acc += blk[L::odW + (long)r * DK + cc] * sKt[j][cc];
-      for (int l = 0; l < DV; ++l) acc += blk[L::odU + (long)r * DV + l] * sV[j][l];
-      acc *= sbt[j];
-    }
-    sdX[r][j] = acc;
+  const long row0 = tok(a, it.b, it.t0, it.h);
+  stage_rows<kBT, CM, CM, PX>(&sX[0][0], n, [&](int r, int c) { return ld4f(blk + L::oX + r * CM + c); });
+  stage_rows<kBT, CM, DK, PK>(&sdW[0][0], n, [&](int r, int c) { return ld4f(blk + L::odW + r * DK + c); });
+  stage_rows<kBT, CM, DK, PK>(&sKt[0][0], n, [&](int r, int c) { return ld4f(blk + L::oKt + r * DK + c); });
+  stage_rows<kBT, CM, DV, PV>(&sdU[0][0], n, [&](int r, int c) { return ld4f(blk + L::odU + r * DV + c); });
+  stage_rows<kBT, CM, DV, PV>(&sV[0][0], n, [&](int r, int c) {
+    return ld4f(v + (row0 + (long)r * a.H) * DV + c);
+  });
+  if (tid < CM) {
+    sbt[tid] = tid < n ? a.beta[tok(a, it.b, it.t0 + tid, it.h)] : 0.f;
+    sdb[tid] = 0.f;
   }
   __syncthreads();
-  // T1 = dX X^T on j < a (only those entries reach the strictly lower dM)
-  for (int r = wv; r < n; r += 4) {
-    const int j = lane;
-    float acc = 0.f;
-    if (j < r)
-      for (int m = 0; m <= j; ++m) acc += sdX[r][m] * sX[j][m];
-    sT[r][j] = acc;
+  // Y = X^T dW: dk^ += e^Gam beta Y, dGam += K~ beta Y, dbeta += K~ . Y
+  for (int t = wv; t < RT * (DK / 16); t += 4) {
+    const int rt = t % RT, ct = t / RT;
+    if (16 * rt >= n) continue;
+    const f32x4 y = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
+                             [&](int kx, int j) { return sdW[kx][16 * ct + j]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, cc = 16 * ct + l16;
+      float part = 0.f;
+      if (row < n) {
+        const long o = (long)row * DK + cc;
+        const float br = sbt[row], kt = sKt[row][cc];
+        blk[L::odk + o] += __expf(blk[L::oG + o]) * br * y[e];
+        blk[L::odG + o] += kt * br * y[e];
+        part = kt * y[e];
+      }
+      part = sum16(part);
+      if (l16 == 0 && row < n) atomicAdd(&sdb[row], part);
+    }
+  }
+  // Z = X^T dU: dv^ = beta Z, dbeta += V^ . Z
+  for (int t = wv; t < RT * (DV / 16); t += 4) {
+    const int rt = t % RT, ct = t / RT;
+    if (16 * rt >= n) continue;
+    const f32x4 z = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
+                             [&](int kx, int j) { return sdU[kx][16 * ct + j]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, l = 16 * ct + l16;
+      float part = 0.f;
+      if (row < n) {
+        dv[tok(a, it.b, it.t0 + row, it.h) * DV + l] = from_f32<IO>(sbt[row] * z[e]);
+        part = sV[row][l] * z[e];
+      }
+      part = sum16(part);
+      if (l16 == 0 && row < n) atomicAdd(&sdb[row], part);
+    }
+  }
+  // dX = (dW K~^T + dU V^^T) diag(beta), strictly lower; wave w: column tile w
+  f32x4 aX[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x4 acc = kZero4;
+    if (16 * rt < n) {
+      acc = mma_tile(acc, DK, [&](int i, int kx) { return sdW[16 * rt + i][kx]; },
+                     [&](int kx, int j) { return sKt[16 * wv + j][kx]; });
+      acc = mma_tile(acc, DV, [&](int i, int kx) { return sdU[16 * rt + i][kx]; },
+                     [&](int kx, int j) { return sV[16 * wv + j][kx]; });
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, col = 16 * wv + l16;
+      acc[e] = col < row ? sbt[col] * acc[e] : 0.f;
+    }
+    aX[rt] = acc;
+  }
+  __syncthreads();  // phase-1 operands are dead from here
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sdX[16 * rt + r4 + e][16 * wv + l16] = aX[rt][e];
+  __syncthreads();
+  // T1 = dX X^T
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x4 acc = kZero4;
+    if (16 * rt < n)
+      acc = mma_tile(acc, n4, [&](int i, int kx) { return sdX[16 * rt + i][kx]; },
+                     [&](int kx, int j) { return sX[16 * wv + j][kx]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[16 * rt + r4 + e][16 * wv + l16] = acc[e];
   }
   __syncthreads();
-  // dM = -X^T T1 (strictly lower); dA = beta dM; dbeta += A . dM
-  for (int r = wv; r < n; r += 4) {
-    const int j = lane;
-    float dm = 0.f, arj = 0.f;
-    if (j < r) {
-      for (int m = r; m < n; ++m) dm -= sX[m][r] * sT[m][j];
-      arj = blk[L::oA + r * CM + j];
+  // dM = -X^T T1 (strictly lower): dA = beta dM, dbeta += A . dM
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (16 * rt >= n) continue;
+    const f32x4 acc = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
+                               [&](int kx, int j) { return sT[kx][16 * wv + j]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, j = 16 * wv + l16;
+      float part = 0.f;
+      if (row < n) {
+        const float dm = j < row ? -acc[e] : 0.f;
+        blk[L::odA + row * CM + j] = sbt[row] * dm;
+        part = j < row ? blk[L::oA + row * CM + j] * dm : 0.f;
+      }
+      part = sum16(part);
+      if (l16 == 0 && row < n) atomicAdd(&sdb[row], part);
     }
-    blk[L::odA + r * CM + j] = j < r ? sbt[r] * dm : 0.f;
-    const float part = wave_sum(arj * dm);
-    if (lane == 0) sdb[r] += part;
   }
   __syncthreads();
   if (tid < n) a.dbeta[tok(a, it.b, it.t0 + tid, it.h)] = sdb[tid];
@@ -456,11 +725,11 @@ __global__ __launch_bounds__(kBT) void bw_grad_solve_kernel(BackwardArgs a) {
 // over j <= r and the column-side sums over r2 >= r of the pair terms, each
 // with its own exponential of a non-positive difference.
 template <int DK, int DV, typename IO>
-__global__ __launch_bounds__(kBT) void bw_grad_gram_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  constexpr int PK = DK + 1, RG = kBT / DK;
-  __shared__ float sK[CM][PK], sQ[CM][PK], sG[CM][PK];
-  __shared__ float sdA[CM][CM + 1], sdP[CM][CM + 1];
+  constexpr int PK = DK + 4, PC = CM + 4, RG = kBP / DK;
+  __shared__ __attribute__((aligned(16))) float sK[CM][PK], sQ[CM][PK], sG[CM][PK];
+  __shared__ __attribute__((aligned(16))) float sdA[CM][PC], sdP[CM][PC];
   const Item it = item_of(a, blockIdx.x);
   const int n = it.n;
   float* blk = a.scratch + (long)blockIdx.x * L::n;
@@ -469,27 +738,28 @@ __global__ __launch_bounds__(kBT) void bw_grad_gram_kernel(BackwardArgs a) {
   const IO* k = static_cast<const IO*>(a.k);
   IO* dq = static_cast<IO*>(a.dq);
   IO* dk = static_cast<IO*>(a.dk);
-  for (int i = tid; i < n * DK; i += kBT) {
-    const int r = i / DK, cc = i % DK;
-    const long off = tok(a, it.b, it.t0 + r, it.h) * DK + cc;
-    sK[r][cc] = to_f32(k[off]);
-    sQ[r][cc] = to_f32(q[off]);
-    sG[r][cc] = blk[L::oG + i];
-  }
-  for (int i = tid; i < n * CM; i += kBT) {
-    sdA[i / CM][i % CM] = blk[L::odA + i];
-    sdP[i / CM][i % CM] = blk[L::odP + i];
-  }
+  const long row0 = tok(a, it.b, it.t0, it.h);
+  stage_rows<kBP, CM, DK, PK>(&sK[0][0], n, [&](int r, int c) {
+    return ld4f(k + (row0 + (long)r * a.H) * DK + c);
+  });
+  stage_rows<kBP, CM, DK, PK>(&sQ[0][0], n, [&](int r, int c) {
+    return ld4f(q + (row0 + (long)r * a.H) * DK + c);
+  });
+  stage_rows<kBP, CM, DK, PK>(&sG[0][0], n, [&](int r, int c) { return ld4f(blk + L::oG + r * DK + c); });
+  stage_rows<kBP, CM, CM, PC>(&sdA[0][0], n, [&](int r, int c) { return ld4f(blk + L::odA + r * CM + c); });
+  stage_rows<kBP, CM, CM, PC>(&sdP[0][0], n, [&](int r, int c) { return ld4f(blk + L::odP + r * CM + c); });
   __syncthreads();
   const int cc = tid % DK;
   for (int r = tid / DK; r < n; r += RG) {
     const float Gr = sG[r][cc], kr = sK[r][cc], qr = sQ[r][cc];
     float SA = 0.f, SP = 0.f, TT = 0.f;
+#pragma unroll 4
     for (int j = 0; j <= r; ++j) {
       const float kje = sK[j][cc] * __expf(Gr - sG[j][cc]);
       SA += sdA[r][j] * kje;
       SP += sdP[r][j] * kje;
     }
+#pragma unroll 4
     for (int r2 = r; r2 < n; ++r2)
       TT += (sdA[r2][r] * sK[r2][cc] + sdP[r2][r] * sQ[r2][cc]) * __expf(sG[r2][cc] - Gr);
     const long i = (long)r * DK + cc;
@@ -515,7 +785,7 @@ hipError_t run_bw(const BackwardArgs& a, hipStream_t st) {
   const long items = (long)nc * a.B * a.H;
   const unsigned chains = (unsigned)(NB * a.B * a.H);
   if (items > 0) {
-    hipLaunchKernelGGL((bw_prep_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBT), 0, st, a);
+    hipLaunchKernelGGL((bw_prep_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBP), 0, st, a);
     hipLaunchKernelGGL((bw_state_chain_kernel<DK, DV>), dim3(chains), dim3(kBT), 0, st, a);
   }
   hipLaunchKernelGGL((bw_reverse_chain_kernel<DK, DV, IO>), dim3(chains), dim3(kBT), 0, st, a);
@@ -524,7 +794,7 @@ hipError_t run_bw(const BackwardArgs& a, hipStream_t st) {
                        st, a);
     hipLaunchKernelGGL((bw_grad_solve_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBT), 0,
                        st, a);
-    hipLaunchKernelGGL((bw_grad_gram_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBT), 0,
+    hipLaunchKernelGGL((bw_grad_gram_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBP), 0,
                        st, a);
   }
   return hipGetLastError();

@@ -253,7 +253,8 @@ size_t kda_backward_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chu
  *  dq, dk: [B][T][H][d_k] io dtype; dv: [B][T][H][d_v] io dtype;
  *  dg:    [B][T][H][d_k] fp32;  dbeta: [B][T][H] fp32;
  *  dS0:   [B][H][d_k][d_v] fp32, or NULL (not written).
- * S0, dST and dS0 must be 16-byte aligned. workspace: device buffer of
+ * q, k, v, g, dO, S0, dST and dS0 must be 16-byte aligned (the other
+ * pointers the alignment of their element type). workspace: device buffer of
  * kda_backward_workspace_bytes (16-byte aligned, contents on entry ignored).
  * flags must be 0. chunk: 16, 32 or 64; T need not be a multiple of it.
  * T = 0 writes dS0 = dST (zero if dST is NULL). All arithmetic is fp32.

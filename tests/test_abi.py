@@ -246,7 +246,10 @@ def test_backward_validation():
     for name in ["q", "k", "v", "g", "beta", "dO", "dq", "dk", "dv", "dg", "dbeta", "ws"]:
         assert call_backward(d, **{name: None}) == K.KDA_ERR_INVALID, name
         assert {"ws": "workspace"}.get(name, name) in kda.last_error()
-    assert call_backward(d, q=FAKE + 2) == K.KDA_ERR_INVALID       # fp32 needs 4 bytes
+    assert call_backward(d, q=FAKE + 4) == K.KDA_ERR_INVALID       # 16-byte activations
+    assert call_backward(d, g=FAKE + 4) == K.KDA_ERR_INVALID
+    assert call_backward(d, dO=FAKE + 8) == K.KDA_ERR_INVALID
+    assert call_backward(d, dq=FAKE + 2) == K.KDA_ERR_INVALID      # fp32 output: 4 bytes
     assert call_backward(d, ws=FAKE + 4) == K.KDA_ERR_INVALID      # 16-byte workspace
     assert call_backward(d, S0=FAKE + 4) == K.KDA_ERR_INVALID
     assert call_backward(d, dST=FAKE + 4) == K.KDA_ERR_INVALID
