@@ -108,6 +108,8 @@ __device__ __forceinline__ float sum16(float x) {
 
 constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 // Four consecutive elements as fp32 (one 16- or 8-byte load).
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 ld4f(const bf16* p) {
@@ -135,6 +137,7 @@ __device__ __forceinline__ void stage_rows(float* dst, int live, F&& ld4) {
   }
 }
 constexpr int kBP = 1024;  // threads of the per-chunk kernels with scalar loops
+constexpr int kBS = 512;   // threads of the solve-gradient kernel
 
 // ---- 1. per chunk-head: Gam, A, P, X, Q~, K~, K^d, W, U' --------------------
 template <int DK, int DV, typename IO>
@@ -174,11 +177,19 @@ __global__ __launch_bounds__(kBP) void bw_prep_kernel(BackwardArgs a) {
     const int j = lane;
     float accA = 0.f, accP = 0.f;
     if (j <= r) {
-#pragma unroll 4
-      for (int cc = 0; cc < DK; ++cc) {
-        const float kj = sK[j][cc] * __expf(sG[r][cc] - sG[j][cc]);
-        accA += sK[r][cc] * kj;
-        accP += sQ[r][cc] * kj;
+#pragma unroll 2
+      for (int cc = 0; cc < DK; cc += 4) {
+        const f32x4 kj = *reinterpret_cast<const f32x4*>(&sK[j][cc]);
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&sG[j][cc]);
+        const f32x4 kr = *reinterpret_cast<const f32x4*>(&sK[r][cc]);
+        const f32x4 qr = *reinterpret_cast<const f32x4*>(&sQ[r][cc]);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sG[r][cc]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ke = kj[e] * __expf(gr[e] - gj[e]);
+          accA += kr[e] * ke;
+          accP += qr[e] * ke;
+        }
       }
     }
     blk[L::oP + r * CM + j] = j <= r ? accP : 0.f;
@@ -481,7 +492,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
 // column tiles w, w+4, ... of dQ~, dW and dK^d (all row tiles) and column
 // tile w of dP.
 template <int DK, int DV, typename IO>
-__global__ __launch_bounds__(kBT) void bw_grad_dense_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kBT, 2) void bw_grad_dense_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
   constexpr int SL = DV < 32 ? DV : 32, SLP = SL + 4;
   constexpr int CTN = DK / 16, CPW = (CTN + 3) / 4, RT = CM / 16;
@@ -590,9 +601,10 @@ __global__ __launch_bounds__(kBT) void bw_grad_dense_kernel(BackwardArgs a) {
 // LDS holds X and, in a first phase, dW, dU, K~, V^; in a second phase the
 // same space holds dX and T1 = dX X^T.
 template <int DK, int DV, typename IO>
-__global__ __launch_bounds__(kBT) void bw_grad_solve_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  constexpr int PX = CM + 4, PK = DK + 4, PV = DV + 4, RT = CM / 16;
+  constexpr int PX = CM + 4, PK = DK + 4, PV = DV + 4, RT = CM / 16, NW = kBS / kWave;
+  constexpr int XPW = RT * RT / NW;  // C x C tiles per wave
   constexpr int PH1 = 2 * CM * PK + 2 * CM * PV, PH2 = 2 * CM * PX;
   __shared__ __attribute__((aligned(16))) float sX[CM][PX];
   __shared__ __attribute__((aligned(16))) float sBuf[PH1 > PH2 ? PH1 : PH2];
@@ -611,11 +623,11 @@ __global__ __launch_bounds__(kBT) void bw_grad_solve_kernel(BackwardArgs a) {
   const IO* v = static_cast<const IO*>(a.v);
   IO* dv = static_cast<IO*>(a.dv);
   const long row0 = tok(a, it.b, it.t0, it.h);
-  stage_rows<kBT, CM, CM, PX>(&sX[0][0], n, [&](int r, int c) { return ld4f(blk + L::oX + r * CM + c); });
-  stage_rows<kBT, CM, DK, PK>(&sdW[0][0], n, [&](int r, int c) { return ld4f(blk + L::odW + r * DK + c); });
-  stage_rows<kBT, CM, DK, PK>(&sKt[0][0], n, [&](int r, int c) { return ld4f(blk + L::oKt + r * DK + c); });
-  stage_rows<kBT, CM, DV, PV>(&sdU[0][0], n, [&](int r, int c) { return ld4f(blk + L::odU + r * DV + c); });
-  stage_rows<kBT, CM, DV, PV>(&sV[0][0], n, [&](int r, int c) {
+  stage_rows<kBS, CM, CM, PX>(&sX[0][0], n, [&](int r, int c) { return ld4f(blk + L::oX + r * CM + c); });
+  stage_rows<kBS, CM, DK, PK>(&sdW[0][0], n, [&](int r, int c) { return ld4f(blk + L::odW + r * DK + c); });
+  stage_rows<kBS, CM, DK, PK>(&sKt[0][0], n, [&](int r, int c) { return ld4f(blk + L::oKt + r * DK + c); });
+  stage_rows<kBS, CM, DV, PV>(&sdU[0][0], n, [&](int r, int c) { return ld4f(blk + L::odU + r * DV + c); });
+  stage_rows<kBS, CM, DV, PV>(&sV[0][0], n, [&](int r, int c) {
     return ld4f(v + (row0 + (long)r * a.H) * DV + c);
   });
   if (tid < CM) {
@@ -624,7 +636,7 @@ __global__ __launch_bounds__(kBT) void bw_grad_solve_kernel(BackwardArgs a) {
   }
   __syncthreads();
   // Y = X^T dW: dk^ += e^Gam beta Y, dGam += K~ beta Y, dbeta += K~ . Y
-  for (int t = wv; t < RT * (DK / 16); t += 4) {
+  for (int t = wv; t < RT * (DK / 16); t += NW) {
     const int rt = t % RT, ct = t / RT;
     if (16 * rt >= n) continue;
     const f32x4 y = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
@@ -645,7 +657,7 @@ __global__ __launch_bounds__(kBT) void bw_grad_solve_kernel(BackwardArgs a) {
     }
   }
   // Z = X^T dU: dv^ = beta Z, dbeta += V^ . Z
-  for (int t = wv; t < RT * (DV / 16); t += 4) {
+  for (int t = wv; t < RT * (DV / 16); t += NW) {
     const int rt = t % RT, ct = t / RT;
     if (16 * rt >= n) continue;
     const f32x4 z = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
@@ -662,50 +674,56 @@ __global__ __launch_bounds__(kBT) void bw_grad_solve_kernel(BackwardArgs a) {
       if (l16 == 0 && row < n) atomicAdd(&sdb[row], part);
     }
   }
-  // dX = (dW K~^T + dU V^^T) diag(beta), strictly lower; wave w: column tile w
-  f32x4 aX[RT];
+  // dX = (dW K~^T + dU V^^T) diag(beta), strictly lower; C x C tile
+  // u = w + NW m of wave w is (row tile u / RT, column tile u % RT)
+  f32x4 aX[XPW];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
     f32x4 acc = kZero4;
     if (16 * rt < n) {
       acc = mma_tile(acc, DK, [&](int i, int kx) { return sdW[16 * rt + i][kx]; },
-                     [&](int kx, int j) { return sKt[16 * wv + j][kx]; });
+                     [&](int kx, int j) { return sKt[16 * ct + j][kx]; });
       acc = mma_tile(acc, DV, [&](int i, int kx) { return sdU[16 * rt + i][kx]; },
-                     [&](int kx, int j) { return sV[16 * wv + j][kx]; });
+                     [&](int kx, int j) { return sV[16 * ct + j][kx]; });
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * rt + r4 + e, col = 16 * wv + l16;
+      const int row = 16 * rt + r4 + e, col = 16 * ct + l16;
       acc[e] = col < row ? sbt[col] * acc[e] : 0.f;
     }
-    aX[rt] = acc;
+    aX[m] = acc;
   }
   __syncthreads();  // phase-1 operands are dead from here
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sdX[16 * rt + r4 + e][16 * wv + l16] = aX[rt][e];
+    for (int e = 0; e < 4; ++e) sdX[16 * rt + r4 + e][16 * ct + l16] = aX[m][e];
+  }
   __syncthreads();
   // T1 = dX X^T
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
     f32x4 acc = kZero4;
     if (16 * rt < n)
       acc = mma_tile(acc, n4, [&](int i, int kx) { return sdX[16 * rt + i][kx]; },
-                     [&](int kx, int j) { return sX[16 * wv + j][kx]; });
+                     [&](int kx, int j) { return sX[16 * ct + j][kx]; });
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sT[16 * rt + r4 + e][16 * wv + l16] = acc[e];
+    for (int e = 0; e < 4; ++e) sT[16 * rt + r4 + e][16 * ct + l16] = acc[e];
   }
   __syncthreads();
   // dM = -X^T T1 (strictly lower): dA = beta dM, dbeta += A . dM
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
     if (16 * rt >= n) continue;
     const f32x4 acc = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
-                               [&](int kx, int j) { return sT[kx][16 * wv + j]; });
+                               [&](int kx, int j) { return sT[kx][16 * ct + j]; });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * rt + r4 + e, j = 16 * wv + l16;
+      const int row = 16 * rt + r4 + e, j = 16 * ct + l16;
       float part = 0.f;
       if (row < n) {
         const float dm = j < row ? -acc[e] : 0.f;
@@ -727,7 +745,7 @@ __global__ __launch_bounds__(kBT) void bw_grad_solve_kernel(BackwardArgs a) {
 template <int DK, int DV, typename IO>
 __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  constexpr int PK = DK + 4, PC = CM + 4, RG = kBP / DK;
+  constexpr int PK = DK + 4, PC = CM + 4, RG = kBP / (DK / 2);
   __shared__ __attribute__((aligned(16))) float sK[CM][PK], sQ[CM][PK], sG[CM][PK];
   __shared__ __attribute__((aligned(16))) float sdA[CM][PC], sdP[CM][PC];
   const Item it = item_of(a, blockIdx.x);
@@ -749,24 +767,42 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
   stage_rows<kBP, CM, CM, PC>(&sdA[0][0], n, [&](int r, int c) { return ld4f(blk + L::odA + r * CM + c); });
   stage_rows<kBP, CM, CM, PC>(&sdP[0][0], n, [&](int r, int c) { return ld4f(blk + L::odP + r * CM + c); });
   __syncthreads();
-  const int cc = tid % DK;
-  for (int r = tid / DK; r < n; r += RG) {
-    const float Gr = sG[r][cc], kr = sK[r][cc], qr = sQ[r][cc];
-    float SA = 0.f, SP = 0.f, TT = 0.f;
+  // two channels per thread (8-byte LDS reads); rows r0, r0 + RG, ...
+  const int c0 = 2 * (tid % (DK / 2));
+  for (int r = tid / (DK / 2); r < n; r += RG) {
+    const f32x2 Gr = *reinterpret_cast<const f32x2*>(&sG[r][c0]);
+    const f32x2 kr = *reinterpret_cast<const f32x2*>(&sK[r][c0]);
+    const f32x2 qr = *reinterpret_cast<const f32x2*>(&sQ[r][c0]);
+    f32x2 SA = {0.f, 0.f}, SP = {0.f, 0.f}, TT = {0.f, 0.f};
 #pragma unroll 4
     for (int j = 0; j <= r; ++j) {
-      const float kje = sK[j][cc] * __expf(Gr - sG[j][cc]);
-      SA += sdA[r][j] * kje;
-      SP += sdP[r][j] * kje;
+      const f32x2 kj = *reinterpret_cast<const f32x2*>(&sK[j][c0]);
+      const f32x2 gj = *reinterpret_cast<const f32x2*>(&sG[j][c0]);
+      const float da = sdA[r][j], dp = sdP[r][j];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float ke = kj[e] * __expf(Gr[e] - gj[e]);
+        SA[e] += da * ke;
+        SP[e] += dp * ke;
+      }
     }
 #pragma unroll 4
-    for (int r2 = r; r2 < n; ++r2)
-      TT += (sdA[r2][r] * sK[r2][cc] + sdP[r2][r] * sQ[r2][cc]) * __expf(sG[r2][cc] - Gr);
-    const long i = (long)r * DK + cc;
-    const long o = tok(a, it.b, it.t0 + r, it.h) * DK + cc;
-    dq[o] = from_f32<IO>(blk[L::odq + i] + SP);
-    dk[o] = from_f32<IO>(blk[L::odk + i] + SA + TT);
-    blk[L::odG + i] += kr * SA + qr * SP - kr * TT;
+    for (int r2 = r; r2 < n; ++r2) {
+      const f32x2 k2 = *reinterpret_cast<const f32x2*>(&sK[r2][c0]);
+      const f32x2 q2 = *reinterpret_cast<const f32x2*>(&sQ[r2][c0]);
+      const f32x2 g2 = *reinterpret_cast<const f32x2*>(&sG[r2][c0]);
+      const float da = sdA[r2][r], dp = sdP[r2][r];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) TT[e] += (da * k2[e] + dp * q2[e]) * __expf(g2[e] - Gr[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const long i = (long)r * DK + c0 + e;
+      const long o = tok(a, it.b, it.t0 + r, it.h) * DK + c0 + e;
+      dq[o] = from_f32<IO>(blk[L::odq + i] + SP[e]);
+      dk[o] = from_f32<IO>(blk[L::odk + i] + SA[e] + TT[e]);
+      blk[L::odG + i] += kr[e] * SA[e] + qr[e] * SP[e] - kr[e] * TT[e];
+    }
   }
   __syncthreads();
   if (tid < DK) {  // dg = reverse in-chunk prefix sum of dGam
@@ -792,7 +828,7 @@ hipError_t run_bw(const BackwardArgs& a, hipStream_t st) {
   if (items > 0) {
     hipLaunchKernelGGL((bw_grad_dense_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBT), 0,
                        st, a);
-    hipLaunchKernelGGL((bw_grad_solve_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBT), 0,
+    hipLaunchKernelGGL((bw_grad_solve_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBS), 0,
                        st, a);
     hipLaunchKernelGGL((bw_grad_gram_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBP), 0,
                        st, a);
