@@ -117,24 +117,48 @@ __device__ __forceinline__ f32x4 ld4f(const bf16* p) {
   return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
-// Stages ROWS x COLS values into LDS (row stride LD floats, 16-byte aligned
-// rows): ld4(r, c) gives row r, columns c..c+3 for r < live; rows at or past
-// `live` are zeros. Every load of a thread is issued before its stores.
+// A thread's 16-byte pieces of a ROWS x COLS block, loaded into registers by
+// get_rows and written to LDS by put_rows: between the two calls the loads
+// stay in flight, so a block for a later step can be fetched while the
+// current one is in use.
+template <int NT, int ROWS, int COLS>
+struct Pieces {
+  static_assert(COLS % 4 == 0, "16-byte pieces");
+  static constexpr int Q = COLS / 4, TOT = ROWS * Q, PER = (TOT + NT - 1) / NT;
+  f32x4 v[PER];
+};
+
+// ld4(r, c) gives row r, columns c..c+3 for r < live; rows at or past `live`
+// are zeros.
+template <int NT, int ROWS, int COLS, class F>
+__device__ __forceinline__ void get_rows(Pieces<NT, ROWS, COLS>& b, int live, F&& ld4) {
+  using P = Pieces<NT, ROWS, COLS>;
+#pragma unroll
+  for (int p = 0; p < P::PER; ++p) {
+    const int i = (int)threadIdx.x + p * NT, r = i / P::Q, c = 4 * (i % P::Q);
+    b.v[p] = (i < P::TOT && r < live) ? ld4(r, c) : kZero4;
+  }
+}
+
+// LDS destination rows of LD floats (LD a multiple of 4, 16-byte aligned rows).
+template <int LD, int NT, int ROWS, int COLS>
+__device__ __forceinline__ void put_rows(const Pieces<NT, ROWS, COLS>& b, float* dst) {
+  using P = Pieces<NT, ROWS, COLS>;
+  static_assert(LD % 4 == 0, "16-byte rows");
+#pragma unroll
+  for (int p = 0; p < P::PER; ++p) {
+    const int i = (int)threadIdx.x + p * NT, r = i / P::Q, c = 4 * (i % P::Q);
+    if (i < P::TOT) *reinterpret_cast<f32x4*>(dst + r * LD + c) = b.v[p];
+  }
+}
+
+// Stages ROWS x COLS values into LDS (row stride LD floats): get_rows then
+// put_rows, every load of a thread issued before its stores.
 template <int NT, int ROWS, int COLS, int LD, class F>
 __device__ __forceinline__ void stage_rows(float* dst, int live, F&& ld4) {
-  static_assert(COLS % 4 == 0 && LD % 4 == 0, "16-byte pieces");
-  constexpr int Q = COLS / 4, TOT = ROWS * Q, PER = (TOT + NT - 1) / NT;
-  f32x4 buf[PER];
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int i = (int)threadIdx.x + p * NT, r = i / Q, c = 4 * (i % Q);
-    buf[p] = (i < TOT && r < live) ? ld4(r, c) : kZero4;
-  }
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int i = (int)threadIdx.x + p * NT, r = i / Q, c = 4 * (i % Q);
-    if (i < TOT) *reinterpret_cast<f32x4*>(dst + r * LD + c) = buf[p];
-  }
+  Pieces<NT, ROWS, COLS> b;
+  get_rows(b, live, ld4);
+  put_rows<LD>(b, dst);
 }
 constexpr int kBP = 1024;  // threads of the per-chunk kernels with scalar loops
 constexpr int kBS = 512;   // threads of the solve-gradient kernel
@@ -171,30 +195,43 @@ __global__ __launch_bounds__(kBP) void bw_prep_kernel(BackwardArgs a) {
     }
   }
   __syncthreads();
-  // A (strictly lower) and P (lower): wave w takes rows w, w+NW, ..., lane j
-  // the column; every exponent Gam_r - Gam_j (j <= r) is <= 0.
-  for (int r = wv; r < n; r += NW) {
-    const int j = lane;
+  // A (strictly lower) and P (lower), every exponent Gam_r - Gam_j (j <= r)
+  // <= 0. Wave w takes the row pairs (r, CM-1-r), r = w, w+NW, ...: lanes
+  // l < r hold row r, column l; the other lanes row CM-1-r, column l - r (its
+  // diagonal included), so all 64 lanes work. The diagonal of row r and the
+  // zeros right of every diagonal come from the pass after.
+  for (int r = wv; r < CM / 2 && r < n; r += NW) {
+    const bool first = lane < r;
+    const int row = first ? r : CM - 1 - r, j = first ? lane : lane - r;
+    if (row >= n) continue;
     float accA = 0.f, accP = 0.f;
-    if (j <= r) {
 #pragma unroll 2
-      for (int cc = 0; cc < DK; cc += 4) {
-        const f32x4 kj = *reinterpret_cast<const f32x4*>(&sK[j][cc]);
-        const f32x4 gj = *reinterpret_cast<const f32x4*>(&sG[j][cc]);
-        const f32x4 kr = *reinterpret_cast<const f32x4*>(&sK[r][cc]);
-        const f32x4 qr = *reinterpret_cast<const f32x4*>(&sQ[r][cc]);
-        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sG[r][cc]);
+    for (int cc = 0; cc < DK; cc += 4) {
+      const f32x4 kj = *reinterpret_cast<const f32x4*>(&sK[j][cc]);
+      const f32x4 gj = *reinterpret_cast<const f32x4*>(&sG[j][cc]);
+      const f32x4 kr = *reinterpret_cast<const f32x4*>(&sK[row][cc]);
+      const f32x4 qr = *reinterpret_cast<const f32x4*>(&sQ[row][cc]);
+      const f32x4 gr = *reinterpret_cast<const f32x4*>(&sG[row][cc]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ke = kj[e] * __expf(gr[e] - gj[e]);
-          accA += kr[e] * ke;
-          accP += qr[e] * ke;
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float ke = kj[e] * __expf(gr[e] - gj[e]);
+        accA += kr[e] * ke;
+        accP += qr[e] * ke;
       }
     }
-    blk[L::oP + r * CM + j] = j <= r ? accP : 0.f;
-    blk[L::oA + r * CM + j] = j < r ? accA : 0.f;
-    sM[r][j] = j < r ? sb[r] * accA : 0.f;
+    blk[L::oP + row * CM + j] = accP;
+    blk[L::oA + row * CM + j] = j < row ? accA : 0.f;
+    sM[row][j] = j < row ? sb[row] * accA : 0.f;
+  }
+  for (int i = tid; i < n * CM; i += kBP) {
+    const int row = i / CM, j = i % CM;
+    if (j < row || (j == row && row >= CM / 2)) continue;
+    float p = 0.f;
+    if (j == row)
+      for (int cc = 0; cc < DK; ++cc) p += sQ[row][cc] * sK[row][cc];
+    blk[L::oP + i] = p;
+    blk[L::oA + i] = 0.f;
+    sM[row][j] = 0.f;
   }
   __syncthreads();
   // X = (I + diag(beta) A)^-1, unit lower triangular, by forward
@@ -275,6 +312,21 @@ struct ChainTiles {
   static constexpr int NUT = (CM / 16) * NCT, UPW = (NUT + 3) / 4;
 };
 
+// Workgroup L -> (column block cbk, sequence-head bh). Workgroups are dealt
+// to the 8 XCDs in turn; when the sequence-head count allows, the NB column
+// blocks of one sequence-head go to the same XCD, so the operands they share
+// (W, K^d, Q~, P) are fetched into that XCD's L2 once.
+__device__ __forceinline__ void chain_map(int L, int NB, int BH, int& cbk, int& bh) {
+  if (BH % 8 == 0) {
+    const int xcd = L % 8, s = L / 8;
+    cbk = s % NB;
+    bh = (s / NB) * 8 + xcd;
+  } else {
+    cbk = L % NB;
+    bh = L / NB;
+  }
+}
+
 // ---- 2. forward state chain: entering state of every chunk, U ---------------
 // One workgroup per (32-column block, head, sequence). Per chunk: keep S,
 // U = U' - W S (over U' in the scratch), S = Diag(e^{Gam_n}) S + K^d^T U.
@@ -287,8 +339,10 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
   __shared__ float sU[CM][CT::SPB];
   __shared__ __attribute__((aligned(16))) float sO[CM][CT::SPO];
   __shared__ __attribute__((aligned(16))) float sEn[DK];
-  const int cbk = blockIdx.x % CT::NB, bh = blockIdx.x / CT::NB, cb0 = cbk * CT::DVB;
   const int BH = a.B * a.H, nc = (a.T + a.chunk - 1) / a.chunk;
+  int cbk, bh;
+  chain_map(blockIdx.x, CT::NB, BH, cbk, bh);
+  const int cb0 = cbk * CT::DVB;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int l16 = lane % 16, r4 = 4 * (lane / 16);
   f32x4 accS[SPW];
@@ -301,12 +355,21 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
                        ? a.S0[((long)bh * DK + 16 * rt + r4 + e) * DV + cb0 + 16 * ct + l16]
                        : 0.f;
   }
+  // operands of a chunk: W, then K^d (through one register set), e^{Gam_n}
+  auto blk_of = [&](int c) { return a.scratch + ((long)c * BH + bh) * L::n; };
+  auto n_of = [&](int c) { return min(a.chunk, a.T - c * a.chunk); };
+  Pieces<kBT, CM, DK> pk;
+  Pieces<kBT, 1, DK> pe;
+  {
+    const float* b0 = blk_of(0);
+    get_rows(pk, n_of(0), [&](int r, int cx) { return ld4f(b0 + L::oW + r * DK + cx); });
+    get_rows(pe, 1, [&](int, int cx) { return ld4f(b0 + L::oEn + cx); });
+  }
   for (int c = 0; c < nc; ++c) {
-    const int n = min(a.chunk, a.T - c * a.chunk), n4 = (n + 3) & ~3;
-    const long item = (long)c * BH + bh;
-    float* blk = a.scratch + item * L::n;
-    float* Sk = a.S0s + item * DK * DV;
-    __syncthreads();  // the previous chunk is done with sS, sU, sO
+    const int n = n_of(c), n4 = (n + 3) & ~3;
+    float* blk = blk_of(c);
+    float* Sk = a.S0s + ((long)c * BH + bh) * DK * DV;
+    __syncthreads();  // the previous chunk is done with sS, sU, sO, sEn
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
       const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
@@ -319,9 +382,19 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
         }
       }
     }
-    stage_rows<kBT, CM, DK, CT::SPO>(&sO[0][0], n,
-                                     [&](int r, int cx) { return ld4f(blk + L::oW + r * DK + cx); });
-    stage_rows<kBT, 1, DK, DK>(sEn, 1, [&](int, int cx) { return ld4f(blk + L::oEn + cx); });
+    put_rows<CT::SPO>(pk, &sO[0][0]);  // W
+    put_rows<DK>(pe, sEn);
+    get_rows(pk, n, [&](int r, int cx) { return ld4f(blk + L::oKd + r * DK + cx); });
+    float up[UPW][4];  // U' of this thread's elements, loaded before the products
+#pragma unroll
+    for (int m = 0; m < UPW; ++m) {
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + r4 + e, col = 16 * ct + l16;
+        up[m][e] = (t < NUT && row < n) ? blk[L::oU + (long)row * DV + cb0 + col] : 0.f;
+      }
+    }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < UPW; ++m) {  // U = U' - W S
@@ -332,19 +405,19 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = 16 * rt + r4 + e, col = 16 * ct + l16;
-          float u = 0.f;
-          if (row < n) {
-            float* pu = blk + L::oU + (long)row * DV + cb0 + col;
-            u = *pu - ws[e];
-            *pu = u;
-          }
+          const float u = row < n ? up[m][e] - ws[e] : 0.f;
+          if (row < n) blk[L::oU + (long)row * DV + cb0 + col] = u;
           sU[row][col] = u;
         }
       }
     }
     __syncthreads();
-    stage_rows<kBT, CM, DK, CT::SPO>(&sO[0][0], n,
-                                     [&](int r, int cx) { return ld4f(blk + L::oKd + r * DK + cx); });
+    put_rows<CT::SPO>(pk, &sO[0][0]);  // K^d
+    if (c + 1 < nc) {
+      const float* bn = blk_of(c + 1);
+      get_rows(pk, n_of(c + 1), [&](int r, int cx) { return ld4f(bn + L::oW + r * DK + cx); });
+      get_rows(pe, 1, [&](int, int cx) { return ld4f(bn + L::oEn + cx); });
+    }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {  // S = Diag(e^{Gam_n}) S + K^d^T U
@@ -373,9 +446,10 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
   __shared__ float sdU[CM][CT::SPB];
   __shared__ __attribute__((aligned(16))) float sO[CM][CT::SPO];
   __shared__ __attribute__((aligned(16))) float sEn[DK];
-  const int cbk = blockIdx.x % CT::NB, bh = blockIdx.x / CT::NB, cb0 = cbk * DVB;
-  const int b = bh / a.H, h = bh % a.H;
   const int BH = a.B * a.H, nc = (a.T + a.chunk - 1) / a.chunk;
+  int cbk, bh;
+  chain_map(blockIdx.x, CT::NB, BH, cbk, bh);
+  const int cb0 = cbk * DVB, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int l16 = lane % 16, r4 = 4 * (lane / 16);
   const IO* dO = static_cast<const IO*>(a.dO);
@@ -389,19 +463,33 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
                        ? a.dST[((long)bh * DK + 16 * rt + r4 + e) * DV + cb0 + 16 * ct + l16]
                        : 0.f;
   }
-  // rows at or past the chunk's last token are zeroed (P is zero right of
-  // its diagonal, so its columns past the last token are zero as stored)
-  int cur_n = 0;
-  auto stage = [&](const float* src, auto cols) {
-    constexpr int COLS = decltype(cols)::value;
-    stage_rows<kBT, CM, COLS, CT::SPO>(&sO[0][0], cur_n,
-                                       [&](int r, int cx) { return ld4f(src + r * COLS + cx); });
+  // Operands of a chunk, through register sets loaded one stage ahead: P,
+  // dO and e^{Gam_n} (prefetched during the previous chunk's last stage),
+  // then K^d, Q~ and W in turn through one set. Rows at or past the chunk's
+  // last token are zeros (P is zero right of its diagonal, so its columns
+  // past the last token are zero as stored).
+  auto blk_of = [&](int c) { return a.scratch + ((long)c * BH + bh) * L::n; };
+  auto n_of = [&](int c) { return min(a.chunk, a.T - c * a.chunk); };
+  Pieces<kBT, CM, CM> pp;
+  Pieces<kBT, CM, DVB> pd;
+  Pieces<kBT, 1, DK> pe;
+  Pieces<kBT, CM, DK> pk;
+  auto get_first = [&](int c) {  // P, dO, e^{Gam_n} of chunk c
+    const float* bc = blk_of(c);
+    const int nn = n_of(c);
+    const long drow0 = tok(a, b, c * a.chunk, h);
+    get_rows(pp, nn, [&](int r, int cx) { return ld4f(bc + L::oP + r * CM + cx); });
+    get_rows(pd, nn, [&](int r, int cx) { return ld4f(dO + (drow0 + (long)r * a.H) * DV + cb0 + cx); });
+    get_rows(pe, 1, [&](int, int cx) { return ld4f(bc + L::oEn + cx); });
   };
+  if (nc > 0) get_first(nc - 1);
   for (int c = nc - 1; c >= 0; --c) {
-    const int t0 = c * a.chunk, n = min(a.chunk, a.T - t0), n4 = (n + 3) & ~3;
-    const long item = (long)c * BH + bh;
-    float* blk = a.scratch + item * L::n;
-    float* dSk = a.dS1s + item * DK * DV;
+    const int n = n_of(c), n4 = (n + 3) & ~3;
+    float* blk = blk_of(c);
+    float* dSk = a.dS1s + ((long)c * BH + bh) * DK * DV;
+    auto get_k = [&](long off) {
+      get_rows(pk, n, [&](int r, int cx) { return ld4f(blk + off + r * DK + cx); });
+    };
     __syncthreads();  // the previous chunk is done with every buffer
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
@@ -415,13 +503,10 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
         }
       }
     }
-    cur_n = n;
-    const long drow0 = tok(a, b, t0, h);
-    stage_rows<kBT, CM, DVB, CT::SPB>(&sdO[0][0], n, [&](int r, int cx) {
-      return ld4f(dO + (drow0 + (long)r * a.H) * DV + cb0 + cx);
-    });
-    stage_rows<kBT, 1, DK, DK>(sEn, 1, [&](int, int cx) { return ld4f(blk + L::oEn + cx); });
-    stage(blk + L::oP, std::integral_constant<int, CM>());
+    put_rows<CT::SPO>(pp, &sO[0][0]);
+    put_rows<CT::SPB>(pd, &sdO[0][0]);
+    put_rows<DK>(pe, sEn);
+    get_k(L::oKd);
     __syncthreads();
     f32x4 accU[UPW];
 #pragma unroll
@@ -433,7 +518,8 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
                            [&](int kx, int j) { return sdO[kx][16 * ct + j]; });
     }
     __syncthreads();
-    stage(blk + L::oKd, std::integral_constant<int, DK>());
+    put_rows<CT::SPO>(pk, &sO[0][0]);  // K^d
+    get_k(L::oQt);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < UPW; ++m) {  // + K^d dS
@@ -451,7 +537,8 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
       }
     }
     __syncthreads();
-    stage(blk + L::oQt, std::integral_constant<int, DK>());
+    put_rows<CT::SPO>(pk, &sO[0][0]);  // Q~
+    get_k(L::oW);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {  // dS = Diag(e^{Gam_n}) dS + Q~^T dO
@@ -464,7 +551,8 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
       }
     }
     __syncthreads();
-    stage(blk + L::oW, std::integral_constant<int, DK>());
+    put_rows<CT::SPO>(pk, &sO[0][0]);  // W
+    if (c > 0) get_first(c - 1);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {  // - W^T dU
