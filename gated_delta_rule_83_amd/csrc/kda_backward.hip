@@ -696,7 +696,10 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
   constexpr int PH1 = 2 * CM * PK + 2 * CM * PV, PH2 = 2 * CM * PX;
   __shared__ __attribute__((aligned(16))) float sX[CM][PX];
   __shared__ __attribute__((aligned(16))) float sBuf[PH1 > PH2 ? PH1 : PH2];
-  __shared__ float sbt[CM], sdb[CM];
+  // dbeta partials, one slot per (product, column tile), summed in a fixed
+  // order at the end (deterministic, unlike float atomics)
+  constexpr int SY = 0, SZ = DK / 16, SM = SZ + DV / 16, NSLOT = SM + RT;
+  __shared__ float sbt[CM], sdb[NSLOT][CM];
   float(*sdW)[PK] = reinterpret_cast<float(*)[PK]>(sBuf);
   float(*sKt)[PK] = reinterpret_cast<float(*)[PK]>(sBuf + CM * PK);
   float(*sdU)[PV] = reinterpret_cast<float(*)[PV]>(sBuf + 2 * CM * PK);
@@ -718,10 +721,8 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
   stage_rows<kBS, CM, DV, PV>(&sV[0][0], n, [&](int r, int c) {
     return ld4f(v + (row0 + (long)r * a.H) * DV + c);
   });
-  if (tid < CM) {
-    sbt[tid] = tid < n ? a.beta[tok(a, it.b, it.t0 + tid, it.h)] : 0.f;
-    sdb[tid] = 0.f;
-  }
+  if (tid < CM) sbt[tid] = tid < n ? a.beta[tok(a, it.b, it.t0 + tid, it.h)] : 0.f;
+  for (int i = tid; i < NSLOT * CM; i += kBS) sdb[i / CM][i % CM] = 0.f;
   __syncthreads();
   // Y = X^T dW: dk^ += e^Gam beta Y, dGam += K~ beta Y, dbeta += K~ . Y
   for (int t = wv; t < RT * (DK / 16); t += NW) {
@@ -741,7 +742,7 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
         part = kt * y[e];
       }
       part = sum16(part);
-      if (l16 == 0 && row < n) atomicAdd(&sdb[row], part);
+      if (l16 == 0 && row < n) sdb[SY + ct][row] = part;
     }
   }
   // Z = X^T dU: dv^ = beta Z, dbeta += V^ . Z
@@ -759,7 +760,7 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
         part = sV[row][l] * z[e];
       }
       part = sum16(part);
-      if (l16 == 0 && row < n) atomicAdd(&sdb[row], part);
+      if (l16 == 0 && row < n) sdb[SZ + ct][row] = part;
     }
   }
   // dX = (dW K~^T + dU V^^T) diag(beta), strictly lower; C x C tile
@@ -819,11 +820,15 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
         part = j < row ? blk[L::oA + row * CM + j] * dm : 0.f;
       }
       part = sum16(part);
-      if (l16 == 0 && row < n) atomicAdd(&sdb[row], part);
+      if (l16 == 0 && row < n) sdb[SM + ct][row] = part;
     }
   }
   __syncthreads();
-  if (tid < n) a.dbeta[tok(a, it.b, it.t0 + tid, it.h)] = sdb[tid];
+  if (tid < n) {
+    float db = 0.f;
+    for (int sl = 0; sl < NSLOT; ++sl) db += sdb[sl][tid];
+    a.dbeta[tok(a, it.b, it.t0 + tid, it.h)] = db;
+  }
 }
 
 // ---- 6. per chunk-head: through the decayed Grams; dq, dk, dg --------------

@@ -132,3 +132,38 @@ def test_backward_full_size_prefill_4k():
     checked in full against the oracle (heads are independent)."""
     inp = workloads.make("prefill_4k", s0_random=True)
     check(inp, 64, "bf16", heads=[0, 95])
+
+
+def test_backward_ignores_workspace_contents_and_is_deterministic():
+    """A workspace filled with NaN gives the same gradients, bit for bit, as a
+    zeroed one (no stage reads scratch it has not written), and two calls in
+    a row agree bitwise; ragged last chunk, two sequences, bf16."""
+    dev = device()
+    inp = workloads.draw(2, 150, 3, 64, 128, io="bf16", seed=15, s0_random=True,
+                         ring_random=True)
+    B, T, H, dk, dv = inp.dims
+    qh, kh, vh = activations(inp)
+    dO, dST = workloads.draw_backward_grads(B, T, H, dk, dv, io="bf16", seed=15)
+    dims = kda.make_dims(B, H, dk, dv, torch.bfloat16)
+    ws = torch.empty(kda.kda_backward_workspace_bytes(dims, T, 64), dtype=torch.uint8,
+                     device=dev)
+    ins = [x.to(dev) for x in (qh, kh, vh, inp.g, inp.beta, inp.S0, dO, dST)]
+
+    def call(fill):
+        if fill == "nan":
+            ws.view(torch.float32).fill_(float("nan"))
+        else:
+            ws.zero_()
+        out = [torch.empty(B, T, H, dk, dtype=torch.bfloat16, device=dev),
+               torch.empty(B, T, H, dk, dtype=torch.bfloat16, device=dev),
+               torch.empty(B, T, H, dv, dtype=torch.bfloat16, device=dev),
+               torch.empty(B, T, H, dk, device=dev), torch.empty(B, T, H, device=dev),
+               torch.empty(B, H, dk, dv, device=dev)]
+        kda.kda_chunk_backward(dims, T, *ins, *out, chunk=64, workspace=ws)
+        torch.cuda.synchronize()
+        return out
+
+    a, b, c = call("zero"), call("nan"), call("nan")
+    for x, y, z in zip(a, b, c):
+        assert torch.isfinite(x.float()).all()
+        assert torch.equal(x, y) and torch.equal(y, z)
