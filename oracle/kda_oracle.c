@@ -405,3 +405,99 @@ int kdao_core_backward(int B, int T, int H, int dk, int dv,
   free(states); free(G); free(Sp); free(r); free(del); free(dd);
   return bad ? -1 : 0;
 }
+
+/* Gradient of steps 1-2 (the width-4 causal conv, SiLU, and the L2
+ * normalisation of q and k) for training: given the raw projections q, k
+ * [B][T][H][dk], v [B][T][H][dv], the conv weights [Ctot][4], the ring read
+ * as history (ring0 [B][3][Ctot], NULL for zeros) and the gradients dqh,
+ * dkh [B][T][H][dk], dvh [B][T][H][dv] of the activations q^, k^, v^,
+ * returns dq, dk, dv (raw projections), dconv_w [Ctot][4] and dring
+ * [B][3][Ctot] (the history). The ring the forward writes (the last three
+ * raw tokens) is not differentiated.
+ *
+ * Written from steps 1-2 by reverse-mode differentiation, per channel c with
+ * x_s the raw value at token s (s < 0 from the ring), y_t = sum_j w[c][j]
+ * x_{t-3+j}, z_t = SiLU(y_t) = y_t s(y_t), s the logistic sigmoid:
+ *   q and k (per token and head, over d_k):
+ *     u = |z|^2 + eps, q^ = z / sqrt(u),
+ *     dz = (dq^ - q^ (q^ . dq^)) / sqrt(u);
+ *   v: dz = dv^;
+ *   dy = dz (s(y) + y s(y) (1 - s(y)));
+ *   dx_{t-3+j} += w[c][j] dy_t,  dw[c][j] += dy_t x_{t-3+j}.
+ * Returns 0, or -1 on bad arguments or allocation failure. */
+int kdao_prologue_backward(int B, int T, int H, int dk, int dv,
+                           const double *q, const double *k, const double *v,
+                           const double *conv_w, const double *ring0,
+                           const double *dqh, const double *dkh, const double *dvh,
+                           double eps, double *dq, double *dk_out, double *dv_out,
+                           double *dconv_w, double *dring) {
+  if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  const long Ctot = (long)H * (2 * dk + dv);
+  const int nmax = dk > dv ? dk : dv;
+  memset(dconv_w, 0, sizeof(double) * Ctot * 4);
+  memset(dring, 0, sizeof(double) * (long)B * 3 * Ctot);
+  double *xe = malloc(sizeof(double) * (long)(T + 3) * nmax);  /* [i][s + 3] */
+  double *dxe = malloc(sizeof(double) * (long)(T + 3) * nmax);
+  double *y = malloc(sizeof(double) * ((long)T * nmax + 1));     /* [t][i] */
+  double *dz = malloc(sizeof(double) * ((long)T * nmax + 1));
+  int bad = !xe || !dxe || !y || !dz;
+  for (int b = 0; b < B && !bad; ++b)
+    for (int h = 0; h < H; ++h)
+      for (int p = 0; p < 3; ++p) {
+        const int n = p < 2 ? dk : dv;
+        const long st = (long)H * n;  /* token stride */
+        const long c0 = p == 0 ? (long)h * dk : p == 1 ? (long)H * dk + (long)h * dk
+                                                       : 2L * H * dk + (long)h * dv;
+        const long base = (long)b * T * st + (long)h * n;
+        const double *x = (p == 0 ? q : p == 1 ? k : v) + base;
+        const double *dxh = (p == 0 ? dqh : p == 1 ? dkh : dvh) + base;
+        double *dxo = (p == 0 ? dq : p == 1 ? dk_out : dv_out) + base;
+        for (int i = 0; i < n; ++i)
+          for (int s = -3; s < T; ++s) {
+            double val = 0.0;
+            if (s >= 0) val = x[(long)s * st + i];
+            else if (ring0) val = ring0[((long)b * 3 + (3 + s)) * Ctot + c0 + i];
+            xe[(long)i * (T + 3) + s + 3] = val;
+            dxe[(long)i * (T + 3) + s + 3] = 0.0;
+          }
+        for (int t = 0; t < T; ++t) {
+          double *yt = y + (long)t * n, *dzt = dz + (long)t * n;
+          for (int i = 0; i < n; ++i) {
+            const double *w = conv_w + 4 * (c0 + i);
+            const double *xi = xe + (long)i * (T + 3) + t;  /* xi[j] = x_{t-3+j} */
+            yt[i] = w[0] * xi[0] + w[1] * xi[1] + w[2] * xi[2] + w[3] * xi[3];
+          }
+          if (p < 2) {
+            double ss = 0.0;
+            for (int i = 0; i < n; ++i) {
+              const double zi = silu(yt[i]);
+              ss += zi * zi;
+            }
+            const double nrm = sqrt(ss + eps);
+            double dot = 0.0;
+            for (int i = 0; i < n; ++i) dot += silu(yt[i]) / nrm * dxh[(long)t * st + i];
+            for (int i = 0; i < n; ++i)
+              dzt[i] = (dxh[(long)t * st + i] - silu(yt[i]) / nrm * dot) / nrm;
+          } else {
+            for (int i = 0; i < n; ++i) dzt[i] = dxh[(long)t * st + i];
+          }
+          for (int i = 0; i < n; ++i) {
+            const double sg = 1.0 / (1.0 + exp(-yt[i]));
+            const double dy = dzt[i] * (sg + yt[i] * sg * (1.0 - sg));
+            const double *w = conv_w + 4 * (c0 + i);
+            double *dw = dconv_w + 4 * (c0 + i);
+            for (int j = 0; j < 4; ++j) {
+              dxe[(long)i * (T + 3) + t + j] += w[j] * dy;
+              dw[j] += dy * xe[(long)i * (T + 3) + t + j];
+            }
+          }
+        }
+        for (int i = 0; i < n; ++i) {
+          for (int t = 0; t < T; ++t) dxo[(long)t * st + i] = dxe[(long)i * (T + 3) + t + 3];
+          for (int s = 0; s < 3; ++s)
+            dring[((long)b * 3 + s) * Ctot + c0 + i] = dxe[(long)i * (T + 3) + s];
+        }
+      }
+  free(xe); free(dxe); free(y); free(dz);
+  return bad ? -1 : 0;
+}

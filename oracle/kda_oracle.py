@@ -90,6 +90,9 @@ class Oracle:
         lib.kdao_gates_from_raw.restype = ctypes.c_int
         lib.kdao_core_backward.argtypes = [ctypes.c_int] * 5 + [dp] * 14
         lib.kdao_core_backward.restype = ctypes.c_int
+        lib.kdao_prologue_backward.argtypes = ([ctypes.c_int] * 5 + [dp] * 8
+                                               + [ctypes.c_double] + [dp] * 5)
+        lib.kdao_prologue_backward.restype = ctypes.c_int
         lib.kdao_max_threads.argtypes = []
         lib.kdao_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -196,6 +199,28 @@ class Oracle:
                                          *[_ptr(x) for x in out])
         if rc != 0:
             raise RuntimeError("kdao_core_backward failed")
+        return tuple(out)
+
+    def prologue_backward(self, q, k, v, conv_w, ring0, dqh, dkh, dvh, eps=L2_EPS):
+        """Gradient of the prologue (conv, SiLU, L2 of q and k) for the linear
+        functional sum(dqh * q^) + sum(dkh * k^) + sum(dvh * v^): returns
+        dq, dk, dv (raw projections), dconv_w [Ctot, 4] and dring [B, 3, Ctot]
+        (the history read from the ring), float64."""
+        q, k, v, dqh, dkh, dvh = map(_f64, (q, k, v, dqh, dkh, dvh))
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        ctot = H * (2 * dk + dv)
+        w = _f64(conv_w)
+        ring = np.zeros((B, 3, ctot)) if ring0 is None else _f64(ring0)
+        assert k.shape == q.shape == dqh.shape == dkh.shape and v.shape == dvh.shape
+        assert w.shape == (ctot, 4) and ring.shape == (B, 3, ctot)
+        out = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros((ctot, 4)),
+               np.zeros((B, 3, ctot))]
+        rc = self.lib.kdao_prologue_backward(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(w),
+                                             _ptr(ring), _ptr(dqh), _ptr(dkh), _ptr(dvh),
+                                             float(eps), *[_ptr(x) for x in out])
+        if rc != 0:
+            raise RuntimeError("kdao_prologue_backward failed")
         return tuple(out)
 
     def chunked_core(self, *args, **kwargs):

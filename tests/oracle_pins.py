@@ -426,6 +426,38 @@ def pin_core_backward_finite_differences(orc):
         np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg=f"d{name}")
 
 
+# --------------------------------------------------------------------------
+# Gradient of the prologue (for training): the hand-derived reverse pass
+# against central finite differences of the forward prologue of the oracle,
+# for every raw input element, conv weight and ring (history) element, on a
+# linear functional of q^, k^ and v^.
+def pin_prologue_backward_finite_differences(orc):
+    q, k, v, g, beta, w, S0, ring = _rand_case(93, B=2, T=5, dk=3, dv=4)
+    rng = np.random.default_rng(94)
+    dqh, dkh, dvh = (rng.standard_normal(x.shape) for x in (q, k, v))
+    args = dict(q=q, k=k, v=v, w=w, ring=ring)
+
+    def loss(a):
+        qh, kh, vh = orc.prologue(a["q"], a["k"], a["v"], a["w"], a["ring"])[:3]
+        return float((qh * dqh).sum() + (kh * dkh).sum() + (vh * dvh).sum())
+
+    grads = orc.prologue_backward(q, k, v, w, ring, dqh, dkh, dvh)
+    h = 1e-6
+    for name, grad in zip(("q", "k", "v", "w", "ring"), grads):
+        x = args[name]
+        assert grad.shape == x.shape
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            saved = x[idx]
+            x[idx] = saved + h
+            lp = loss(args)
+            x[idx] = saved - h
+            lm = loss(args)
+            x[idx] = saved
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg=f"d{name}")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_zero_decay_is_delta_rule,
@@ -443,4 +475,5 @@ ALL_PINS = [
     pin_gated_rmsnorm_closed_forms,
     pin_gates_from_raw,
     pin_core_backward_finite_differences,
+    pin_prologue_backward_finite_differences,
 ]

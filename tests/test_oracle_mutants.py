@@ -69,6 +69,17 @@ MUTANTS = {
     "bwd_dbeta_without_read": [("db += dd[j] * (vt[j] - r[j]);", "db += dd[j] * vt[j];")],
     "bwd_readout_added_late": [("          G[(long)i * dv + j] += qt[i] * dot[j];\n", ""),
                                ("        dgt[i] = ag;\n", "        dgt[i] = ag;\n        (void)qt;\n")],
+    # the gradient of the prologue
+    "pbwd_no_norm_projection": [("dzt[i] = (dxh[(long)t * st + i] - silu(yt[i]) / nrm * dot) / nrm;",
+                                 "dzt[i] = dxh[(long)t * st + i] / nrm;")],
+    "pbwd_silu_slope_only_sigmoid": [("const double dy = dzt[i] * (sg + yt[i] * sg * (1.0 - sg));",
+                                      "const double dy = dzt[i] * sg;")],
+    "pbwd_conv_taps_reversed": [("dxe[(long)i * (T + 3) + t + j] += w[j] * dy;",
+                                 "dxe[(long)i * (T + 3) + t + j] += w[3 - j] * dy;")],
+    "pbwd_weight_grad_wrong_token": [("dw[j] += dy * xe[(long)i * (T + 3) + t + j];",
+                                      "dw[j] += dy * xe[(long)i * (T + 3) + t + 3];")],
+    "pbwd_ring_grad_dropped": [("dring[((long)b * 3 + s) * Ctot + c0 + i] = dxe[(long)i * (T + 3) + s];",
+                                "dring[((long)b * 3 + s) * Ctot + c0 + i] = 0.0;")],
 }
 
 
