@@ -429,4 +429,58 @@ kda_status kda_chunk_backward(const kda_dims* d, int32_t T, const void* q, const
   return KDA_OK;
 }
 
+size_t kda_prologue_backward_workspace_bytes(const kda_dims* d, int32_t T) {
+  if (check_dims(d) != KDA_OK || T < 0) return 0;
+  return (size_t)d->batch * kda::prologue_bwd_segments(T) * ctot_of(d) * 4 * sizeof(float);
+}
+
+kda_status kda_prologue_backward(const kda_dims* d, int32_t T, const void* q, const void* k,
+                                 const void* v, const float* conv_w, const void* ring,
+                                 const void* dq_hat, const void* dk_hat, const void* dv_hat,
+                                 void* dq, void* dk, void* dv, float* dconv_w, float* dring,
+                                 void* workspace, size_t workspace_bytes, uint32_t flags,
+                                 hipStream_t stream) {
+  g_err[0] = 0;
+  kda_status st = check_dims(d);
+  if (st != KDA_OK) return st;
+  if (flags != 0)
+    return fail(KDA_ERR_INVALID, "kda_prologue_backward takes no flags (got 0x%x)", flags);
+  if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);
+  if ((size_t)d->batch * d->heads * kda::prologue_bwd_segments(T) > 0x7fffffffu)
+    return fail(KDA_ERR_UNSUPPORTED, "T = %d: too many (sequence, head, segment) items", T);
+  const size_t esz = io_size(d->io);
+  KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
+  KDA_REQUIRE_PTR(dconv_w, "dconv_w", 16);
+  if (ring && !aligned(ring, esz)) return fail(KDA_ERR_INVALID, "ring is misaligned");
+  if (dring && !aligned(dring, 4)) return fail(KDA_ERR_INVALID, "dring is misaligned");
+  if (T > 0) {
+    KDA_REQUIRE_PTR(q, "q", esz);
+    KDA_REQUIRE_PTR(k, "k", esz);
+    KDA_REQUIRE_PTR(v, "v", esz);
+    KDA_REQUIRE_PTR(dq_hat, "dq_hat", esz);
+    KDA_REQUIRE_PTR(dk_hat, "dk_hat", esz);
+    KDA_REQUIRE_PTR(dv_hat, "dv_hat", esz);
+    KDA_REQUIRE_PTR(dq, "dq", esz);
+    KDA_REQUIRE_PTR(dk, "dk", esz);
+    KDA_REQUIRE_PTR(dv, "dv", esz);
+    KDA_REQUIRE_PTR(workspace, "workspace", 16);
+    const size_t need = kda_prologue_backward_workspace_bytes(d, T);
+    if (workspace_bytes < need)
+      return fail(KDA_ERR_INVALID, "workspace of %zu bytes is below the %zu bytes needed",
+                  workspace_bytes, need);
+  }
+  hipError_t e;
+  if (T == 0 && dring) {  // no tokens: the history's gradient is zero
+    e = kda::launch_fill_zero(dring, (size_t)d->batch * 3 * ctot_of(d) * sizeof(float), stream);
+    if (e != hipSuccess) return hip_fail(e, "fill launch");
+  }
+  kda::PrologueBwdArgs a{q,      k,      v,      conv_w, ring,     dq_hat,
+                         dk_hat, dv_hat, dq,     dk,     dv,       dconv_w,
+                         dring,  static_cast<float*>(workspace), d->batch, T,
+                         d->heads, d->d_k, d->d_v, kda::prologue_bwd_segments(T)};
+  e = kda::launch_prologue_backward(a, d->io, stream);
+  if (e != hipSuccess) return hip_fail(e, "prologue backward launch");
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -148,4 +148,24 @@ struct BackwardArgs {
 size_t backward_ws_bytes(int B, int T, int H, int dk, int dv, int chunk);
 hipError_t launch_backward(BackwardArgs a, kda_dtype io, void* ws, hipStream_t stream);
 
+struct PrologueBwdArgs {
+  const void* q;        // [B][T][H][dk] raw projections (io dtype)
+  const void* k;
+  const void* v;        // [B][T][H][dv]
+  const float* conv_w;  // [Ctot][4]
+  const void* ring;     // [B][3][Ctot] history before token 0 (io dtype), or NULL
+  const void* dqh;      // [B][T][H][dk] gradient of q^ (io dtype)
+  const void* dkh;
+  const void* dvh;      // [B][T][H][dv]
+  void* dq_raw;         // [B][T][H][dk] (io dtype)
+  void* dk_raw;
+  void* dv_raw;         // [B][T][H][dv]
+  float* dconv_w;       // [Ctot][4]
+  float* dring;         // [B][3][Ctot], or NULL
+  float* wpart;         // [B][nseg][Ctot][4] per-segment weight gradients
+  int B, T, H, dk, dv, nseg;
+};
+int prologue_bwd_segments(int T);
+hipError_t launch_prologue_backward(const PrologueBwdArgs& a, kda_dtype io, hipStream_t stream);
+
 }  // namespace kda

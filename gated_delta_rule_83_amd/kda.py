@@ -24,7 +24,8 @@ EXPORTED = [
     "kda_state_S", "kda_state_ring", "kda_state_get_dims", "kda_conv_prologue",
     "kda_decode_step", "kda_prefill_workspace_bytes", "kda_chunk_prefill",
     "kda_gated_rmsnorm", "kda_decode_step_gated", "kda_backward_workspace_bytes",
-    "kda_chunk_backward", "kda_last_error", "kda_version",
+    "kda_chunk_backward", "kda_prologue_backward_workspace_bytes", "kda_prologue_backward",
+    "kda_last_error", "kda_version",
 ]
 
 
@@ -74,6 +75,8 @@ def lib():
         "kda_backward_workspace_bytes": (sz, [dp, i32, i32]),
         "kda_chunk_backward": (ctypes.c_int, [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                               vp, vp, vp, vp, i32, vp, sz, u32, vp]),
+        "kda_prologue_backward_workspace_bytes": (sz, [dp, i32]),
+        "kda_prologue_backward": (ctypes.c_int, [dp, i32] + [vp] * 14 + [sz, u32, vp]),
         "kda_last_error": (ctypes.c_char_p, []),
         "kda_version": (ctypes.c_char_p, []),
     }
@@ -248,6 +251,29 @@ def kda_chunk_backward(dims, T, q, k, v, g, beta, S0, dO, dST, dq, dk, dv, dg, d
         _ptr(dST, "dST", f32), _ptr(dq, "dq", io), _ptr(dk, "dk", io), _ptr(dv, "dv", io),
         _ptr(dg, "dg", f32), _ptr(dbeta, "dbeta", f32), _ptr(dS0, "dS0", f32), int(chunk),
         _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes), int(flags), _stream(stream)))
+
+
+def kda_prologue_backward_workspace_bytes(dims, T) -> int:
+    return int(lib().kda_prologue_backward_workspace_bytes(ctypes.byref(dims), int(T)))
+
+
+def kda_prologue_backward(dims, T, q, k, v, conv_w, ring, dq_hat, dk_hat, dv_hat, dq, dk, dv,
+                          dconv_w, dring, workspace=None, flags=0, stream=None):
+    """Gradients of the prologue (include/kda.h). ring and dring may be None;
+    with workspace None one is taken from torch's allocator for this call."""
+    io = io_dtype(dims)
+    need = kda_prologue_backward_workspace_bytes(dims, T)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dconv_w.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    f32 = torch.float32
+    _check(lib().kda_prologue_backward(
+        ctypes.byref(dims), int(T), _ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io),
+        _ptr(conv_w, "conv_w", f32), _ptr(ring, "ring", io), _ptr(dq_hat, "dq_hat", io),
+        _ptr(dk_hat, "dk_hat", io), _ptr(dv_hat, "dv_hat", io), _ptr(dq, "dq", io),
+        _ptr(dk, "dk", io), _ptr(dv, "dv", io), _ptr(dconv_w, "dconv_w", f32),
+        _ptr(dring, "dring", f32), _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes),
+        int(flags), _stream(stream)))
 
 
 def kda_version() -> str:

@@ -275,6 +275,40 @@ kda_status kda_chunk_backward(const kda_dims* dims, int32_t T, const void* q,
                               float* dbeta, float* dS0, int32_t chunk, void* workspace,
                               size_t workspace_bytes, uint32_t flags, hipStream_t stream);
 
+/* Device workspace that kda_prologue_backward needs: the per-64-token-segment
+ * conv-weight gradients, B * ceil(T / 64) * Ctot * 16 bytes (0 for invalid
+ * arguments; 0 for T = 0). */
+size_t kda_prologue_backward_workspace_bytes(const kda_dims* dims, int32_t T);
+
+/* Gradient of the prologue (the width-4 causal conv, SiLU, and the L2
+ * normalisation of q and k, as kda_conv_prologue computes them) for
+ * training: from the gradients of q^, k^, v^ (e.g. those kda_chunk_backward
+ * returns) to those of the raw projections, the conv weights and the ring's
+ * history. The ring that the forward writes (the last three raw tokens) is
+ * not differentiated.
+ *  q, k:  [B][T][H][d_k] raw projections (io dtype); v: [B][T][H][d_v];
+ *  conv_w: [Ctot][4] fp32 (16-byte aligned);
+ *  ring:  [B][3][Ctot] io dtype, the history read before token 0, or NULL
+ *         for zeros;
+ *  dq_hat, dk_hat: [B][T][H][d_k] io dtype; dv_hat: [B][T][H][d_v];
+ *  dq, dk: [B][T][H][d_k] io dtype (written); dv: [B][T][H][d_v];
+ *  dconv_w: [Ctot][4] fp32 (written, 16-byte aligned);
+ *  dring: [B][3][Ctot] fp32 (written), or NULL.
+ * workspace: kda_prologue_backward_workspace_bytes (16-byte aligned). flags
+ * must be 0. All arithmetic is fp32; the weight gradient is summed in a
+ * fixed order (bitwise reproducible). T = 0 writes zero dconv_w and dring.
+ * Source: "KV缓存从11.25GB缩到0.21GB：…", section "KDA 递推公式先衰减再差分"
+ * (the short conv with SiLU before q/k/v, the L2 normalisation of q and k);
+ * the gradient is its reverse-mode derivative (no formula is printed).
+ * Errors: KDA_ERR_INVALID (NULL or misaligned pointer, T < 0, flags, small
+ * workspace), KDA_ERR_UNSUPPORTED (dims). */
+kda_status kda_prologue_backward(const kda_dims* dims, int32_t T, const void* q,
+                                 const void* k, const void* v, const float* conv_w,
+                                 const void* ring, const void* dq_hat, const void* dk_hat,
+                                 const void* dv_hat, void* dq, void* dk, void* dv,
+                                 float* dconv_w, float* dring, void* workspace,
+                                 size_t workspace_bytes, uint32_t flags, hipStream_t stream);
+
 /* Description of the last error on the calling thread ("" if none). */
 const char* kda_last_error(void);
 

@@ -261,3 +261,33 @@ def test_backward_validation():
     assert call_backward(d, T=0, ws_bytes=0, ws=None, q=None, dO=None) == K.KDA_OK
     bad = kda.make_dims(1, 1, 24, 32, kda.KDA_F32)
     assert call_backward(bad, ws_bytes=0) == K.KDA_ERR_UNSUPPORTED
+
+
+def test_prologue_backward_validation():
+    d = kda.make_dims(2, 3, 16, 32, kda.KDA_F32)
+    L = kda.lib()
+    ctot = 3 * (2 * 16 + 32)
+    assert kda.kda_prologue_backward_workspace_bytes(d, 64) == 2 * 1 * ctot * 16
+    assert kda.kda_prologue_backward_workspace_bytes(d, 65) == 2 * 2 * ctot * 16
+    assert kda.kda_prologue_backward_workspace_bytes(d, -1) == 0
+    need = kda.kda_prologue_backward_workspace_bytes(d, 8)
+    names = ["q", "k", "v", "w", "ring", "dqh", "dkh", "dvh", "dq", "dk", "dv", "dw", "dring",
+             "ws"]
+
+    def call(T=8, ws_bytes=need, flags=0, **over):
+        p = {n: over.get(n, FAKE) for n in names}
+        return L.kda_prologue_backward(ctypes.byref(d), T, *[_vp(p[n]) for n in names],
+                                       ws_bytes, flags, None)
+
+    assert call(T=-1) == K.KDA_ERR_INVALID
+    assert call(flags=1) == K.KDA_ERR_INVALID
+    for name in ["q", "k", "v", "w", "dqh", "dkh", "dvh", "dq", "dk", "dv", "dw", "ws"]:
+        assert call(**{name: None}) == K.KDA_ERR_INVALID, name
+    assert call(w=FAKE + 4) == K.KDA_ERR_INVALID
+    assert call(dw=FAKE + 4) == K.KDA_ERR_INVALID
+    assert call(ws=FAKE + 4) == K.KDA_ERR_INVALID
+    assert call(ws_bytes=need - 1) == K.KDA_ERR_INVALID
+    assert "workspace" in kda.last_error()
+    bad = kda.make_dims(1, 1, 24, 32, kda.KDA_F32)
+    assert L.kda_prologue_backward(ctypes.byref(bad), 8, *[_vp(FAKE)] * 14, need, 0, None) == \
+        K.KDA_ERR_UNSUPPORTED

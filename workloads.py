@@ -130,6 +130,17 @@ def draw_backward_grads(B, T, H, dk, dv, io="f32", seed=0):
     return dO, dST
 
 
+def draw_prologue_grads(B, T, H, dk, dv, io="f32", seed=0):
+    """Gradients of the activations q^, k^, v^ for a backward pass through
+    the prologue, from a generator of their own (seed + 700,000): each
+    ~ N(0, 1), rounded to bf16 for bf16 workloads. Returns (dqh, dkh, dvh)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed) + 700_000)
+    out = [torch.randn(B, T, H, d, generator=gen, dtype=torch.float32) for d in (dk, dk, dv)]
+    if io == "bf16":
+        out = [x.to(torch.bfloat16) for x in out]
+    return tuple(out)
+
+
 def make(name: str, **overrides) -> Inputs:
     """Draw the named workload; keyword overrides replace its parameters
     (e.g. a smaller T for a quick check)."""
