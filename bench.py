@@ -311,6 +311,33 @@ def backward_bench(kda, workloads, torch, dev, args):
     ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     med = ms[len(ms) // 2]
     assert all(torch.isfinite(t.float()).all().item() for t in out)
+    # the prologue's gradient from the activation gradients just computed
+    ctot = H * (2 * dk + dv)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    ring0 = torch.zeros(B, 3, ctot, dtype=torch.bfloat16, device=dev)
+    pout = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+            torch.empty(ctot, 4, device=dev), torch.empty(B, 3, ctot, device=dev)]
+    pws = torch.empty(kda.kda_prologue_backward_workspace_bytes(dims, T), dtype=torch.uint8,
+                      device=dev)
+
+    def pcall():
+        kda.kda_prologue_backward(dims, T, q, k, v, conv_w, ring0, out[0], out[1], out[2],
+                                  *pout, workspace=pws)
+
+    for _ in range(args.backward_warmup):
+        pcall()
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        pcall()
+        e1.record()
+    torch.cuda.synchronize()
+    pms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    pmed = pms[len(pms) // 2]
+    assert all(torch.isfinite(t.float()).all().item() for t in pout)
+    # raw q, k, v and the three activation gradients read, three raw gradients
+    # written (bf16), plus the conv weights and their gradient
+    pbytes = B * T * H * (2 * dk + dv) * 2 * 3 + ctot * 4 * 4 * 2
     flops = backward_flops(B, T, H, dk, dv, 64)
     nbytes = backward_bytes(B, T, H, dk, dv)
     res = {"workload": "chunked backward (gradients of q^, k^, v^, g, beta, S0) of the "
@@ -321,8 +348,16 @@ def backward_bench(kda, workloads, torch, dev, args):
            "fp32_frac": flops / (med / 1e3) / 1e12 / FP32_VECTOR_TFLOPS,
            "compulsory_bytes": nbytes, "hbm_GBps": nbytes / (med / 1e3) / 1e9,
            "hbm_frac": nbytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS,
-           "workspace_bytes": ws.numel()}
-    del ws, out
+           "workspace_bytes": ws.numel(),
+           "prologue": {"what": "kda_prologue_backward: gradients of the raw q, k, v, the conv "
+                                "weights and the ring history from those of q^, k^, v^",
+                        "ms": pmed, "ms_min": pms[0], "ms_max": pms[-1],
+                        "compulsory_bytes": pbytes,
+                        "hbm_GBps": pbytes / (pmed / 1e3) / 1e9,
+                        "hbm_frac": pbytes / (pmed / 1e3) / 1e9 / HBM_PEAK_GBPS},
+           "training_backward_ms": med + pmed,
+           "training_backward_tokens_per_s": B * T / ((med + pmed) / 1e3)}
+    del ws, out, pws, pout
     return res
 
 

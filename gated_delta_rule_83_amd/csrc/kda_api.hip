@@ -451,15 +451,17 @@ kda_status kda_prologue_backward(const kda_dims* d, int32_t T, const void* q, co
   const size_t esz = io_size(d->io);
   KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
   KDA_REQUIRE_PTR(dconv_w, "dconv_w", 16);
-  if (ring && !aligned(ring, esz)) return fail(KDA_ERR_INVALID, "ring is misaligned");
+  // q, k, v, the ring and the activation gradients are read 16 (fp32) or 8
+  // (bf16) bytes at a time
+  if (ring && !aligned16(ring)) return fail(KDA_ERR_INVALID, "ring is not 16-byte aligned");
   if (dring && !aligned(dring, 4)) return fail(KDA_ERR_INVALID, "dring is misaligned");
   if (T > 0) {
-    KDA_REQUIRE_PTR(q, "q", esz);
-    KDA_REQUIRE_PTR(k, "k", esz);
-    KDA_REQUIRE_PTR(v, "v", esz);
-    KDA_REQUIRE_PTR(dq_hat, "dq_hat", esz);
-    KDA_REQUIRE_PTR(dk_hat, "dk_hat", esz);
-    KDA_REQUIRE_PTR(dv_hat, "dv_hat", esz);
+    KDA_REQUIRE_PTR(q, "q", 16);
+    KDA_REQUIRE_PTR(k, "k", 16);
+    KDA_REQUIRE_PTR(v, "v", 16);
+    KDA_REQUIRE_PTR(dq_hat, "dq_hat", 16);
+    KDA_REQUIRE_PTR(dk_hat, "dk_hat", 16);
+    KDA_REQUIRE_PTR(dv_hat, "dv_hat", 16);
     KDA_REQUIRE_PTR(dq, "dq", esz);
     KDA_REQUIRE_PTR(dk, "dk", esz);
     KDA_REQUIRE_PTR(dv, "dv", esz);

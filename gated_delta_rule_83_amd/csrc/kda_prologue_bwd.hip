@@ -11,7 +11,7 @@
 // dz = dv^ (v); dy = dz (s(y) + y s(y) (1 - s(y))), s the logistic sigmoid;
 // dx_{t-3+j} += w[c][j] dy_t and dw[c][j] += dy_t x_{t-3+j}.
 //
-// One workgroup per (sequence, head, 64-token segment): the raw values of
+// One workgroup per (sequence, head, 32-token segment): the raw values of
 // the segment and the 3 tokens before it are staged in LDS, dy is formed for
 // the segment and the 3 tokens after it (wave per token, lanes over
 // channels, the two L2 sums by wave reductions), then dx of the segment,
@@ -22,9 +22,34 @@
 namespace kda {
 namespace {
 
-constexpr int kSeg = 64;       // tokens per workgroup
+constexpr int kSeg = 32;       // tokens per workgroup
 constexpr int kPBT = 256;      // threads per workgroup
 constexpr int kHalo = 3;       // conv history
+
+__device__ __forceinline__ f32x4 ld4x(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4x(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// rows x N values into LDS rows of 128 floats, 4 per load, every load of a
+// thread issued before its stores; src(u, c) gives the four values of row u
+// from column c.
+template <int N, int MAXROWS, class F>
+__device__ __forceinline__ void stage(float (*dst)[128], int rows, F&& src) {
+  constexpr int Q = N / 4, PER = (MAXROWS * Q + kPBT - 1) / kPBT;
+  f32x4 buf[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int i = (int)threadIdx.x + p * kPBT, u = i / Q, c = 4 * (i % Q);
+    buf[p] = u < rows ? src(u, c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int i = (int)threadIdx.x + p * kPBT, u = i / Q, c = 4 * (i % Q);
+    if (u < rows) *reinterpret_cast<f32x4*>(&dst[u][c]) = buf[p];
+  }
+}
 
 template <int N, bool L2, typename IO>
 __device__ void proj_backward(const PrologueBwdArgs& a, int b, int h, int seg, long c0,
@@ -36,19 +61,27 @@ __device__ void proj_backward(const PrologueBwdArgs& a, int b, int h, int seg, l
   const long base = (long)b * T * st + (long)h * N;       // token 0 of (b, h)
   const long Ctot = (long)a.H * (2 * a.dk + a.dv);
   const IO* ring = static_cast<const IO*>(a.ring);
-  // raw values of tokens t0-3 .. te-1 (row u is token t0 - 3 + u)
-  for (int i = tid; i < (te - t0 + kHalo) * N; i += kPBT) {
-    const int u = i / N, c = i % N, t = t0 - kHalo + u;
-    float val = 0.f;
-    if (t >= 0) val = to_f32(x[base + (long)t * st + c]);
-    else if (ring) val = to_f32(ring[((long)b * 3 + (3 + t)) * Ctot + c0 + c]);
-    sx[u][c] = val;
-  }
+  // raw values of tokens t0-3 .. te-1 (row u is token t0 - 3 + u), and the
+  // activation gradients of tokens t0 .. te-1 (sdy, replaced by dy in place)
+  stage<N, kSeg + 2 * kHalo>(sx, te - t0 + kHalo, [&](int u, int c) {
+    const int t = t0 - kHalo + u;
+    if (t >= 0) return ld4x(x + base + (long)t * st + c);
+    if (ring) return ld4x(ring + ((long)b * 3 + (3 + t)) * Ctot + c0 + c);
+    return f32x4{0.f, 0.f, 0.f, 0.f};
+  });
+  stage<N, kSeg + kHalo>(sdy, te - t0,
+                         [&](int u, int c) { return ld4x(dxh + base + (long)(t0 + u) * st + c); });
   __syncthreads();
   // dy of tokens t0 .. te-1: wave per token, lanes over channels
   constexpr int CPL = (N + kWave - 1) / kWave;
+  f32x4 wl[CPL];
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int c = lane + kWave * m;
+    wl[m] = c < N ? *reinterpret_cast<const f32x4*>(a.conv_w + 4 * (c0 + c))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   for (int u = wv; u < te - t0; u += kPBT / kWave) {
-    const long row = base + (long)(t0 + u) * st;
     float yv[CPL], zv[CPL], gv[CPL];
     float ss = 0.f, dot = 0.f;
 #pragma unroll
@@ -56,10 +89,10 @@ __device__ void proj_backward(const PrologueBwdArgs& a, int b, int h, int seg, l
       const int c = lane + kWave * m;
       yv[m] = zv[m] = gv[m] = 0.f;
       if (c < N) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(a.conv_w + 4 * (c0 + c));
+        const f32x4 w = wl[m];
         yv[m] = w[0] * sx[u][c] + w[1] * sx[u + 1][c] + w[2] * sx[u + 2][c] + w[3] * sx[u + 3][c];
         zv[m] = yv[m] / (1.0f + __expf(-yv[m]));
-        gv[m] = to_f32(dxh[row + c]);
+        gv[m] = sdy[u][c];
         ss += zv[m] * zv[m];
         dot += zv[m] * gv[m];
       }
@@ -82,19 +115,24 @@ __device__ void proj_backward(const PrologueBwdArgs& a, int b, int h, int seg, l
     }
   }
   __syncthreads();
-  // dx of the segment's tokens: dx_t = sum_j w[j] dy_{t+3-j} (t + 3 - j < T)
-  for (int i = tid; i < (t1 - t0) * N; i += kPBT) {
-    const int u = i / N, c = i % N;
+  // dx of the segment's tokens: dx_t = sum_j w[j] dy_{t+3-j} (t + 3 - j < T);
+  // a thread's channel is the same in every iteration (N divides kPBT)
+  static_assert(kPBT % N == 0, "channel per thread");
+  {
+    const int c = tid % N;
     const f32x4 w = *reinterpret_cast<const f32x4*>(a.conv_w + 4 * (c0 + c));
-    float acc = 0.f;
+    for (int u = tid / N; u < t1 - t0; u += kPBT / N) {
+      float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (u + 3 - j < te - t0) acc += w[j] * sdy[u + 3 - j][c];
-    dxo[base + (long)(t0 + u) * st + c] = from_f32<IO>(acc);
+      for (int j = 0; j < 4; ++j)
+        if (u + 3 - j < te - t0) acc += w[j] * sdy[u + 3 - j][c];
+      dxo[base + (long)(t0 + u) * st + c] = from_f32<IO>(acc);
+    }
   }
   // the segment's share of dw, and the ring's gradient in the first segment
   for (int c = tid; c < N; c += kPBT) {
     f32x4 dw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int u = 0; u < t1 - t0; ++u) {
       const float d = sdy[u][c];
 #pragma unroll
@@ -118,8 +156,8 @@ __device__ void proj_backward(const PrologueBwdArgs& a, int b, int h, int seg, l
 
 template <int DK, int DV, typename IO>
 __global__ __launch_bounds__(kPBT) void prologue_bwd_kernel(PrologueBwdArgs a) {
-  __shared__ float sx[kSeg + 2 * kHalo][128];
-  __shared__ float sdy[kSeg + kHalo][128];
+  __shared__ __attribute__((aligned(16))) float sx[kSeg + 2 * kHalo][128];
+  __shared__ __attribute__((aligned(16))) float sdy[kSeg + kHalo][128];
   const int seg = blockIdx.x % a.nseg, bh = blockIdx.x / a.nseg;
   const int b = bh / a.H, h = bh % a.H;
   const IO* q = static_cast<const IO*>(a.q);

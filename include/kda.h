@@ -275,8 +275,8 @@ kda_status kda_chunk_backward(const kda_dims* dims, int32_t T, const void* q,
                               float* dbeta, float* dS0, int32_t chunk, void* workspace,
                               size_t workspace_bytes, uint32_t flags, hipStream_t stream);
 
-/* Device workspace that kda_prologue_backward needs: the per-64-token-segment
- * conv-weight gradients, B * ceil(T / 64) * Ctot * 16 bytes (0 for invalid
+/* Device workspace that kda_prologue_backward needs: the per-32-token-segment
+ * conv-weight gradients, B * ceil(T / 32) * Ctot * 16 bytes (0 for invalid
  * arguments; 0 for T = 0). */
 size_t kda_prologue_backward_workspace_bytes(const kda_dims* dims, int32_t T);
 
@@ -294,6 +294,8 @@ size_t kda_prologue_backward_workspace_bytes(const kda_dims* dims, int32_t T);
  *  dq, dk: [B][T][H][d_k] io dtype (written); dv: [B][T][H][d_v];
  *  dconv_w: [Ctot][4] fp32 (written, 16-byte aligned);
  *  dring: [B][3][Ctot] fp32 (written), or NULL.
+ * q, k, v, ring, dq_hat, dk_hat and dv_hat must be 16-byte aligned (the
+ * outputs dq, dk, dv the alignment of their element type).
  * workspace: kda_prologue_backward_workspace_bytes (16-byte aligned). flags
  * must be 0. All arithmetic is fp32; the weight gradient is summed in a
  * fixed order (bitwise reproducible). T = 0 writes zero dconv_w and dring.

@@ -267,8 +267,8 @@ def test_prologue_backward_validation():
     d = kda.make_dims(2, 3, 16, 32, kda.KDA_F32)
     L = kda.lib()
     ctot = 3 * (2 * 16 + 32)
-    assert kda.kda_prologue_backward_workspace_bytes(d, 64) == 2 * 1 * ctot * 16
-    assert kda.kda_prologue_backward_workspace_bytes(d, 65) == 2 * 2 * ctot * 16
+    assert kda.kda_prologue_backward_workspace_bytes(d, 32) == 2 * 1 * ctot * 16
+    assert kda.kda_prologue_backward_workspace_bytes(d, 33) == 2 * 2 * ctot * 16
     assert kda.kda_prologue_backward_workspace_bytes(d, -1) == 0
     need = kda.kda_prologue_backward_workspace_bytes(d, 8)
     names = ["q", "k", "v", "w", "ring", "dqh", "dkh", "dvh", "dq", "dk", "dv", "dw", "dring",
@@ -285,6 +285,9 @@ def test_prologue_backward_validation():
         assert call(**{name: None}) == K.KDA_ERR_INVALID, name
     assert call(w=FAKE + 4) == K.KDA_ERR_INVALID
     assert call(dw=FAKE + 4) == K.KDA_ERR_INVALID
+    assert call(q=FAKE + 4) == K.KDA_ERR_INVALID
+    assert call(ring=FAKE + 8) == K.KDA_ERR_INVALID
+    assert call(dvh=FAKE + 8) == K.KDA_ERR_INVALID
     assert call(ws=FAKE + 4) == K.KDA_ERR_INVALID
     assert call(ws_bytes=need - 1) == K.KDA_ERR_INVALID
     assert "workspace" in kda.last_error()
