@@ -82,16 +82,18 @@ __device__ void proj_backward(const PrologueBwdArgs& a, int b, int h, int seg, l
                   : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int u = wv; u < te - t0; u += kPBT / kWave) {
-    float yv[CPL], zv[CPL], gv[CPL];
+    float yv[CPL], zv[CPL], gv[CPL], sv[CPL];
     float ss = 0.f, dot = 0.f;
 #pragma unroll
     for (int m = 0; m < CPL; ++m) {
       const int c = lane + kWave * m;
-      yv[m] = zv[m] = gv[m] = 0.f;
+      yv[m] = zv[m] = gv[m] = sv[m] = 0.f;
       if (c < N) {
         const f32x4 w = wl[m];
         yv[m] = w[0] * sx[u][c] + w[1] * sx[u + 1][c] + w[2] * sx[u + 2][c] + w[3] * sx[u + 3][c];
-        zv[m] = yv[m] / (1.0f + __expf(-yv[m]));
+        // sigmoid by the hardware reciprocal (about 1 ulp), as in the forward's SiLU
+        sv[m] = __builtin_amdgcn_rcpf(1.0f + __expf(-yv[m]));
+        zv[m] = yv[m] * sv[m];
         gv[m] = sdy[u][c];
         ss += zv[m] * zv[m];
         dot += zv[m] * gv[m];
@@ -101,7 +103,7 @@ __device__ void proj_backward(const PrologueBwdArgs& a, int b, int h, int seg, l
     if constexpr (L2) {
       ss = wave_sum(ss);
       dot = wave_sum(dot);
-      inv = 1.0f / sqrtf(ss + kL2Eps);
+      inv = __builtin_amdgcn_rsqf(ss + kL2Eps);
     }
 #pragma unroll
     for (int m = 0; m < CPL; ++m) {
@@ -109,7 +111,7 @@ __device__ void proj_backward(const PrologueBwdArgs& a, int b, int h, int seg, l
       if (c < N) {
         // (dq^ - q^ (q^ . dq^)) / |z| with q^ = z / |z| and q^ . dq^ = (z . dq^) / |z|
         const float dz = L2 ? (gv[m] - zv[m] * dot * inv * inv) * inv : gv[m];
-        const float sg = 1.0f / (1.0f + __expf(-yv[m]));
+        const float sg = sv[m];
         sdy[u][c] = dz * (sg + yv[m] * sg * (1.0f - sg));
       }
     }
@@ -178,6 +180,7 @@ __global__ __launch_bounds__(256) void conv_w_grad_kernel(const float* wpart, lo
   const long c = (long)blockIdx.x * 256 + threadIdx.x;
   if (c >= ctot) return;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
   for (long p = 0; p < parts; ++p) acc += *reinterpret_cast<const f32x4*>(wpart + (p * ctot + c) * 4);
   *reinterpret_cast<f32x4*>(dconv_w + c * 4) = acc;
 }
