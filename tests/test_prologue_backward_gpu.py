@@ -144,3 +144,63 @@ def test_training_gradient_chained():
     print("chained training gradient: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for n, e in errs.items():
         assert e <= 1e-4, (n, e)
+
+
+def test_training_backward_in_captured_graph_matches_eager():
+    """Both backward calls with caller workspaces launch only kernels, so they
+    can be captured in one HIP graph: each replay (outputs overwritten with
+    NaN by eager work in between) gives the eager gradients bit for bit."""
+    dev = device()
+    inp = workloads.draw(1, 150, 2, 128, 64, io="bf16", seed=25, s0_random=True,
+                         ring_random=True)
+    B, T, H, dk, dv = inp.dims
+    bf = torch.bfloat16
+    dims = kda.make_dims(B, H, dk, dv, bf)
+    ctot = H * (2 * dk + dv)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    w, ring = inp.conv_w.to(dev), inp.ring0.to(dev)
+    g, beta, S0 = inp.g.to(dev), inp.beta.to(dev), inp.S0.to(dev)
+    acts = [torch.empty(B, T, H, d, device=dev) for d in (dk, dk, dv)]
+    kda.kda_conv_prologue(dims, T, q, k, v, w, ring.clone(), *acts)
+    qh, kh, vh = (x.to(bf) for x in acts)
+    dO, dST = (x.to(dev) for x in workloads.draw_backward_grads(B, T, H, dk, dv, io="bf16",
+                                                                  seed=25))
+    ws1 = torch.empty(kda.kda_backward_workspace_bytes(dims, T, 64), dtype=torch.uint8,
+                      device=dev)
+    ws2 = torch.empty(kda.kda_prologue_backward_workspace_bytes(dims, T), dtype=torch.uint8,
+                      device=dev)
+
+    def outputs():
+        return [torch.empty(B, T, H, dk, dtype=bf, device=dev),
+                torch.empty(B, T, H, dk, dtype=bf, device=dev),
+                torch.empty(B, T, H, dv, dtype=bf, device=dev),
+                torch.empty(B, T, H, dk, device=dev), torch.empty(B, T, H, device=dev),
+                torch.empty(B, H, dk, dv, device=dev),
+                torch.empty(B, T, H, dk, dtype=bf, device=dev),
+                torch.empty(B, T, H, dk, dtype=bf, device=dev),
+                torch.empty(B, T, H, dv, dtype=bf, device=dev),
+                torch.empty(ctot, 4, device=dev), torch.empty(B, 3, ctot, device=dev)]
+
+    def call(o):
+        kda.kda_chunk_backward(dims, T, qh, kh, vh, g, beta, S0, dO, dST, *o[:6], chunk=64,
+                               workspace=ws1)
+        kda.kda_prologue_backward(dims, T, q, k, v, w, ring, o[0], o[1], o[2], *o[6:],
+                                  workspace=ws2)
+
+    eager, cap = outputs(), outputs()
+    call(cap)  # warm-up, eager
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        call(eager)
+        torch.cuda.synchronize()
+        for t in cap:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(cap, eager)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs"
