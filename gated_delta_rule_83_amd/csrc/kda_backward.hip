@@ -161,6 +161,28 @@ __device__ __forceinline__ void stage_rows(float* dst, int live, F&& ld4) {
   put_rows<LD>(b, dst);
 }
 constexpr int kBP = 1024;  // threads of the per-chunk kernels with scalar loops
+
+// Decay factors e^{Gam_r - Gam_j} (j <= r) of a chunk may be formed as the
+// product e^{Gam_r} e^{-Gam_j} when every channel's total in-chunk decay
+// -Gam_{n-1} is at most this (e^60 ~ 1e26 keeps every factor, and its
+// products with the unit-norm activations and their gradients, well inside
+// fp32); the pair sums then become matrix products. Chunks that decay faster
+// take the explicit per-pair exponentials.
+constexpr float kFactorMaxDecay = 60.f;
+
+// true when -Gam[n-1][c] <= kFactorMaxDecay for every channel c (all
+// threads of the workgroup take part; the result is uniform).
+template <int NT, int DK, int LD>
+__device__ __forceinline__ bool chunk_factorable(const float (*sG)[LD], int n, int* flag) {
+  if (threadIdx.x == 0) *flag = 1;
+  __syncthreads();
+  for (int c = threadIdx.x; c < DK; c += NT)
+    if (!(-sG[n - 1][c] <= kFactorMaxDecay)) *flag = 0;
+  __syncthreads();
+  const bool ok = *flag != 0;
+  __syncthreads();
+  return ok;
+}
 constexpr int kBS = 512;   // threads of the solve-gradient kernel
 
 // ---- 1. per chunk-head: Gam, A, P, X, Q~, K~, K^d, W, U' --------------------
@@ -859,7 +881,44 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
   stage_rows<kBP, CM, DK, PK>(&sG[0][0], n, [&](int r, int c) { return ld4f(blk + L::oG + r * DK + c); });
   stage_rows<kBP, CM, CM, PC>(&sdA[0][0], n, [&](int r, int c) { return ld4f(blk + L::odA + r * CM + c); });
   stage_rows<kBP, CM, CM, PC>(&sdP[0][0], n, [&](int r, int c) { return ld4f(blk + L::odP + r * CM + c); });
+  __shared__ int sflag;
   __syncthreads();
+  if (chunk_factorable<kBP, DK, PK>(sG, n, &sflag)) {
+    // With e^{Gam_r - Gam_j} = e^{Gam_r} e^{-Gam_j}, per channel c:
+    //   SA = e^{Gam} (dA K-), SP = e^{Gam} (dP K-), TT = e^{-Gam} (dA^T K~ + dP^T Q~)
+    // with K- = k^ e^{-Gam}, K~ = k^ e^{Gam}, Q~ = q^ e^{Gam}: fp32 MFMA
+    // tiles, the exponentials formed per operand element.
+    const int lane = tid % kWave, wv = tid / kWave, l16 = lane % 16, r4 = 4 * (lane / 16);
+    const int n4 = (n + 3) & ~3;
+    constexpr int NW = kBP / kWave, NT16 = (CM / 16) * (DK / 16);
+    for (int t = wv; t < NT16; t += NW) {
+      const int rt = t / (DK / 16), ct = t % (DK / 16);
+      if (16 * rt >= n) continue;
+      const int cb = 16 * ct;
+      auto kminus = [&](int kx, int j) { return sK[kx][cb + j] * __expf(-sG[kx][cb + j]); };
+      const f32x4 rs = mma_tile(kZero4, n4, [&](int i, int kx) { return sdA[16 * rt + i][kx]; },
+                                kminus);
+      const f32x4 rp = mma_tile(kZero4, n4, [&](int i, int kx) { return sdP[16 * rt + i][kx]; },
+                                kminus);
+      f32x4 ct4 = mma_tile(kZero4, n4, [&](int i, int kx) { return sdA[kx][16 * rt + i]; },
+                           [&](int kx, int j) { return sK[kx][cb + j] * __expf(sG[kx][cb + j]); });
+      ct4 = mma_tile(ct4, n4, [&](int i, int kx) { return sdP[kx][16 * rt + i]; },
+                     [&](int kx, int j) { return sQ[kx][cb + j] * __expf(sG[kx][cb + j]); });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + r4 + e, c = cb + l16;
+        if (r >= n) continue;
+        const float G = sG[r][c], eg = __expf(G);
+        const float SA = eg * rs[e], SP = eg * rp[e], TT = ct4[e] * __expf(-G);
+        const float kr = sK[r][c], qr = sQ[r][c];
+        const long i = (long)r * DK + c;
+        const long o = tok(a, it.b, it.t0 + r, it.h) * DK + c;
+        dq[o] = from_f32<IO>(blk[L::odq + i] + SP);
+        dk[o] = from_f32<IO>(blk[L::odk + i] + SA + TT);
+        blk[L::odG + i] += kr * SA + qr * SP - kr * TT;
+      }
+    }
+  } else {
   // two channels per thread (8-byte LDS reads); rows r0, r0 + RG, ...
   const int c0 = 2 * (tid % (DK / 2));
   for (int r = tid / (DK / 2); r < n; r += RG) {
@@ -896,6 +955,7 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
       dk[o] = from_f32<IO>(blk[L::odk + i] + SA[e] + TT[e]);
       blk[L::odG + i] += kr[e] * SA[e] + qr[e] * SP[e] - kr[e] * TT[e];
     }
+  }
   }
   __syncthreads();
   if (tid < DK) {  // dg = reverse in-chunk prefix sum of dGam
