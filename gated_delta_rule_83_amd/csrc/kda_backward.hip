@@ -217,43 +217,70 @@ __global__ __launch_bounds__(kBP) void bw_prep_kernel(BackwardArgs a) {
     }
   }
   __syncthreads();
-  // A (strictly lower) and P (lower), every exponent Gam_r - Gam_j (j <= r)
-  // <= 0. Wave w takes the row pairs (r, CM-1-r), r = w, w+NW, ...: lanes
-  // l < r hold row r, column l; the other lanes row CM-1-r, column l - r (its
-  // diagonal included), so all 64 lanes work. The diagonal of row r and the
-  // zeros right of every diagonal come from the pass after.
-  for (int r = wv; r < CM / 2 && r < n; r += NW) {
-    const bool first = lane < r;
-    const int row = first ? r : CM - 1 - r, j = first ? lane : lane - r;
-    if (row >= n) continue;
-    float accA = 0.f, accP = 0.f;
-#pragma unroll 2
-    for (int cc = 0; cc < DK; cc += 4) {
-      const f32x4 kj = *reinterpret_cast<const f32x4*>(&sK[j][cc]);
-      const f32x4 gj = *reinterpret_cast<const f32x4*>(&sG[j][cc]);
-      const f32x4 kr = *reinterpret_cast<const f32x4*>(&sK[row][cc]);
-      const f32x4 qr = *reinterpret_cast<const f32x4*>(&sQ[row][cc]);
-      const f32x4 gr = *reinterpret_cast<const f32x4*>(&sG[row][cc]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ke = kj[e] * __expf(gr[e] - gj[e]);
-        accA += kr[e] * ke;
-        accP += qr[e] * ke;
-      }
+  __shared__ int sflag;
+  if (chunk_factorable<kBP, DK, PK>(sG, n, &sflag)) {
+    // A = K~ K-^T (strictly lower), P = Q~ K-^T (lower), with K~ = k^ e^{Gam},
+    // Q~ = q^ e^{Gam}, K- = k^ e^{-Gam} formed per operand element: one 16 x 16
+    // tile of the C x C matrices per wave (tiles right of the diagonal are zero)
+    static_assert((CM / 16) * (CM / 16) == NW, "one C x C tile per wave");
+    const int rt = wv / (CM / 16), ct = wv % (CM / 16);
+    f32x4 ta = kZero4, tp = kZero4;
+    if (16 * rt < n && ct <= rt) {
+      auto kminus = [&](int kx, int j) { return sK[16 * ct + j][kx] * __expf(-sG[16 * ct + j][kx]); };
+      ta = mma_tile(kZero4, DK, [&](int i, int kx) {
+        return sK[16 * rt + i][kx] * __expf(sG[16 * rt + i][kx]);
+      }, kminus);
+      tp = mma_tile(kZero4, DK, [&](int i, int kx) {
+        return sQ[16 * rt + i][kx] * __expf(sG[16 * rt + i][kx]);
+      }, kminus);
     }
-    blk[L::oP + row * CM + j] = accP;
-    blk[L::oA + row * CM + j] = j < row ? accA : 0.f;
-    sM[row][j] = j < row ? sb[row] * accA : 0.f;
-  }
-  for (int i = tid; i < n * CM; i += kBP) {
-    const int row = i / CM, j = i % CM;
-    if (j < row || (j == row && row >= CM / 2)) continue;
-    float p = 0.f;
-    if (j == row)
-      for (int cc = 0; cc < DK; ++cc) p += sQ[row][cc] * sK[row][cc];
-    blk[L::oP + i] = p;
-    blk[L::oA + i] = 0.f;
-    sM[row][j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + r4 + e, j = 16 * ct + l16;
+      if (r >= n) continue;
+      blk[L::oP + r * CM + j] = j <= r ? tp[e] : 0.f;
+      blk[L::oA + r * CM + j] = j < r ? ta[e] : 0.f;
+      sM[r][j] = j < r ? sb[r] * ta[e] : 0.f;
+    }
+  } else {
+    // A (strictly lower) and P (lower), every exponent Gam_r - Gam_j (j <= r)
+    // <= 0. Wave w takes the row pairs (r, CM-1-r), r = w, w+NW, ...: lanes
+    // l < r hold row r, column l; the other lanes row CM-1-r, column l - r (its
+    // diagonal included), so all 64 lanes work. The diagonal of row r and the
+    // zeros right of every diagonal come from the pass after.
+    for (int r = wv; r < CM / 2 && r < n; r += NW) {
+      const bool first = lane < r;
+      const int row = first ? r : CM - 1 - r, j = first ? lane : lane - r;
+      if (row >= n) continue;
+      float accA = 0.f, accP = 0.f;
+  #pragma unroll 2
+      for (int cc = 0; cc < DK; cc += 4) {
+        const f32x4 kj = *reinterpret_cast<const f32x4*>(&sK[j][cc]);
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&sG[j][cc]);
+        const f32x4 kr = *reinterpret_cast<const f32x4*>(&sK[row][cc]);
+        const f32x4 qr = *reinterpret_cast<const f32x4*>(&sQ[row][cc]);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sG[row][cc]);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ke = kj[e] * __expf(gr[e] - gj[e]);
+          accA += kr[e] * ke;
+          accP += qr[e] * ke;
+        }
+      }
+      blk[L::oP + row * CM + j] = accP;
+      blk[L::oA + row * CM + j] = j < row ? accA : 0.f;
+      sM[row][j] = j < row ? sb[row] * accA : 0.f;
+    }
+    for (int i = tid; i < n * CM; i += kBP) {
+      const int row = i / CM, j = i % CM;
+      if (j < row || (j == row && row >= CM / 2)) continue;
+      float p = 0.f;
+      if (j == row)
+        for (int cc = 0; cc < DK; ++cc) p += sQ[row][cc] * sK[row][cc];
+      blk[L::oP + i] = p;
+      blk[L::oA + i] = 0.f;
+      sM[row][j] = 0.f;
+    }
   }
   __syncthreads();
   // X = (I + diag(beta) A)^-1, unit lower triangular, by forward
