@@ -28,9 +28,10 @@
 // block, keeps the entering state of every chunk) -> reverse chain (same
 // grid, keeps the leaving-state gradient of every chunk and dU) -> dense
 // gradients (per chunk-head) -> inverse and beta gradients (per chunk-head)
-// -> decayed-Gram gradients and dg (per chunk-head). The decay factors are
-// formed as exponentials of non-positive differences, so any finite g <= 0
-// is accepted.
+// -> decayed-Gram gradients and dg (per chunk-head). Any finite g <= 0 is
+// accepted: a chunk whose total decay stays within a limit forms its decayed
+// pair terms as MFMA products of e^{Gam}- and e^{-Gam}-scaled rows, any other
+// chunk one exponential of a non-positive difference per pair.
 #include <type_traits>
 
 #include "kda_common.h"

@@ -245,8 +245,10 @@ size_t kda_backward_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chu
  * prologue (conv, SiLU, L2) is not part of it.
  *  q, k:  [B][T][H][d_k] q^, k^ as the recurrence consumes them (io dtype);
  *  v:     [B][T][H][d_v] v^;
- *  g:     [B][T][H][d_k] fp32 log-decay, finite and <= 0 (any such value:
- *         the decay factors are exponentials of non-positive differences);
+ *  g:     [B][T][H][d_k] fp32 log-decay, finite and <= 0 (any such value: a
+ *         chunk whose decay exceeds 60 on some channel takes exponentials of
+ *         non-positive differences, the others products of two factors
+ *         within 1e+-26);
  *  beta:  [B][T][H] fp32;
  *  S0:    [B][H][d_k][d_v] fp32 entering state, or NULL for zero;
  *  dO:    [B][T][H][d_v] io dtype;  dST: [B][H][d_k][d_v] fp32, or NULL for zero;
