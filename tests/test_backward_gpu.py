@@ -167,3 +167,13 @@ def test_backward_ignores_workspace_contents_and_is_deterministic():
     for x, y, z in zip(a, b, c):
         assert torch.isfinite(x.float()).all()
         assert torch.equal(x, y) and torch.equal(y, z)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dk,dv", [(a, b) for a in (16, 32, 64, 128) for b in (16, 32, 64, 128)])
+def test_backward_every_shape(dk, dv, chunk, io):
+    """Every supported (d_k, d_v, chunk, I/O type): 70 tokens (a ragged last
+    chunk for every chunk size), two sequences, random S0 and ring."""
+    inp = workloads.draw(2, 70, 2, dk, dv, io=io, seed=31, s0_random=True, ring_random=True)
+    check(inp, chunk, io)

@@ -204,3 +204,11 @@ def test_training_backward_in_captured_graph_matches_eager():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(cap, eager)):
             assert torch.equal(a, b), f"replay {rep}: output {i} differs"
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(a, b) for a in (16, 32, 64, 128) for b in (16, 32, 64, 128)])
+def test_prologue_backward_every_shape(dk, dv, io):
+    """Every supported (d_k, d_v, I/O type): 70 tokens (three segments, the
+    last ragged), two sequences, a random ring."""
+    check(workloads.draw(2, 70, 2, dk, dv, io=io, seed=32, ring_random=True), io)
