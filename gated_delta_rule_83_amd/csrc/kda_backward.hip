@@ -778,6 +778,16 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
   for (int t = wv; t < RT * (DK / 16); t += NW) {
     const int rt = t % RT, ct = t / RT;
     if (16 * rt >= n) continue;
+    // this tile's dk^, dGam partials and Gam, loaded before the products
+    float pk[4], pg[4], gg[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e;
+      const long o = (long)row * DK + 16 * ct + l16;
+      pk[e] = row < n ? blk[L::odk + o] : 0.f;
+      pg[e] = row < n ? blk[L::odG + o] : 0.f;
+      gg[e] = row < n ? blk[L::oG + o] : 0.f;
+    }
     const f32x4 y = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
                              [&](int kx, int j) { return sdW[kx][16 * ct + j]; });
 #pragma unroll
@@ -787,8 +797,8 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
       if (row < n) {
         const long o = (long)row * DK + cc;
         const float br = sbt[row], kt = sKt[row][cc];
-        blk[L::odk + o] += __expf(blk[L::oG + o]) * br * y[e];
-        blk[L::odG + o] += kt * br * y[e];
+        blk[L::odk + o] = pk[e] + __expf(gg[e]) * br * y[e];
+        blk[L::odG + o] = pg[e] + kt * br * y[e];
         part = kt * y[e];
       }
       part = sum16(part);
