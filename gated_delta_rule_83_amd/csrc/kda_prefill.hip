@@ -19,11 +19,15 @@
 // workspace. A second kernel ("chain") walks the chunks of each (sequence,
 // head, dv-block) in order, keeping its block of S in MFMA accumulators.
 //
-// Overflow-safe Gram matrices: A and P are computed on MFMA as products of
-// factors k_r e^{Gam_r - Gam_m} and k_j e^{Gam_m - Gam_j}, where m is the
-// first row of the 16-row block of r. For j < m both exponents are <= 0; for
-// j inside the diagonal block the second exponent is a sum of at most 15
-// decays, which the documented precondition keeps inside the fp32 range.
+// Overflow-safe Gram matrices, for any g <= 0 (-inf included): no factor is
+// the exponential of a positive number. For j in an earlier 16-token block b
+// than r's block a, e^{Gam_r - Gam_j} is the product of the row factor
+// e^{Gam_r - Gam_m(a)}, the block factor e^{Gam_m(a) - Gam_e(b)} and the
+// column factor e^{Gam_e(b) - Gam_j} (m = a block's first token, e = its
+// last), each <= 1, and those tiles run on MFMA. Pairs inside one block are
+// formed explicitly as sums over channels of k_r k_j (or q_r k_j) times the
+// product of e^{g} over tokens j+1 .. r. Every exponent is a sum of decays of
+// one sign, so a very large decay costs no precision through cancellation.
 #include "kda_prefill.h"
 
 namespace kda {
@@ -109,7 +113,8 @@ struct PrepSmem {
   // that the 16 rows of a fragment read fall in different LDS banks)
   static constexpr int LDW = DKP + 16 / (int)sizeof(MT);
   static constexpr size_t oK = oQ + nQ, nK = mx((size_t)C * LDK * 4, (size_t)C * LDW * sizeof(MT));
-  // R: e^{Gam_r - Gam_m(r)} (fp32), later X (fp32 [C][LDC]) then X as MT [C][LDT]
+  // R: the decays g (fp32), then k^ E with E = e^{Gam_e - Gam_r} (the column
+  // factors), later X (fp32 [C][LDC]) then X as MT [C][LDT]
   static constexpr size_t oR = oK + nK;
   static constexpr size_t oXb = oR + (size_t)C * LDC * 4;
   static constexpr size_t nR = mx((size_t)C * LDK * 4, (size_t)C * LDC * 4 + (size_t)C * LDT * sizeof(MT));
@@ -118,8 +123,8 @@ struct PrepSmem {
   static constexpr size_t nL = mx((size_t)C * LDC * 4, (size_t)2 * NRB * DK * 4);
   static constexpr size_t oV = oL + nL;                              // (beta v^)^T as MT [DV][LDT]
   static constexpr size_t oB = oV + (size_t)DV * LDT * sizeof(MT);   // beta [C]
-  // block decays: EB[a] = e^{Gam_16a}, EN[a] = e^{Gam_{C-1} - Gam_16a},
-  // BT[a][b] = e^{Gam_16a - Gam_16b} for b < a
+  // block decays: EB[a] = e^{Gam_m(a)}, EN[a] = e^{Gam_{C-1} - Gam_e(a)},
+  // BT[a][b] = e^{Gam_m(a) - Gam_e(b)} for b < a
   static constexpr size_t oE = oB + (size_t)C * 4;
   static constexpr int NBT = NRB * (NRB - 1) / 2;
   static constexpr size_t bytes = oE + (size_t)(2 * NRB + NBT) * DK * 4;
@@ -311,107 +316,184 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
         for (int e = 0; e < 8; ++e) VTile<MT>::store(&sVT[qc0 + e][qr0], vt[e]);
       }
     } else if (role == 3) {
-      // strip-local inclusive prefix sums of g, parked in the R region
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // the strip's decays (0 past the last token) to the R region; its
+      // first decay and the sum of the other 15 to sFirst / sTot
       if (a.flags & KDA_F_RAW_GATES) {  // raw projections: the log-decay formed here
 #pragma unroll
         for (int r = 0; r < GS; ++r)
           buf[r] = f32x4{log_sigmoid(buf[r].x), log_sigmoid(buf[r].y), log_sigmoid(buf[r].z),
                          log_sigmoid(buf[r].w)};
       }
+      f32x4 rest = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < GS; ++r) {
         const bool valid = GS * gs + r < n;
         const f32x4 gv = valid ? buf[r] : f32x4{0.f, 0.f, 0.f, 0.f};
         if (r == 0) *reinterpret_cast<f32x4*>(&sFirst[gs][gc0]) = gv;
-        acc += gv;
-        *reinterpret_cast<f32x4*>(&sR[GS * gs + r][gc0]) = acc;
+        else rest += gv;
+        *reinterpret_cast<f32x4*>(&sR[GS * gs + r][gc0]) = gv;
       }
-      *reinterpret_cast<f32x4*>(&sTot[gs][gc0]) = acc;
+      *reinterpret_cast<f32x4*>(&sTot[gs][gc0]) = rest;
     }
     __syncthreads();
 
-    // ---- 1b. (g threads) block-level decays from the strip sums:
-    //          EB[a] = e^{Gam_16a}, EN[a] = e^{Gam_{C-1} - Gam_16a},
-    //          BT[a][b] = e^{Gam_16a - Gam_16b} (b < a), e^{Gam_n} to the workspace;
-    //          (all threads) R = e^{Gam_r - Gam_16a} from the strip-local sums
-    //          (Gam_r - Gam_16a = L_r - L_16a, L_16a = the strip's first g) and
-    //          the MFMA-ready factors, in place: q^ <- q^ R, k^ <- k^ R,
-    //          L <- k^ / R (all finite, see header).
+    // ---- 1b. (g threads) block decays, each the exponential of a sum of
+    //          decays over the tokens it spans (first, rest: a block's first
+    //          decay and the sum of its other 15): EB[a] = e^{Gam_m(a)},
+    //          EN[a] = e^{Gam_{C-1} - Gam_e(a)} over the later blocks,
+    //          BT[a][b] = e^{Gam_m(a) - Gam_e(b)} over the gap (b < a), and
+    //          e^{Gam_n} to the workspace.
+    //          (all threads) the pair terms inside each diagonal 16 x 16 block
+    //          explicitly: task (block a, row i, channel group cg) walks the
+    //          distance d = 0..15 keeping G = prod of e^{g} over tokens
+    //          r-d+1 .. r (r = 16a + i) for its channels cg + 16u, and the 16
+    //          lanes of a row sum over channels; lane cg keeps distance cg.
+    constexpr int NDT = (NRB * 256 + kPrepNT - 1) / kPrepNT;  // tasks per thread
+    constexpr int NCPT = DK / 16;                             // channels per task
+    float dA[NDT], dP[NDT];
     if (role == 3) {
-      float off[4] = {0.f, 0.f, 0.f, 0.f}, last[4] = {0.f, 0.f, 0.f, 0.f};
-      float gm[NRB][4];
-      float run[4] = {0.f, 0.f, 0.f, 0.f};
+      f32x4 fst[NRB], rst[NRB];
 #pragma unroll
-      for (int s2 = 0; s2 < NRB; ++s2)
+      for (int b2 = 0; b2 < NRB; ++b2) {
+        fst[b2] = *reinterpret_cast<const f32x4*>(&sFirst[b2][gc0]);
+        rst[b2] = *reinterpret_cast<const f32x4*>(&sTot[b2][gc0]);
+      }
+      f32x4 before = {0.f, 0.f, 0.f, 0.f}, after = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float tot = sTot[s2][gc0 + e];
-          gm[s2][e] = run[e] + sFirst[s2][gc0 + e];  // Gam at block start 16*s2
-          if (s2 < gs) off[e] += tot;
-          run[e] += tot;
-          last[e] += tot;
-        }
-      float g0[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) g0[e] = gm[gs][e];
-      (void)off;
+      for (int b2 = 0; b2 < NRB; ++b2) {
+        if (b2 < gs) before += fst[b2] + rst[b2];
+        if (b2 > gs) after += fst[b2] + rst[b2];
+      }
       f32x4 eb, en;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        eb[e] = __expf(g0[e]);
-        en[e] = __expf(last[e] - g0[e]);
+        eb[e] = __expf(before[e] + fst[gs][e]);
+        en[e] = __expf(after[e]);
       }
       *reinterpret_cast<f32x4*>(&sEB[gs][gc0]) = eb;
       *reinterpret_cast<f32x4*>(&sEN[gs][gc0]) = en;
+      f32x4 gap = fst[gs];
 #pragma unroll
-      for (int b2 = 0; b2 < NRB; ++b2) {
+      for (int b2 = NRB - 1; b2 >= 0; --b2) {
         if (b2 < gs) {
           f32x4 bt;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bt[e] = __expf(g0[e] - gm[b2][e]);
+          for (int e = 0; e < 4; ++e) bt[e] = __expf(gap[e]);
           *reinterpret_cast<f32x4*>(&sBT[gs * (gs - 1) / 2 + b2][gc0]) = bt;
+          gap += rst[b2] + fst[b2];
         }
       }
       if (gs == 0) {
-        f32x4 dn;
+        f32x4 all = {0.f, 0.f, 0.f, 0.f}, dn;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dn[e] = __expf(last[e]);
+        for (int b2 = 0; b2 < NRB; ++b2) all += fst[b2] + rst[b2];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dn[e] = __expf(all[e]);
         *reinterpret_cast<f32x4*>(Dn + gc0) = dn;
       }
     }
-    for (int idx = tid; idx < C * (DK / 4); idx += kPrepNT) {
-      const int r = idx / (DK / 4), c0 = 4 * (idx % (DK / 4));
-      f32x4* pr = reinterpret_cast<f32x4*>(&sR[r][c0]);
-      f32x4* pk = reinterpret_cast<f32x4*>(&sK[r][c0]);
-      f32x4* pq = reinterpret_cast<f32x4*>(&sQ[r][c0]);
-      const f32x4 lr = *pr, lm = *reinterpret_cast<const f32x4*>(&sFirst[r / 16][c0]);
-      const f32x4 kv = *pk;
-      f32x4 rv, kc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        rv[e] = __expf(lr[e] - lm[e]);
-        kc[e] = kv[e] * __expf(lm[e] - lr[e]);
+    for (int u = 0; u < NDT; ++u) {
+      dA[u] = dP[u] = 0.f;
+      const int task = tid + u * kPrepNT;
+      if (task < NRB * 256) {  // whole waves take part or not
+        const int ab = task / 256, i = (task / 16) % 16, cg = task % 16;
+        const int r = 16 * ab + i;
+        float kr[NCPT], qr[NCPT], G[NCPT];
+#pragma unroll
+        for (int w = 0; w < NCPT; ++w) {
+          kr[w] = sK[r][cg + 16 * w];
+          qr[w] = sQ[r][cg + 16 * w];
+          G[w] = 1.f;
+        }
+        for (int d = 0; d < 16; ++d) {
+          const int j = max(r - d, 16 * ab), jn = max(r - d + 1, 16 * ab + 1);
+          float ta = 0.f, tp = 0.f;
+#pragma unroll
+          for (int w = 0; w < NCPT; ++w) {
+            if (d > 0) G[w] *= __expf(sR[jn][cg + 16 * w]);
+            const float kg = sK[j][cg + 16 * w] * G[w];
+            ta += kr[w] * kg;
+            tp += qr[w] * kg;
+          }
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            ta += __shfl_xor(ta, off, kWave);
+            tp += __shfl_xor(tp, off, kWave);
+          }
+          if (cg == d) {
+            dA[u] = ta;
+            dP[u] = tp;
+          }
+        }
       }
-      *pq = *pq * rv;
-      *pk = kv * rv;
-      *pr = kc;
     }
     __syncthreads();
-    // from here on: sQ = q^ R, sK = k^ R, sR = k^ / R
+
+    // ---- 1c. (g threads) the row factors R = e^{Gam_r - Gam_m} and column
+    //          factors E = e^{Gam_e - Gam_r} of the strip's tokens (m, e =
+    //          the block's first and last token), as sums of the decays
+    //          between, applied in place: q^ <- q^ R, k^ <- k^ R and the
+    //          R region <- k^ E. (all threads) the diagonal blocks' pair
+    //          terms: beta_r A_rj (j < r) to sL, P_rj (j <= r, zero above)
+    //          to the workspace.
+    if (role == 3) {
+      f32x4 gv[GS];
+#pragma unroll
+      for (int r = 0; r < GS; ++r) gv[r] = *reinterpret_cast<const f32x4*>(&sR[GS * gs + r][gc0]);
+      f32x4 run = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < GS; ++r) {  // R: decays of tokens m+1 .. r
+        if (r > 0) run += gv[r];
+        f32x4 rv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[e] = __expf(run[e]);
+        f32x4* pq = reinterpret_cast<f32x4*>(&sQ[GS * gs + r][gc0]);
+        f32x4* pk = reinterpret_cast<f32x4*>(&sK[GS * gs + r][gc0]);
+        *pq = *pq * rv;
+        gv[r] = *pk;             // k^ of token r, for E below
+        *pk = gv[r] * rv;
+      }
+      run = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = GS - 1; r >= 0; --r) {  // E: decays of tokens r+1 .. e
+        f32x4 ev;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ev[e] = __expf(run[e]);
+        f32x4* pr = reinterpret_cast<f32x4*>(&sR[GS * gs + r][gc0]);
+        run += *pr;              // the decay of token r (still in place)
+        *pr = gv[r] * ev;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NDT; ++u) {
+      const int task = tid + u * kPrepNT;
+      if (task < NRB * 256) {
+        const int ab = task / 256, i = (task / 16) % 16, d = task % 16;
+        const int r = 16 * ab + i;
+        if (d <= i) {
+          if (d > 0) sL[r][r - d] = sB[r] * dA[u];
+          blk[L::oP + (size_t)r * CP + (r - d)] = (MT)dP[u];
+        } else {
+          blk[L::oP + (size_t)r * CP + (r + d - i)] = (MT)0.f;
+        }
+      }
+    }
+    __syncthreads();
+    // from here on: sQ = q^ R, sK = k^ R, sR = k^ E
 
     // ---- 2. A (beta-scaled, strictly lower) to LDS and P (lower) to the
-    //         workspace: tile (a, bc <= a) on MFMA; row factors k^ R, q^ R,
-    //         column factors k^ / R scaled by BT[a][bc] = e^{Gam_16a - Gam_16bc}
+    //         workspace: the tiles (a, bc < a) on MFMA; row factors k^ R,
+    //         q^ R, column factors k^ E scaled by BT[a][bc] = e^{Gam_m(a) - Gam_e(bc)}
     {
       constexpr int NKS = DKP / KS;
-      constexpr int NTILE = NRB * (NRB + 1) / 2;
+      constexpr int NTILE = NRB * (NRB - 1) / 2;
       for (int tile = wv; tile < NTILE; tile += kPrepNW) {
-        int arb = 0, rem = tile;
-        while (rem > arb) { rem -= arb + 1; ++arb; }
+        int arb = 1, rem = tile;
+        while (rem >= arb) { rem -= arb; ++arb; }
         const int bc = rem;
         const int r = 16 * arb + l16, j = 16 * bc + l16;
-        const float* bt = bc < arb ? &sBT[arb * (arb - 1) / 2 + bc][0] : nullptr;
+        const float* bt = &sBT[arb * (arb - 1) / 2 + bc][0];
         f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -421,12 +503,10 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
             lds_rd(&sK[r][c0], vk);
             lds_rd(&sQ[r][c0], vq);
             lds_rd(&sR[j][c0], vc);
-            if (bt) {
-              float bv[KPL];
-              lds_rd(bt + c0, bv);
+            float bv[KPL];
+            lds_rd(bt + c0, bv);
 #pragma unroll
-              for (int e = 0; e < KPL; ++e) vc[e] *= bv[e];
-            }
+            for (int e = 0; e < KPL; ++e) vc[e] *= bv[e];
           } else {
 #pragma unroll
             for (int e = 0; e < KPL; ++e) vk[e] = vq[e] = vc[e] = 0.f;
@@ -451,7 +531,7 @@ __global__ __launch_bounds__(kPrepNT) void prefill_prep_kernel(PrefillArgs a, in
       }
     }
 
-    // ---- 3. Q~ = e^{Gam_16a} (q^ R) and K^^T = e^{Gam_n - Gam_16a} (k^ / R)
+    // ---- 3. Q~ = e^{Gam_m(a)} (q^ R) and K^^T = e^{Gam_n - Gam_e(a)} (k^ E)
     //         (fragment-major) to the workspace ------------------------
     {
       constexpr int NPQ = C * DKP / KPL;

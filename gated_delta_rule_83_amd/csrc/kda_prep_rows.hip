@@ -22,6 +22,22 @@
 // four consecutive tokens of one channel per lane, exactly, and two lanes
 // (l and l^16) pair up into one 16-byte fragment piece.
 //
+// Decayed pair terms without overflow, for any g <= 0 (-inf included). The
+// factor e^{Gam_r - Gam_j} of a pair j <= r (r in 16-token block a, j in
+// block b) is the product of a row factor R_r = e^{Gam_r - Gam_m(a)} <= 1
+// (m = a block's first token, e = its last), a column factor and a block
+// factor, chosen per column block b:
+//   - narrow b (no key channel decays by more than kSpan over its last 15
+//     tokens): column factor 1/R_j <= e^{kSpan}, block factor
+//     e^{Gam_m(a) - Gam_m(b)} (b < a) or 1 (b = a);
+//   - wide b: column factor E_j = e^{Gam_e(b) - Gam_j} <= 1 and block factor
+//     e^{Gam_m(a) - Gam_e(b)} <= 1 (b < a); its diagonal tile is formed by
+//     the block's wave in fp32, as sums over channels of k_r k_j (or q_r k_j)
+//     times the running product of e^{g} over tokens j+1 .. r along the DPP
+//     row.
+// All factors stay within e^{+-kSpan}, and every exponent is a sum of decays
+// of one sign, so no cancellation loses precision when one decay is large.
+//
 // LDS holds only what crosses waves (45 KiB at C = 64, d = 128, in three
 // regions reused from phase to phase) and the kernel is held to 168 VGPRs,
 // so three items share a CU and one item's loads overlap another's math.
@@ -49,6 +65,55 @@ __device__ __forceinline__ float dppf(float old, float src) {
   return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(unsigned, old),
                                              __builtin_bit_cast(unsigned, src)));
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp0f(float src) {
+  return __builtin_bit_cast(float, dpp0<CTRL>(__builtin_bit_cast(unsigned, src)));
+}
+
+// Largest decay over a block's last 15 tokens (natural log) for which the
+// block keeps the column factors 1/R (and its diagonal tile the factored MFMA
+// product): the factors then stay within e^{+-kSpan}, far inside the bf16 /
+// fp32 range.
+constexpr float kSpan = 64.0f;
+
+// Pair terms of a diagonal 16 x 16 tile for the eight channels of one
+// slice, distances D0 .. min(D0 + 7, 15): lane i of a DPP row holds token i
+// (k, the row-side operand x = k or q, and a = e^{g}). Stepping the distance
+// D by one shifts two running values one lane along the row: kj becomes k of
+// token i - D, and G = a_i * (G of lane i - 1) the product of a over tokens
+// i - D + 1 .. i; sum_c x_i kj G is added to acc[D - D0]. Lanes i < D see
+// zeros shifted in from outside the row; their sums are not used.
+template <int D0, int NE>
+__device__ __forceinline__ void diag_terms(const float* k, const float* x, const float* av,
+                                           float (&acc)[8]) {
+  float kj[NE], G[NE];
+  if constexpr (D0 == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) t += x[e] * k[e];
+    acc[0] += t;
+  }
+#pragma unroll
+  for (int e = 0; e < NE; ++e) kj[e] = k[e];
+#pragma unroll
+  for (int D = 1; D < 16 && D < D0 + 8; ++D) {
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      kj[e] = dpp0f<kRowShr + 1>(kj[e]);
+      G[e] = D == 1 ? av[e] : av[e] * dpp0f<kRowShr + 1>(G[e]);
+      t += x[e] * (kj[e] * G[e]);
+    }
+    // one distance at a time: the sum is formed here and the running values
+    // pass through, so no step's shifted copies stay live for later
+#pragma unroll
+    for (int e = 0; e < NE; ++e) asm volatile("" : "+v"(kj[e]), "+v"(G[e]));
+    asm volatile("" : "+v"(t));
+    if (D >= D0) acc[D - D0] += t;
+  }
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // element e of eight packed bf16 (exact)
 __device__ __forceinline__ float bfe(const u32x4& w, int e) {
@@ -79,11 +144,13 @@ struct RowsSmem {
       mx(mx((size_t)NWQ * 16, (size_t)C * LDC * 4), (size_t)DV * LDT * 2);
   // C: the raw inputs of the three tokens before each block ([NRB][3][NCH]
   //    bf16) -> block decays EB[a] = e^{Gam_m(a)}, EN[a] = e^{Gam_n - Gam_m(a)}
-  //    and BT[a][b] = e^{Gam_m(a) - Gam_m(b)} (b < a), fp32 [.][DK] -> X as bf16
+  //    (narrow a) or e^{Gam_n - Gam_e(a)} (wide a), BT[a][b] (b < a; row
+  //    a(a-1)/2 + b) = e^{Gam_m(a) - Gam_m(b)} (narrow b) or
+  //    e^{Gam_m(a) - Gam_e(b)} (wide b), fp32 [.][DK] -> X as bf16
   static constexpr size_t nC = mx(mx((size_t)NRB * 3 * NCH * 2, (size_t)(2 * NRB + NBT) * DK * 4),
                                   (size_t)C * LDT * 2);
-  static constexpr size_t oB = nA, oC = oB + nB;
-  static constexpr size_t bytes = oC + nC;
+  static constexpr size_t oB = nA, oC = oB + nB, oF = oC + nC;  // F: a wide flag per block
+  static constexpr size_t bytes = oF + 16;
 };
 
 // (launch bounds: C/16 waves, at least three waves per SIMD, i.e. three
@@ -117,6 +184,7 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   float (*sEB)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oC);
   float (*sEN)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oC + (size_t)NRB * DK * 4);
   float (*sBT)[DK] = reinterpret_cast<float (*)[DK]>(smem + SM::oC + (size_t)2 * NRB * DK * 4);
+  int* sWide = reinterpret_cast<int*>(smem + SM::oF);
 
   const int tid = threadIdx.x, lane = tid % kWave, rb = tid / kWave;
   const int i = lane % 16, gq = lane / 16;
@@ -142,6 +210,30 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   constexpr float kEps = CONV ? kL2Eps / (kLn2 * kLn2) : kL2Eps;
   bf16* blk = reinterpret_cast<bf16*>(ws + ((size_t)cl * a.B * H + (size_t)b * H + h) * L::bytes);
   float* Dn = reinterpret_cast<float*>(blk + L::nT);
+  // the lane's eight log-decays of slice s as the recurrence applies them
+  // (formed from the raw projection with RAW), 0 past the last token
+  // (NE = 8: the slice's eight channels; NE = 4: channels 4 h4 .. 4 h4 + 3)
+  auto load_decay = [&](int s, int h4, auto nec, float* x) __attribute__((always_inline)) {
+    constexpr int NE = decltype(nec)::value;
+    if constexpr (SG) {
+      const float gv = a.g[row];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) x[e] = gv;
+    } else {
+      const float* gp = a.g + row * DK + 32 * s + 8 * gq + 4 * h4;
+#pragma unroll
+      for (int u = 0; u < NE / 4; ++u) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(gp + 4 * u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * u + e] = w[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      if constexpr (RAW) x[e] = log_sigmoid(x[e]);
+      x[e] = valid ? x[e] : 0.f;
+    }
+  };
 
   // ---- 0. loads: conv weights of the head (to LDS), then the lane's token
   //         (q, k, v, g, beta); the conv history of each block to LDS: the
@@ -236,6 +328,7 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   //          the rest to LDS ------------------------------------------------
   if constexpr (RAW) betav = sigmoid(betav);  // raw projection: beta formed here
   float R[NKS][8];
+  bool wide = false;
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
     float p[8];
@@ -271,8 +364,14 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
     if (i == 15) {
       *reinterpret_cast<f32x4*>(&sTot[rb][32 * s + 8 * gq]) = f32x4{p[0], p[1], p[2], p[3]};
       *reinterpret_cast<f32x4*>(&sTot[rb][32 * s + 8 * gq + 4]) = f32x4{p[4], p[5], p[6], p[7]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wide |= !(p[e] >= -kSpan);
     }
   }
+  // this wave's block decays by more than kSpan on some channel (or by -inf):
+  // it is wide (wave-uniform; the other waves read it after the barrier)
+  const bool explicit_diag = __builtin_amdgcn_ballot_w64(wide) != 0;
+  if (lane == 0) sWide[rb] = explicit_diag;
   if constexpr (CONV) __syncthreads();  // conv weights and history visible
 
   // ---- 1a. q, k, v: short conv + SiLU (taps by row shifts), L2 of q, k ----
@@ -352,25 +451,128 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   }
   __syncthreads();
 
-  // ---- 1b. block decays from Gam at each block's first token,
-  //          Gam_m(a) = sum_{b < a} (first + rest)[b] + first[a], and at the
-  //          chunk's last token (Gam_n; e^{Gam_n} also to the workspace) -----
+  // ---- 1b. block decays, each the exponential of a sum of decays over the
+  //          tokens it spans (first[a] = g of block a's first token, rest[a]
+  //          = the sum over its other 15): EB[a] = e^{Gam_m(a)}; EN[a] over
+  //          the tokens after block a's first (narrow a) or last (wide a)
+  //          token; BT[a][b] (b < a) over the tokens after block b's first
+  //          (narrow b) or last (wide b) token up to block a's first;
+  //          e^{Gam_n} to the workspace
   for (int c = tid; c < DK; c += NT) {
-    float gm[NRB], cum = 0.f;
+    float fst[NRB], rst[NRB];
+    bool wd[NRB];
 #pragma unroll
     for (int bb = 0; bb < NRB; ++bb) {
-      const float f = sFirst[bb][c];
-      gm[bb] = cum + f;
-      cum += f + sTot[bb][c];
+      fst[bb] = sFirst[bb][c];
+      rst[bb] = sTot[bb][c];
+      wd[bb] = sWide[bb] != 0;
     }
+    float cum = 0.f;
 #pragma unroll
     for (int bb = 0; bb < NRB; ++bb) {
-      sEB[bb][c] = __expf(gm[bb]);
-      sEN[bb][c] = __expf(cum - gm[bb]);
-#pragma unroll
-      for (int b2 = 0; b2 < bb; ++b2) sBT[bb * (bb - 1) / 2 + b2][c] = __expf(gm[bb] - gm[b2]);
+      sEB[bb][c] = __expf(cum + fst[bb]);
+      cum += fst[bb] + rst[bb];
     }
     Dn[c] = __expf(cum);
+    float later = 0.f;
+#pragma unroll
+    for (int bb = NRB - 1; bb >= 0; --bb) {
+      sEN[bb][c] = __expf(wd[bb] ? later : later + rst[bb]);
+      later += fst[bb] + rst[bb];
+    }
+#pragma unroll
+    for (int bb = 1; bb < NRB; ++bb) {
+      float gap = fst[bb];
+#pragma unroll
+      for (int b2 = bb - 1; b2 >= 0; --b2) {
+        sBT[bb * (bb - 1) / 2 + b2][c] = __expf(wd[b2] ? gap : gap + rst[b2]);
+        gap += rst[b2] + fst[b2];
+      }
+    }
+  }
+
+  // ---- 1b'. a wave whose block decays past kSpan forms its diagonal tile
+  //           here, in fp32, from the unscaled q^, k^ and e^{g} (reloaded):
+  //           beta_r A_rj (j < r) to sL[r][j] and P_rj (j <= r) transposed to
+  //           sL[j][r]; the inverse reads only the strictly lower part ------
+  if (explicit_diag) {
+    // Room for the passes below: R (as fp16) and the beta v^ pieces wait in
+    // this wave's rows of the -W and U' blocks of the workspace, which only
+    // this wave writes, and only in step 4 (4 * NKS and 4 * NVS dwords per lane).
+    unsigned* rpark = reinterpret_cast<unsigned*>(blk + L::oW + (size_t)rb * NKS * kWave * 8) +
+                      (size_t)lane * NKS * 4;
+    unsigned* vpark = reinterpret_cast<unsigned*>(blk + L::oU + (size_t)rb * (DV / 16) * kWave * 4) +
+                      (size_t)lane * NVS * 4;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      u32x4 w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        w[u] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(R[s][2 * u], R[s][2 * u + 1]));
+      reinterpret_cast<u32x4*>(rpark)[s] = w;
+    }
+#pragma unroll
+    for (int s = 0; s < NVS; ++s) reinterpret_cast<u32x4*>(vpark)[s] = __builtin_bit_cast(u32x4, vb[s]);
+    asm volatile("" ::: "memory");
+    // four passes of eight distances (A: 1..8, 9..15; P: 0..7, 8..15), each
+    // summed over the slices, reduced over the lane's four channel groups
+    // and stored, so that only eight sums are live at a time
+    auto pass = [&](auto d0c, auto isp) __attribute__((always_inline)) {
+      constexpr int D0 = decltype(d0c)::value;
+      constexpr bool ISP = decltype(isp)::value;
+      float acc[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+#pragma unroll
+        for (int h4 = 0; h4 < 2; ++h4) {  // four channels at a time
+          // opaque copies, so that the passes do not share (and keep alive)
+          // one another's shifted values
+          float av[4], kk[4], xx[4];
+          load_decay(s, h4, std::integral_constant<int, 4>{}, av);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kk[e] = kf[s][4 * h4 + e];
+            xx[e] = ISP ? qf[s][4 * h4 + e] : kf[s][4 * h4 + e];
+            asm volatile("" : "+v"(av[e]), "+v"(kk[e]), "+v"(xx[e]));
+            av[e] = __expf(av[e]);
+          }
+          diag_terms<D0, 4>(kk, xx, av, acc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one slice's decays at a time
+      }
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        acc[dd] += __shfl_xor(acc[dd], 16, kWave);
+        acc[dd] += __shfl_xor(acc[dd], 32, kWave);
+        const int d = D0 + dd;
+        if (d < 16 && d % 4 == gq && d <= i) {
+          if constexpr (ISP) sL[r - d][r] = acc[dd];
+          else sL[r][r - d] = betav * acc[dd];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // passes one after the other
+    };
+    pass(std::integral_constant<int, 1>{}, std::false_type{});
+    pass(std::integral_constant<int, 9>{}, std::false_type{});
+    pass(std::integral_constant<int, 0>{}, std::true_type{});
+    pass(std::integral_constant<int, 8>{}, std::true_type{});
+    asm volatile("" ::: "memory");  // read back what was parked, not a forwarded copy
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const u32x4 w = reinterpret_cast<const u32x4*>(rpark)[s];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const unsigned wu = w[u];  // (a bit_cast of the vector element itself reads element 0)
+        const f16x2 hv = __builtin_bit_cast(f16x2, wu);
+        R[s][2 * u] = (float)hv[0];
+        R[s][2 * u + 1] = (float)hv[1];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NVS; ++s) vb[s] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(vpark)[s]);
   }
   __syncthreads();
 
@@ -382,21 +584,41 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
     for (int e = 0; e < 8; ++e) sel[hf][e] = (bf16)(8 * gq + e == i + 16 * hf ? 1.f : 0.f);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // ---- 1c. per slice: Q~ = e^{Gam} q^ and K^^T = e^{Gam_n - Gam} k^ to the
-  //          workspace, k^/R to LDS; q^ <- q^ R and k^ <- k^ R (the Gram
-  //          row factors). A barrier first: sKi overwrites the block sums ---
+  // ---- 1c. per slice: the column factor E = 1/R (narrow block) or
+  //          e^{Gam_e - Gam_r} from a row scan of the decays after the token
+  //          (wide); Q~ = e^{Gam} q^ = EB (q^ R) and K^^T = e^{Gam_n - Gam} k^
+  //          = EN (k^ E) to the workspace, k^ E to LDS; q^ <- q^ R and
+  //          k^ <- k^ R (the Gram row factors). The barrier above also
+  //          orders sKi after the block sums it overwrites -----------------
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
     const f32x4* pb = reinterpret_cast<const f32x4*>(&sEB[rb][32 * s + 8 * gq]);
     const f32x4* pn = reinterpret_cast<const f32x4*>(&sEN[rb][32 * s + 8 * gq]);
     const f32x4 b0 = pb[0], b1 = pb[1], n0 = pn[0], n1 = pn[1];
+    float E[8];
+    if (explicit_diag) {
+      float x[8];
+      load_decay(s, 0, std::integral_constant<int, 8>{}, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // decays of tokens i+1 .. 15 of the block
+        x[e] = dpp0f<kRowShl + 1>(x[e]);
+        x[e] += dpp0f<kRowShl + 1>(x[e]);
+        x[e] += dpp0f<kRowShl + 2>(x[e]);
+        x[e] += dpp0f<kRowShl + 4>(x[e]);
+        x[e] += dpp0f<kRowShl + 8>(x[e]);
+        E[e] = __expf(x[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) E[e] = __builtin_amdgcn_rcpf(R[s][e]);
+    }
     float qt[8], ki[8], kh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float eb = e < 4 ? b0[e] : b1[e - 4], en = e < 4 ? n0[e] : n1[e - 4];
       const float rr = R[s][e];
       const float qr = qf[s][e] * rr, kr = kf[s][e] * rr;
-      ki[e] = kf[s][e] * __builtin_amdgcn_rcpf(rr);
+      ki[e] = kf[s][e] * E[e];
       qt[e] = eb * qr;
       kh[e] = en * ki[e];
       qf[s][e] = qr;
@@ -416,9 +638,10 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
   __syncthreads();
 
   // ---- 2. Gram tiles of this wave's block row, transposed: the product of
-  //         A operand k^/R of block bc (LDS) and B operand (k^ R), (q^ R) of
+  //         A operand k^ E of block bc (LDS) and B operand (k^ R), (q^ R) of
   //         this wave's tokens, scaled by BT[rb][bc] for bc < rb, is the
-  //         tile (rows j of block bc, columns r of block rb) of A^T and P^T.
+  //         tile (rows j of block bc, columns r of block rb) of A^T and P^T
+  //         (the diagonal tile of a wide block comes from sL, formed in 1b').
   //         Lane (l%16, l/16) then holds A_rj, P_rj for r = 16rb + l%16 and
   //         j = 16bc + 4(l/16) + e: beta_r A_rj (strictly lower) goes to
   //         LDS as one 16-byte row piece, P (lower) to the workspace as
@@ -432,38 +655,49 @@ __global__ __launch_bounds__(C * 4, 3) void prefill_prep_rows_kernel(PrefillArgs
     for (int bc = 0; bc < NRB; ++bc) {
       f32x4 accA = zero4, accP = zero4;
       if (bc <= rb) {
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          const bf16x8 fa =
-              *reinterpret_cast<const bf16x8*>(sKi + ((size_t)(bc * NKS + s) * kWave + lane) * 8);
-          float bk[8], bqv[8];
-          if (bc < rb) {
-            const f32x4* pb = reinterpret_cast<const f32x4*>(
-                &sBT[rb * (rb - 1) / 2 + bc][32 * s + 8 * gq]);
-            const f32x4 t0v = pb[0], t1v = pb[1];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float sc = e < 4 ? t0v[e] : t1v[e - 4];
-              bk[e] = kf[s][e] * sc;
-              bqv[e] = qf[s][e] * sc;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              bk[e] = kf[s][e];
-              bqv[e] = qf[s][e];
-            }
-          }
-          accA = M::mma(fa, to_bf16x8(bk), accA);
-          accP = M::mma(fa, to_bf16x8(bqv), accP);
-          __builtin_amdgcn_sched_barrier(0);
-        }
         f32x4 la;
+        if (bc == rb && explicit_diag) {
+          // reads of this wave's own 1b' values, before its stores below
+          const f32x4 fa4 = *reinterpret_cast<const f32x4*>(&sL[r][16 * bc + 4 * gq]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int jj = 16 * bc + 4 * gq + e;
-          la[e] = jj < r ? betav * accA[e] : 0.f;
-          accP[e] = jj <= r ? accP[e] : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int jj = 16 * bc + 4 * gq + e;
+            la[e] = jj < r ? fa4[e] : 0.f;
+            accP[e] = jj <= r ? sL[jj][r] : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) {
+            const bf16x8 fa =
+                *reinterpret_cast<const bf16x8*>(sKi + ((size_t)(bc * NKS + s) * kWave + lane) * 8);
+            float bk[8], bqv[8];
+            if (bc < rb) {
+              const f32x4* pb = reinterpret_cast<const f32x4*>(
+                  &sBT[rb * (rb - 1) / 2 + bc][32 * s + 8 * gq]);
+              const f32x4 t0v = pb[0], t1v = pb[1];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float sc = e < 4 ? t0v[e] : t1v[e - 4];
+                bk[e] = kf[s][e] * sc;
+                bqv[e] = qf[s][e] * sc;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                bk[e] = kf[s][e];
+                bqv[e] = qf[s][e];
+              }
+            }
+            accA = M::mma(fa, to_bf16x8(bk), accA);
+            accP = M::mma(fa, to_bf16x8(bqv), accP);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int jj = 16 * bc + 4 * gq + e;
+            la[e] = jj < r ? betav * accA[e] : 0.f;
+            accP[e] = jj <= r ? accP[e] : 0.f;
+          }
         }
         *reinterpret_cast<f32x4*>(&sL[r][16 * bc + 4 * gq]) = la;
       }

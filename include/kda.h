@@ -88,9 +88,8 @@ typedef struct {
                               the kernels form the decay g = log(sigmoid(a)) (alpha =
                               sigmoid(a) in (0, 1)) and beta = sigmoid(b) themselves.
                               Combines with KDA_F_SCALAR_G (then a is [B][T][H]).
-                              For kda_chunk_prefill the decay so formed must meet
-                              that call's precondition on g (a of -5 or more per
-                              token always does).
+                              Any a that is not NaN is accepted (a = -inf gives
+                              g = -inf: the rows are cleared).
                               Source: "为什么 Kimi K3 敢把 KV Cache 扔掉？…", section 6:
                               the Alpha/Beta projection sets the forgetting and update
                               strengths, alpha in [0, 1]; the squashing by a sigmoid
@@ -179,9 +178,12 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chun
  * current S and ring and leaving them at token T (same result as T decode
  * steps up to rounding).
  *  q, k: [B][T][H][d_k] raw (io dtype); v: [B][T][H][d_v].
- *  g:    [B][T][H][d_k] fp32; precondition: finite and <= 0, and on every key
- *        channel the sum of g over any 16 consecutive tokens is >= -80
- *        (the intra-chunk decay factors must stay inside the fp32 range).
+ *  g:    [B][T][H][d_k] fp32; precondition: g <= 0 and not NaN. Any such
+ *        value is handled, -inf included (it clears the rows, as in a
+ *        decode step): every decay factor the kernels form is the
+ *        exponential of a sum of decays of one sign, bounded by 1, except
+ *        the factored diagonal tiles of 16-token blocks whose decay stays
+ *        within 64 on every key channel (others are formed term by term).
  *        [B][T][H] with KDA_F_SCALAR_G (same precondition).
  *  beta: [B][T][H] fp32.  conv_w: [Ctot][4] fp32.
  *  o:    [B][T][H][d_v] io dtype (written).

@@ -1,8 +1,9 @@
 """Degenerate inputs of the recurrence on the GPU, decode and prefill, against
 the fp64 oracle: no update (beta = 0), full update with q = k (exact recall),
-no decay (g = 0) over many chunks, the strongest decay the prefill accepts
-(every 16-token run of g summing to -78.4), and all-zero q, k, v (the L2
-step then divides 0 by sqrt(eps)).
+no decay (g = 0) over many chunks, a strong decay (-4.9 per token: 16-token
+blocks decay by 73.5, past the factored diagonal tiles' limit, so those are
+formed term by term), and all-zero q, k, v (the L2 step then divides 0 by
+sqrt(eps)). Stronger and infinite decays: test_strong_decay_gpu.py.
 
 Tolerances: fp32 max |err| <= 1e-4; bf16 max|err|/max|ref| <= 2e-2.
 """
