@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "kda_common.h"
@@ -317,11 +318,15 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chun
                                          dims->io);
 }
 
-kda_status kda_chunk_prefill(kda_state* stt, int32_t T, const void* q, const void* k,
-                             const void* v, const float* g, const float* beta,
-                             const float* conv_w, void* o, int32_t chunk, void* workspace,
-                             size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
-  g_err[0] = 0;
+namespace {
+
+// Validation shared by the prefill entry points; on success *per_chunk and
+// *nchunks give the workspace one chunk of all B*H chunk-heads needs and the
+// chunk count of the call.
+kda_status check_prefill(const kda_state* stt, int32_t T, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta, const float* conv_w,
+                         const void* o, int32_t chunk, uint32_t flags, size_t* per_chunk,
+                         size_t* nchunks) {
   if (!stt) return fail(KDA_ERR_INVALID, "state is NULL");
   kda_status st = check_flags(flags, kStepFlags);
   if (st != KDA_OK) return st;
@@ -329,6 +334,8 @@ kda_status kda_chunk_prefill(kda_state* stt, int32_t T, const void* q, const voi
   if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);
   if (chunk != 16 && chunk != 32 && chunk != 64)
     return fail(KDA_ERR_UNSUPPORTED, "chunk = %d: supported chunks are 16, 32, 64", chunk);
+  *per_chunk = kda::prefill_ws_bytes_per_chunk(d->heads, d->batch, d->d_k, d->d_v, chunk, d->io);
+  *nchunks = ((size_t)T + chunk - 1) / chunk;
   if (T == 0) return KDA_OK;
   const size_t esz = io_size(d->io);
   KDA_REQUIRE_PTR(q, "q", esz);
@@ -338,9 +345,39 @@ kda_status kda_chunk_prefill(kda_state* stt, int32_t T, const void* q, const voi
   KDA_REQUIRE_PTR(beta, "beta", 4);
   KDA_REQUIRE_PTR(o, "o", esz);
   if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
-  const size_t per_chunk =
-      kda::prefill_ws_bytes_per_chunk(d->heads, d->batch, d->d_k, d->d_v, chunk, d->io);
-  const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
+  return KDA_OK;
+}
+
+// The prefill itself, once the workspace is chosen: the chunked kernels,
+// then the ring advance.
+kda_status run_prefill(kda_state* stt, int32_t T, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* conv_w, void* o,
+                       int32_t chunk, void* workspace, size_t workspace_bytes, uint32_t flags,
+                       hipStream_t stream) {
+  const kda_dims* d = &stt->dims;
+  kda::PrefillArgs a{stt->S, stt->ring, q, k, v, g, beta, conv_w, o,
+                     d->batch, T, d->heads, d->d_k, d->d_v, chunk, flags};
+  hipError_t e = kda::launch_prefill(a, d->io, workspace, workspace_bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  if (!(flags & KDA_F_SKIP_CONV)) {
+    e = kda::launch_ring_advance(q, k, v, stt->ring, d->batch, T, d->heads, d->d_k, d->d_v,
+                                 d->io, stream);
+    if (e != hipSuccess) return hip_fail(e, "ring advance launch");
+  }
+  return KDA_OK;
+}
+
+}  // namespace
+
+kda_status kda_chunk_prefill(kda_state* stt, int32_t T, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta,
+                             const float* conv_w, void* o, int32_t chunk, void* workspace,
+                             size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+  g_err[0] = 0;
+  size_t per_chunk = 0, nchunks = 0;
+  kda_status st = check_prefill(stt, T, q, k, v, g, beta, conv_w, o, chunk, flags, &per_chunk,
+                                &nchunks);
+  if (st != KDA_OK || T == 0) return st;
   if (workspace) {
     if (!aligned16(workspace)) return fail(KDA_ERR_INVALID, "workspace is not 16-byte aligned");
     if (workspace_bytes < per_chunk)
@@ -363,16 +400,72 @@ kda_status kda_chunk_prefill(kda_state* stt, int32_t T, const void* q, const voi
     workspace = stt->ws;
     workspace_bytes = stt->ws_bytes;
   }
-  kda::PrefillArgs a{stt->S, stt->ring, q, k, v, g, beta, conv_w, o,
-                     d->batch, T, d->heads, d->d_k, d->d_v, chunk, flags};
-  hipError_t e = kda::launch_prefill(a, d->io, workspace, workspace_bytes, stream);
-  if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  if (!(flags & KDA_F_SKIP_CONV)) {
-    e = kda::launch_ring_advance(q, k, v, stt->ring, d->batch, T, d->heads, d->d_k, d->d_v,
-                                 d->io, stream);
-    if (e != hipSuccess) return hip_fail(e, "ring advance launch");
+  return run_prefill(stt, T, q, k, v, g, beta, conv_w, o, chunk, workspace, workspace_bytes,
+                     flags, stream);
+}
+
+// ---- allocation-free prefill ----------------------------------------------
+// The workspace of kda_chunk_prefill_noalloc: one fixed array per device,
+// loaded with the library's code object and held until the process ends.
+// Host code uses only the device address obtained for it below, never the
+// array's name (which on the host is a stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device
+
+// The device address of `scratch` on the device of `stream`, looked up once
+// per device (with that device current, as the call requires).
+kda_status scratch_for(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDevice_t sdev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
   }
+  if (sdev != cur)
+    return fail(KDA_ERR_INVALID, "the stream belongs to device %d but device %d is current",
+                (int)sdev, cur);
+  if (cur < 0 || cur >= kMaxDevices)
+    return fail(KDA_ERR_UNSUPPORTED, "device %d: at most %d devices", cur, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[cur]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static scratch");
+    if (!p) return fail(KDA_ERR_HIP, "hipGetSymbolAddress returned NULL for the static scratch");
+    g_scratch_ptr[cur] = p;
+  }
+  *out = g_scratch_ptr[cur];
   return KDA_OK;
+}
+
+}  // namespace
+
+kda_status kda_chunk_prefill_noalloc(kda_state* stt, int32_t T, const void* q, const void* k,
+                                     const void* v, const float* g, const float* beta,
+                                     const float* conv_w, void* o, int32_t chunk, uint32_t flags,
+                                     hipStream_t stream) {
+  g_err[0] = 0;
+  size_t per_chunk = 0, nchunks = 0;
+  kda_status st = check_prefill(stt, T, q, k, v, g, beta, conv_w, o, chunk, flags, &per_chunk,
+                                &nchunks);
+  if (st != KDA_OK || T == 0) return st;
+  if (per_chunk > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+    return fail(KDA_ERR_UNSUPPORTED,
+                "one chunk of %d sequences x %d heads needs %zu bytes of workspace, more than "
+                "the %zu-byte static scratch of kda_chunk_prefill_noalloc",
+                stt->dims.batch, stt->dims.heads, per_chunk, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_for(stream, &ws);
+  if (st != KDA_OK) return st;
+  return run_prefill(stt, T, q, k, v, g, beta, conv_w, o, chunk, ws,
+                     (size_t)KDA_NOALLOC_SCRATCH_BYTES, flags, stream);
 }
 
 size_t kda_backward_workspace_bytes(const kda_dims* d, int32_t T, int32_t chunk) {

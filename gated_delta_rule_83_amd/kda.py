@@ -18,11 +18,13 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_OOM = 0, -1, -2, -3, -4
 KDA_F32, KDA_BF16 = 0, 1
 KDA_F_SKIP_CONV, KDA_F_SKIP_L2, KDA_F_SCALAR_G, KDA_F_RAW_GATES = 1, 2, 4, 8
+KDA_NOALLOC_SCRATCH_BYTES = 64 << 20  # the fixed scratch of kda_chunk_prefill_noalloc
 
 EXPORTED = [
     "kda_state_bytes", "kda_state_alloc", "kda_state_reset", "kda_state_free",
     "kda_state_S", "kda_state_ring", "kda_state_get_dims", "kda_conv_prologue",
     "kda_decode_step", "kda_prefill_workspace_bytes", "kda_chunk_prefill",
+    "kda_chunk_prefill_noalloc",
     "kda_gated_rmsnorm", "kda_decode_step_gated", "kda_backward_workspace_bytes",
     "kda_chunk_backward", "kda_prologue_backward_workspace_bytes", "kda_prologue_backward",
     "kda_last_error", "kda_version",
@@ -69,6 +71,8 @@ def lib():
         "kda_prefill_workspace_bytes": (sz, [dp, i32, i32]),
         "kda_chunk_prefill": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz,
                                              u32, vp]),
+        "kda_chunk_prefill_noalloc": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                     u32, vp]),
         "kda_gated_rmsnorm": (ctypes.c_int, [dp, i32, vp, vp, vp, f32, vp, vp]),
         "kda_decode_step_gated": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
                                                  u32, vp]),
@@ -226,6 +230,18 @@ def kda_chunk_prefill(handle, T, q, k, v, g, beta, conv_w, o, chunk=64, workspac
         _ptr(g, "g", torch.float32), _ptr(beta, "beta", torch.float32),
         _ptr(conv_w, "conv_w", torch.float32), _ptr(o, "o", io), int(chunk),
         _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes), int(flags), _stream(stream)))
+
+
+def kda_chunk_prefill_noalloc(handle, T, q, k, v, g, beta, conv_w, o, chunk=64, flags=0,
+                              stream=None, io=None):
+    """kda_chunk_prefill with the library's fixed device scratch as the
+    workspace: the call allocates nothing (include/kda.h)."""
+    io = io or io_dtype(kda_state_get_dims(handle))
+    _check(lib().kda_chunk_prefill_noalloc(
+        handle, int(T), _ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io),
+        _ptr(g, "g", torch.float32), _ptr(beta, "beta", torch.float32),
+        _ptr(conv_w, "conv_w", torch.float32), _ptr(o, "o", io), int(chunk), int(flags),
+        _stream(stream)))
 
 
 def kda_backward_workspace_bytes(dims, T, chunk=64) -> int:

@@ -201,6 +201,31 @@ kda_status kda_chunk_prefill(kda_state* st, int32_t T, const void* q,
                              int32_t chunk, void* workspace, size_t workspace_bytes,
                              uint32_t flags, hipStream_t stream);
 
+/* Size of the fixed device scratch of kda_chunk_prefill_noalloc (64 MiB). */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* kda_chunk_prefill for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments and results as kda_chunk_prefill, without the
+ * workspace: the call neither allocates nor frees anything (no hipMalloc,
+ * hipFree or allocating library routine). Its workspace is a fixed array of
+ * KDA_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, held by the
+ * library from its first use on that GPU until the process ends; T is
+ * processed in as many segments as that array needs (one chunk of all
+ * B * H heads must fit: 74,240 bytes per head and sequence at chunk 64,
+ * d_k = d_v = 128, bf16, i.e. up to 904 of them).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one
+ * GPU (two streams, two threads) race and must not be issued. The array's
+ * contents on entry do not matter. The stream must belong to the current
+ * device.
+ * Errors: as kda_chunk_prefill, plus KDA_ERR_UNSUPPORTED when one chunk of
+ * the state's sequences and heads needs more than the array holds, and
+ * KDA_ERR_INVALID when the stream belongs to another device. */
+kda_status kda_chunk_prefill_noalloc(kda_state* st, int32_t T, const void* q, const void* k,
+                                     const void* v, const float* g, const float* beta,
+                                     const float* conv_w, void* o, int32_t chunk,
+                                     uint32_t flags, hipStream_t stream);
+
 /* Output gate after the readout: a gated RMSNorm of each (sequence, token,
  * head) row of d_v readout values,
  *   out = x / sqrt(mean over d_v of x^2 + eps) * norm_w * sigmoid(gate).
