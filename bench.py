@@ -20,8 +20,10 @@ the same with the gates formed in the kernels from raw projections
 and the output gate (gated RMSNorm of the readout: fused into the decode step,
 and as its own kernel on the prefill output) under "output_gate".
 Beside them: the latency of one K3-shape decode step (batch 1, fp32, warm and
-with the caches flushed) under "single_step", a plain 1 GiB device copy as
-the practical bandwidth ceiling ("copy_GBps", "roofline.frac_of_copy"), and
+with the caches flushed) under "single_step", the practical bandwidth ceiling
+of a state stream ("stream_ceiling": a non-temporal in-place read-modify-write
+of 1 GiB, kda_stream_rmw; "roofline.frac_of_stream_ceiling"; a plain torch
+copy beside it), and
 the fp64 oracle timed on the host (all cores and one core on the decode
 workload, all cores on the 4096-token prefill) under "cpu_baseline".
 One JSON line is printed.
@@ -69,10 +71,20 @@ def prefill_bytes(B, T, H, dk, dv, io_bytes=2, scalar_g=False):
 
 
 def prefill_flops(B, T, H, dk, dv, C):
-    """Algorithmic FLOPs of the chunked form per token-head: the three state
-    contractions (W S, Q~ S, K^T U: 6 dk dv), the intra-chunk matrices
-    (A and P, each C dk on average: 2 C dk), the WY products (W, U': C (dk+dv))
-    and P U (C dv), plus the triangular solve (C^2/3 per column pair)."""
+    """Algorithmic FLOPs of the chunked form per token-head, the count of the
+    hot-path scope table: the three state contractions (W S or K~ S, Q~ S,
+    K^T U: 6 d^2), the four triangular C x C by d products (A, P, T V or
+    T K~, P U: 4 C d, half of each dense product) and the triangular inverse
+    (C^2 / 3); d = dk = dv. 132,437 at d = 128, C = 64."""
+    d = dk
+    per = 6 * dk * dv + 4 * C * d + (C * C) // 3
+    return B * T * H * per
+
+
+def prefill_flops_as_built(B, T, H, dk, dv, C):
+    """The count the kernels' own products add up to per token-head (a coarser
+    average of the triangular products): 6 dk dv + 2 C dk (A, P) +
+    C (dk + dv) (W, U') + C dv (P U) + C^2 / 3."""
     per = 6 * dk * dv + 2 * C * dk + C * (dk + dv) + C * dv + (C * C) // 3
     return B * T * H * per
 
@@ -93,6 +105,13 @@ def backward_flops(B, T, H, dk, dv, C):
     return B * T * H * per
 
 
+def backward_forward_flops(B, T, H, dk, dv, C):
+    """The part of backward_flops that recomputes the forward (A and P, W and
+    U', U and the state update, the inverse)."""
+    per = 2 * C * dk + C * (dk + dv) + 4 * dk * dv + (C * C) // 3
+    return B * T * H * per
+
+
 def backward_bytes(B, T, H, dk, dv, io_bytes=2):
     """Compulsory bytes of one backward call: q^, k^, v^, dO and dq, dk, dv in
     the I/O type, g and dg fp32, beta and dbeta fp32, plus S0, dST and dS0."""
@@ -101,31 +120,130 @@ def backward_bytes(B, T, H, dk, dv, io_bytes=2):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-DECODE_SOURCES = ["gated_delta_rule_83_amd/csrc/kda_decode.hip",
-                  "gated_delta_rule_83_amd/csrc/kda_common.h"]
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+CSRC = "gated_delta_rule_83_amd/csrc/"
+# (file, first marker, last marker): the digest covers only the text the
+# kernel is built from; None markers = the whole file
+COMMON_DECODE_PART = (CSRC + "kda_common.h", "namespace kda {",
+                      "hipError_t launch_decode(")
+DECODE_SOURCES = [(CSRC + "kda_decode.hip", None, None), COMMON_DECODE_PART]
+PREFILL_SOURCES = [(CSRC + "kda_prep_rows.hip", None, None),
+                   (CSRC + "kda_prefill.hip", None, None),
+                   (CSRC + "kda_prefill.h", None, None),
+                   (CSRC + "kda_common.h", "namespace kda {", "hipError_t launch_prefill(")]
 
 
-def source_digest(paths):
+def source_digest(parts):
     import hashlib
 
     h = hashlib.sha256()
-    for rel in paths:
+    for rel, first, last in parts:
         with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+            text = f.read()
+        if first is not None:
+            a = text.index(first.encode())
+            b = text.index(last.encode(), a) + len(last)
+            text = text[a:b]
+        h.update(text)
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed FETCH_SIZE/WRITE_SIZE
-    counter runs, or None when the decode kernel's source changed since."""
+def measured_traffic(path, parts):
+    """The committed FETCH_SIZE/WRITE_SIZE record of a kernel, or None when
+    its source changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_digest") != source_digest(DECODE_SOURCES):
+    if rec.get("source_digest") != source_digest(parts):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
+
+
+def counter_means(csv_path, counter):
+    """Mean per dispatch of one counter, per (kernel name, grid size), from a
+    rocprofv3 counter-collection CSV (values of one dispatch summed over
+    instances)."""
+    import collections
+    import csv
+
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row.get("Kernel_Name") or row.get("Kernel-Name")
+            disp = row.get("Dispatch_Id") or row.get("Dispatch-Id")
+            per[(name, row.get("Grid_Size", ""))][disp] += float(row["Counter_Value"])
+    return {key: (sum(d.values()) / len(d), len(d)) for key, d in per.items()}
+
+
+def record_traffic(fetch_csv, write_csv, command):
+    """Writes profiles/decode_traffic.json and profiles/prefill_traffic.json
+    from the FETCH_SIZE and WRITE_SIZE counter runs of this benchmark
+    (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, each over
+    `python bench.py ... --no-stack --no-gdn --no-backward`). The counters
+    are scaled by what they read for kda_stream_rmw over 1 GiB in the same
+    runs (1 GiB read, 1 GiB written per dispatch)."""
+    fetch, write = counter_means(fetch_csv, "FETCH_SIZE"), counter_means(write_csv, "WRITE_SIZE")
+
+    def pick(table, *parts, grid=None):
+        hits = [(n, v) for (n, gs), v in table.items()
+                if all(p in n for p in parts) and (grid is None or gs == str(grid))]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {parts}, found {[n for n, _ in hits]}")
+        return hits[0]
+
+    gib_kib = float(1 << 20)
+    fscale = gib_kib / pick(fetch, "stream_rmw_kernel")[1][0]
+    wscale = gib_kib / pick(write, "stream_rmw_kernel")[1][0]
+    common = {"scale": "FETCH_SIZE x %.4f, WRITE_SIZE x %.4f (kda_stream_rmw over 1 GiB: "
+                       "1 GiB read and 1 GiB written per dispatch)" % (fscale, wscale),
+              "fetch_scale": fscale, "write_scale": wscale, "command": command}
+
+    def traffic(parts, grid):
+        (name, (f_kib, nf)) = pick(fetch, *parts, grid=grid)
+        (_, (w_kib, _)) = pick(write, *parts, grid=grid)
+        return name, nf, f_kib, w_kib, 1024 * (f_kib * fscale + w_kib * wscale)
+
+    # the 64-sequence decode without the gate: 64 x 96 workgroups of 1024
+    name, n, f_kib, w_kib, tb = traffic(("decode_step_kernel<128, 128, 1024",
+                                         "false>(kda::DecodeAr"), 64 * 96 * 1024)
+    algo = decode_bytes(64, 96, 128, 128)
+    rec = dict(common, kernel=name, dispatches=n,
+               workload="64 sequences x 96 heads x 128x128, bf16 I/O",
+               source_files=[p_ for p_, _, _ in DECODE_SOURCES],
+               source_digest=source_digest(DECODE_SOURCES),
+               fetch_kib_per_dispatch=f_kib, write_kib_per_dispatch=w_kib,
+               traffic_bytes_per_launch=tb, algorithmic_bytes_per_launch=algo,
+               traffic_over_algorithmic=tb / algo)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    per_kernel, total = {}, 0.0
+    for label, parts, grid in (
+            ("prep", ("prefill_prep_rows_kernel<64, 128, 128, true, false, false>",),
+             64 * 96 * 256),
+            ("chain", ("prefill_chain_roles_kernel",), 2 * 96 * 512),
+            ("ring_advance", ("ring_advance_kernel", "DF16b"), None)):
+        name, n, f_kib, w_kib, tb = traffic(parts, grid)
+        per_kernel[label] = {"kernel": name, "dispatches": n, "fetch_kib_per_dispatch": f_kib,
+                             "write_kib_per_dispatch": w_kib, "traffic_bytes": tb}
+        total += tb
+    palgo = prefill_bytes(1, 4096, 96, 128, 128)
+    rec = dict(common, workload="prefill T=4096, batch 1, 96 heads of 128x128, chunk 64, bf16",
+               source_files=[p_ for p_, _, _ in PREFILL_SOURCES],
+               source_digest=source_digest(PREFILL_SOURCES), per_kernel=per_kernel,
+               traffic_bytes_per_call=total, compulsory_bytes_per_call=palgo,
+               traffic_over_compulsory=total / palgo)
+    with open(PREFILL_TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(TRAFFIC_FILE) as f:
+        dec = json.load(f)
+    print(json.dumps({"decode_traffic_over_algorithmic": dec["traffic_over_algorithmic"],
+                      "prefill_traffic_over_compulsory": total / palgo,
+                      "prefill_per_kernel_MB": {k: v["traffic_bytes"] / 1e6
+                                                for k, v in per_kernel.items()}}))
 
 
 def single_step_latency(kda, workloads, torch, dev, reps=20):
@@ -339,6 +457,7 @@ def backward_bench(kda, workloads, torch, dev, args):
     # written (bf16), plus the conv weights and their gradient
     pbytes = B * T * H * (2 * dk + dv) * 2 * 3 + ctot * 4 * 4 * 2
     flops = backward_flops(B, T, H, dk, dv, 64)
+    fwd_flops = backward_forward_flops(B, T, H, dk, dv, 64)
     nbytes = backward_bytes(B, T, H, dk, dv)
     res = {"workload": "chunked backward (gradients of q^, k^, v^, g, beta, S0) of the "
                        "4096-token prefill, batch 1, 96 heads of 128x128, chunk 64, bf16 I/O, "
@@ -346,6 +465,10 @@ def backward_bench(kda, workloads, torch, dev, args):
            "tokens_per_s": B * T / (med / 1e3), "ms": med, "ms_min": ms[0], "ms_max": ms[-1],
            "calls": len(ms), "flops": flops, "tflops": flops / (med / 1e3) / 1e12,
            "fp32_frac": flops / (med / 1e3) / 1e12 / FP32_VECTOR_TFLOPS,
+           "flops_note": "flops includes the forward the call recomputes; flops_gradient "
+                         "excludes it",
+           "flops_gradient": flops - fwd_flops,
+           "fp32_frac_gradient": (flops - fwd_flops) / (med / 1e3) / 1e12 / FP32_VECTOR_TFLOPS,
            "compulsory_bytes": nbytes, "hbm_GBps": nbytes / (med / 1e3) / 1e9,
            "hbm_frac": nbytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS,
            "workspace_bytes": ws.numel(),
@@ -383,6 +506,9 @@ def parse():
     p.add_argument("--backward-warmup", type=int, default=5)
     p.add_argument("--no-gdn", action="store_true",
                    help="skip the flag variants (KDA_F_SCALAR_G, KDA_F_RAW_GATES)")
+    p.add_argument("--record-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                   help="(no GPU) write the committed counter records from two rocprofv3 "
+                        "counter CSVs of this benchmark, and the command that made them")
     return p.parse_args()
 
 
@@ -481,6 +607,9 @@ def variant_bench(kda, workloads, torch, dev, args, decode_name, prefill_name, f
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KDA state of every (sequence, head) is "
               "independent, so more GPUs would each run this same kernel on their own "
@@ -567,11 +696,20 @@ def main():
     def prefill():
         pst.prefill(pT, pd["q"], pd["k"], pd["v"], pd["g"], pd["beta"], pw, po, chunk=64)
 
-    # warm-up calls (the prefill kernels take 60-80 calls, about 25 ms of
-    # sustained load, to settle: the first calls run up to 25 % longer), then
-    # calls bracketed one by one by events on the launch stream (back to
-    # back, no host synchronization between them); the median call is
-    # reported
+    # the first calls, each bracketed by events (the first one allocates the
+    # handle's workspace), then warm-up calls (the prefill kernels take 60-80
+    # calls, about 25 ms of sustained load, to settle: the first calls run up
+    # to 25 % longer), then calls bracketed one by one by events on the
+    # launch stream (back to back, no host synchronization between them); the
+    # median call is reported
+    first_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(10)]
+    for e0, e1 in first_evs:
+        e0.record()
+        prefill()
+        e1.record()
+    torch.cuda.synchronize()
+    first_ms = [e0.elapsed_time(e1) for e0, e1 in first_evs]
     for _ in range(args.prefill_warmup):
         prefill()
     torch.cuda.synchronize()
@@ -587,6 +725,7 @@ def main():
     b2b_ms = back_to_back_ms(torch, prefill, args.prefill_reps)
     pbytes = prefill_bytes(pB, pT, pH, pdk, pdv)
     pflops = prefill_flops(pB, pT, pH, pdk, pdv, 64)
+    pflops_built = prefill_flops_as_built(pB, pT, pH, pdk, pdv, 64)
     assert torch.isfinite(pst.S).all().item()
 
     # the output gate as its own kernel on the prefill's output (one read of
@@ -620,11 +759,32 @@ def main():
         "decode and prefill workloads above drawn as pre-activations", raw_gates=True)
 
     bwd = None if args.no_backward else backward_bench(kda, workloads, torch, dev, args)
+    dtraffic = measured_traffic(TRAFFIC_FILE, DECODE_SOURCES)
+    ptraffic = measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SOURCES)
 
     # ---------------- one K3-shape decode step: latency, warm and flushed ---
     single = single_step_latency(kda, workloads, torch, dev)
 
-    # ---------------- practical HBM ceiling: a plain 1 GiB device copy ----
+    # ---------------- practical HBM ceiling of a state stream --------------
+    # a non-temporal in-place read-modify-write (the decode's access pattern,
+    # kda_stream_rmw) over the headline's state size (384 MiB) and the
+    # stack's (6 GiB), and a plain torch device copy of 1 GiB beside it
+    stream_gbps = {}
+    for label, nbytes in (("384MiB", 384 << 20), ("6GiB", 6 << 30)):
+        buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        kda.kda_stream_rmw(buf, 1.0)
+        torch.cuda.synchronize()
+        best = 0.0
+        for _ in range(3):
+            ev0.record()
+            for _ in range(5):
+                kda.kda_stream_rmw(buf, 1.0)
+            ev1.record()
+            torch.cuda.synchronize()
+            best = max(best, 2 * nbytes * 5 / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+        stream_gbps[label] = best
+        del buf
+    torch.cuda.empty_cache()
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -710,7 +870,7 @@ def main():
                    "batch": B, "heads": H, "d_k": dk, "d_v": dv, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(),
+                     "traffic": dtraffic["traffic_bytes_per_launch"] if dtraffic else None,
                      "kernel": "decode_step_kernel<128,128,1024,bf16,nontemporal>",
                      "bytes_per_launch": dbytes, "avg_launch_us": per_launch_s * 1e6},
         "prefill": {"workload": "chunked prefill T=4096, batch 1, 96 heads, chunk 64, bf16",
@@ -720,9 +880,15 @@ def main():
                     "tokens_per_s_back_to_back": pT * pB / (b2b_ms / 1e3),
                     "hbm_GBps": pbytes / (pre_ms / 1e3) / 1e9,
                     "hbm_frac": pbytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                    "ms_first_call": first_ms[0], "ms_first_10_calls": first_ms,
                     "tflops": pflops / (pre_ms / 1e3) / 1e12,
                     "mfma_frac": pflops / (pre_ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
-                    "compulsory_bytes": pbytes, "flops": pflops},
+                    "compulsory_bytes": pbytes, "flops": pflops,
+                    "flops_per_token_head": pflops // (pB * pT * pH),
+                    "flops_as_built": pflops_built,
+                    "mfma_frac_as_built": pflops_built / (pre_ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
+                    "traffic": ptraffic["traffic_bytes_per_call"] if ptraffic else None,
+                    "traffic_per_kernel": ptraffic["per_kernel"] if ptraffic else None},
         "stack": stack,
         "backward": bwd,
         "scalar_decay": gdn,
@@ -745,8 +911,16 @@ def main():
         "wall_s_timed_region": wall,
         "cpu_baseline": cpu,
     }
-    line["copy_GBps"] = copy_gbps
-    line["roofline"]["frac_of_copy"] = achieved / copy_gbps
+    line["stream_ceiling"] = {
+        "what": "kda_stream_rmw: non-temporal in-place read-modify-write, 16-byte accesses "
+                "(the state stream's pattern), best of 3 x 5 calls, on the headline's state "
+                "size and the stack's; torch copy_ of 1 GiB beside it",
+        "GBps_384MiB": stream_gbps["384MiB"], "GBps_6GiB": stream_gbps["6GiB"],
+        "frac_of_peak_384MiB": stream_gbps["384MiB"] / HBM_PEAK_GBPS,
+        "torch_copy_GBps": copy_gbps}
+    line["roofline"]["frac_of_stream_ceiling"] = achieved / stream_gbps["384MiB"]
+    if stack is not None:
+        stack["decode_frac_of_stream_ceiling"] = stack["decode_GBps"] / stream_gbps["6GiB"]
     line["single_step"] = single
     print(json.dumps(line))
 

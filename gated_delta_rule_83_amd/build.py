@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prologue.hip", "kda_prefill.hip",
            "kda_prep_rows.hip", "kda_gate.hip", "kda_backward.hip",
-           "kda_prologue_bwd.hip"]
+           "kda_prologue_bwd.hip", "kda_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -468,6 +468,16 @@ kda_status kda_chunk_prefill_noalloc(kda_state* stt, int32_t T, const void* q, c
                      (size_t)KDA_NOALLOC_SCRATCH_BYTES, flags, stream);
 }
 
+kda_status kda_stream_rmw(void* buf, size_t bytes, float scale, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!buf) return fail(KDA_ERR_INVALID, "buf is NULL");
+  if (!aligned16(buf) || bytes % 16 != 0)
+    return fail(KDA_ERR_INVALID, "buf must be 16-byte aligned and bytes a multiple of 16");
+  hipError_t e = kda::launch_stream_rmw(buf, bytes, scale, stream);
+  if (e != hipSuccess) return hip_fail(e, "stream probe launch");
+  return KDA_OK;
+}
+
 size_t kda_backward_workspace_bytes(const kda_dims* d, int32_t T, int32_t chunk) {
   if (check_dims(d) != KDA_OK || T < 0 || (chunk != 16 && chunk != 32 && chunk != 64)) return 0;
   return kda::backward_ws_bytes(d->batch, T, d->heads, d->d_k, d->d_v, chunk);

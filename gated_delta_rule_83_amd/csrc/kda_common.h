@@ -107,6 +107,10 @@ hipError_t launch_ring_advance(const void* q, const void* k, const void* v, void
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
+// In-place non-temporal read-modify-write of bytes (a multiple of 16) at buf:
+// buf *= scale, 16 bytes per access (the HBM ceiling of a state stream).
+hipError_t launch_stream_rmw(void* buf, size_t bytes, float scale, hipStream_t stream);
+
 struct PrefillArgs {
   float* S;            // [B][H][dk][dv]
   void* ring;          // [B][3][Ctot]

@@ -27,7 +27,7 @@ EXPORTED = [
     "kda_chunk_prefill_noalloc",
     "kda_gated_rmsnorm", "kda_decode_step_gated", "kda_backward_workspace_bytes",
     "kda_chunk_backward", "kda_prologue_backward_workspace_bytes", "kda_prologue_backward",
-    "kda_last_error", "kda_version",
+    "kda_stream_rmw", "kda_last_error", "kda_version",
 ]
 
 
@@ -81,6 +81,7 @@ def lib():
                                               vp, vp, vp, vp, i32, vp, sz, u32, vp]),
         "kda_prologue_backward_workspace_bytes": (sz, [dp, i32]),
         "kda_prologue_backward": (ctypes.c_int, [dp, i32] + [vp] * 14 + [sz, u32, vp]),
+        "kda_stream_rmw": (ctypes.c_int, [vp, sz, f32, vp]),
         "kda_last_error": (ctypes.c_char_p, []),
         "kda_version": (ctypes.c_char_p, []),
     }
@@ -242,6 +243,14 @@ def kda_chunk_prefill_noalloc(handle, T, q, k, v, g, beta, conv_w, o, chunk=64, 
         _ptr(g, "g", torch.float32), _ptr(beta, "beta", torch.float32),
         _ptr(conv_w, "conv_w", torch.float32), _ptr(o, "o", io), int(chunk), int(flags),
         _stream(stream)))
+
+
+def kda_stream_rmw(buf, scale=1.0, stream=None):
+    """In-place buf *= scale with the decode's state-stream memory pattern
+    (a measurement helper; include/kda.h)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().kda_stream_rmw(_ptr(buf, "buf"), ctypes.c_size_t(nbytes), ctypes.c_float(scale),
+                                _stream(stream)))
 
 
 def kda_backward_workspace_bytes(dims, T, chunk=64) -> int:

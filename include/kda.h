@@ -109,7 +109,12 @@ typedef struct kda_state kda_state;
  * Returns 0 for invalid or unsupported dims. */
 size_t kda_state_bytes(const kda_dims* dims, size_t* ring_bytes);
 
-/* Creates a state handle for dims.
+/* Creates a state handle for dims: the per-head state S and the conv ring,
+ * the session state a decode step carries from token to token. Source: "KV缓存
+ * 从11.25GB缩到0.21GB：…", section "Kimi Delta Attention 把注意力状态压成固定大小"
+ * (a fixed-size state per head instead of a growing cache) and section "KDA
+ * 递推公式先衰减再差分" (the 3-token ring of raw projections is kept as session
+ * state between calls).
  *  s_mem:    device buffer of kda_state_bytes() bytes, layout S[B][H][d_k][d_v]
  *            fp32, or NULL to let the library allocate it (hipMalloc).
  *  ring_mem: device buffer of ring_bytes, layout ring[B][3][Ctot] in the io
@@ -121,7 +126,9 @@ size_t kda_state_bytes(const kda_dims* dims, size_t* ring_bytes);
 kda_status kda_state_alloc(const kda_dims* dims, void* s_mem, void* ring_mem,
                            kda_state** out);
 
-/* Zeroes S and the ring of the listed sequences (a sequence start).
+/* Zeroes S and the ring of the listed sequences (a sequence start: an empty
+ * state and no conv history; source: section "KDA 递推公式先衰减再差分", the
+ * zero history before a sequence's first token).
  * seq_ids is a HOST array of n sequence indices in [0, B); seq_ids = NULL
  * resets all B sequences (n is then ignored). The zeroing is done by a fill
  * kernel on the stream (no hipMemsetAsync), so it may be graph-captured.
@@ -129,11 +136,13 @@ kda_status kda_state_alloc(const kda_dims* dims, void* s_mem, void* ring_mem,
 kda_status kda_state_reset(kda_state* st, const int32_t* seq_ids, int32_t n,
                            hipStream_t stream);
 
-/* Frees the handle, and the buffers the library allocated for it. NULL is a no-op. */
+/* Frees the handle, and the buffers the library allocated for it (S and the
+ * ring when it allocated them, its prefill workspace). NULL is a no-op. */
 void kda_state_free(kda_state* st);
 
 /* Device views of the state (for checkpointing: copy out to save, copy in
- * to restore). NULL for a NULL handle. */
+ * to restore; the ring belongs to the saved session as much as S, section
+ * "KDA 递推公式先衰减再差分"). NULL for a NULL handle. */
 float* kda_state_S(kda_state* st);
 void* kda_state_ring(kda_state* st);
 kda_status kda_state_get_dims(const kda_state* st, kda_dims* out);
@@ -190,6 +199,12 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chun
  *  chunk: 16, 32 or 64 (64 recommended). T need not be a multiple of chunk.
  *  workspace: device buffer of workspace_bytes, or NULL to use a buffer the
  *        state handle allocates on first use (and keeps until kda_state_free).
+ *        With NULL the call allocates (hipMalloc) whenever the handle's buffer
+ *        is smaller than the call needs (up to 2 GiB; then T runs in
+ *        segments): the first such call, and any later one that needs more,
+ *        frees the old buffer and allocates the new one, which synchronises
+ *        the host with the device and cannot be captured in a HIP graph. Pass
+ *        a workspace (or use kda_chunk_prefill_noalloc) to avoid both.
  * With io = bf16 the contractions run on bf16 MFMA with fp32 accumulation and
  * an fp32 state; with io = fp32 they run on fp32 MFMA.
  * Source: "为什么 Kimi K3 敢把 KV Cache 扔掉？…", section 5 (chunks with
@@ -339,6 +354,15 @@ kda_status kda_prologue_backward(const kda_dims* dims, int32_t T, const void* q,
                                  const void* dv_hat, void* dq, void* dk, void* dv,
                                  float* dconv_w, float* dring, void* workspace,
                                  size_t workspace_bytes, uint32_t flags, hipStream_t stream);
+
+/* Measurement helper, not part of the recurrence: multiplies the fp32 values
+ * of a device buffer in place by scale, with the memory pattern of the
+ * decode step's state stream (16-byte non-temporal loads, then stores: every
+ * byte read once and written once). Timing it gives the practical HBM
+ * ceiling that the state stream is compared against.
+ *  buf: device buffer, 16-byte aligned; bytes: a multiple of 16.
+ * Errors: KDA_ERR_INVALID (NULL or misaligned buffer, bytes). */
+kda_status kda_stream_rmw(void* buf, size_t bytes, float scale, hipStream_t stream);
 
 /* Description of the last error on the calling thread ("" if none). */
 const char* kda_last_error(void);

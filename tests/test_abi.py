@@ -119,6 +119,52 @@ def test_prefill_validation(fake_state):
     assert "below" in kda.last_error()
 
 
+def test_prefill_null_workspace_validates_before_allocating(fake_state):
+    """With workspace = NULL the call may allocate the handle's buffer (and so
+    synchronise); every argument is checked before that, so a bad call fails
+    with its own error and allocates nothing (include/kda.h)."""
+    assert call_prefill(fake_state, ws=None, q=None) == K.KDA_ERR_INVALID
+    assert "q is NULL" in kda.last_error()
+    assert call_prefill(fake_state, ws=None, chunk=8) == K.KDA_ERR_UNSUPPORTED
+    assert call_prefill(fake_state, ws=None, T=0) == K.KDA_OK
+    assert call_prefill(fake_state, ws=FAKE + 8, ws_bytes=1 << 30) == K.KDA_ERR_INVALID
+    assert "16-byte aligned" in kda.last_error()
+
+
+def call_prefill_noalloc(h, T=8, chunk=64, flags=0, q=FAKE, w=FAKE):
+    return kda.lib().kda_chunk_prefill_noalloc(h, T, _vp(q), _vp(FAKE), _vp(FAKE), _vp(FAKE),
+                                               _vp(FAKE), _vp(w), _vp(FAKE), chunk, flags, None)
+
+
+def test_prefill_noalloc_validation(fake_state):
+    """The allocation-free prefill validates like kda_chunk_prefill and rejects
+    a state whose single chunk does not fit its fixed scratch, all before any
+    device call."""
+    assert call_prefill_noalloc(None) == K.KDA_ERR_INVALID
+    assert call_prefill_noalloc(fake_state, q=None) == K.KDA_ERR_INVALID
+    assert "q is NULL" in kda.last_error()
+    assert call_prefill_noalloc(fake_state, chunk=48) == K.KDA_ERR_UNSUPPORTED
+    assert call_prefill_noalloc(fake_state, T=0) == K.KDA_OK
+    assert call_prefill_noalloc(fake_state, flags=16) == K.KDA_ERR_INVALID
+    d = kda.make_dims(12, 96, 128, 128, kda.KDA_BF16)  # 85.5 MB per chunk > 64 MiB
+    assert kda.kda_prefill_workspace_bytes(d, 64, 64) > kda.KDA_NOALLOC_SCRATCH_BYTES
+    h = ctypes.c_void_p()
+    assert kda.lib().kda_state_alloc(ctypes.byref(d), ctypes.c_void_p(FAKE),
+                                     ctypes.c_void_p(2 * FAKE), ctypes.byref(h)) == 0
+    try:
+        assert call_prefill_noalloc(h, T=64) == K.KDA_ERR_UNSUPPORTED
+        assert "static scratch" in kda.last_error()
+    finally:
+        kda.kda_state_free(h)
+
+
+def test_stream_probe_validation():
+    L = kda.lib()
+    assert L.kda_stream_rmw(None, 16, ctypes.c_float(1.0), None) == K.KDA_ERR_INVALID
+    assert L.kda_stream_rmw(_vp(FAKE + 4), 16, ctypes.c_float(1.0), None) == K.KDA_ERR_INVALID
+    assert L.kda_stream_rmw(_vp(FAKE), 20, ctypes.c_float(1.0), None) == K.KDA_ERR_INVALID
+
+
 def test_scalar_decay_flag_validation(fake_state):
     """KDA_F_SCALAR_G and KDA_F_RAW_GATES are flags of the decode step and the
     prefill only: there validation goes on past them (to the NULL q here); the
