@@ -41,6 +41,10 @@ bool supported_width(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 1
 
 size_t io_size(kda_dtype io) { return io == KDA_BF16 ? 2 : 4; }
 
+// The io field of validated dims as the enum (check_dims has rejected every
+// other value).
+kda_dtype io_of(const kda_dims* d) { return static_cast<kda_dtype>(d->io); }
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool aligned16(const void* p) { return aligned(p, 16); }
 
@@ -54,7 +58,7 @@ kda_status check_dims(const kda_dims* d) {
   if (d->conv_width != 4)
     return fail(KDA_ERR_INVALID, "conv_width must be 4 (got %d)", d->conv_width);
   if (d->io != KDA_F32 && d->io != KDA_BF16)
-    return fail(KDA_ERR_INVALID, "io dtype %d is not KDA_F32 or KDA_BF16", (int)d->io);
+    return fail(KDA_ERR_INVALID, "io dtype %d is not KDA_F32 or KDA_BF16", d->io);
   if (!supported_width(d->d_k) || !supported_width(d->d_v))
     return fail(KDA_ERR_UNSUPPORTED, "d_k=%d d_v=%d: supported widths are 16, 32, 64, 128",
                 d->d_k, d->d_v);
@@ -70,7 +74,7 @@ size_t s_bytes_of(const kda_dims* d) {
 }
 
 size_t ring_bytes_of(const kda_dims* d) {
-  return (size_t)d->batch * 3 * ctot_of(d) * io_size(d->io);
+  return (size_t)d->batch * 3 * ctot_of(d) * io_size(io_of(d));
 }
 
 // `allowed` is the set of flag bits the entry point understands.
@@ -107,7 +111,7 @@ kda_status decode_common(kda_state* stt, const void* q, const void* k, const voi
                          const void* gate, const float* norm_w, float eps, void* o,
                          uint32_t flags, hipStream_t stream) {
   const kda_dims* d = &stt->dims;
-  const size_t esz = io_size(d->io);
+  const size_t esz = io_size(io_of(d));
   KDA_REQUIRE_PTR(q, "q", esz);
   KDA_REQUIRE_PTR(k, "k", esz);
   KDA_REQUIRE_PTR(v, "v", esz);
@@ -117,7 +121,7 @@ kda_status decode_common(kda_state* stt, const void* q, const void* k, const voi
   if (!(flags & KDA_F_SKIP_CONV)) KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
   kda::DecodeArgs a{stt->S, stt->ring, q, k, v, g, beta, conv_w, o,
                     d->batch, d->heads, d->d_k, d->d_v, flags, gate, norm_w, eps};
-  hipError_t e = kda::launch_decode(a, d->io, stream);
+  hipError_t e = kda::launch_decode(a, io_of(d), stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KDA_OK;
 }
@@ -235,7 +239,7 @@ kda_status kda_conv_prologue(const kda_dims* dims, int32_t T, const void* q, con
   if (T == 0) return KDA_OK;
   if ((long long)dims->batch * T * dims->heads > (1LL << 31) * 3)
     return fail(KDA_ERR_UNSUPPORTED, "B*T*H too large for one launch");
-  const size_t esz = io_size(dims->io);
+  const size_t esz = io_size(io_of(dims));
   KDA_REQUIRE_PTR(q, "q", esz);
   KDA_REQUIRE_PTR(k, "k", esz);
   KDA_REQUIRE_PTR(v, "v", esz);
@@ -248,11 +252,11 @@ kda_status kda_conv_prologue(const kda_dims* dims, int32_t T, const void* q, con
   }
   kda::PrologueArgs a{q, k, v, conv_w, ring, q_out, k_out, v_out,
                       dims->batch, T, dims->heads, dims->d_k, dims->d_v, flags};
-  hipError_t e = kda::launch_prologue(a, dims->io, stream);
+  hipError_t e = kda::launch_prologue(a, io_of(dims), stream);
   if (e != hipSuccess) return hip_fail(e, "prologue launch");
   if (!(flags & KDA_F_SKIP_CONV)) {
     e = kda::launch_ring_advance(q, k, v, ring, dims->batch, T, dims->heads, dims->d_k,
-                                 dims->d_v, dims->io, stream);
+                                 dims->d_v, io_of(dims), stream);
     if (e != hipSuccess) return hip_fail(e, "ring advance launch");
   }
   return KDA_OK;
@@ -278,7 +282,7 @@ kda_status kda_decode_step_gated(kda_state* stt, const void* q, const void* k, c
   kda_status st = check_flags(flags, kStepFlags);
   if (st != KDA_OK) return st;
   if ((st = check_eps(eps)) != KDA_OK) return st;
-  KDA_REQUIRE_PTR(gate, "gate", io_size(stt->dims.io));
+  KDA_REQUIRE_PTR(gate, "gate", io_size(io_of(&stt->dims)));
   KDA_REQUIRE_PTR(norm_w, "norm_w", 4);
   return decode_common(stt, q, k, v, g, beta, conv_w, gate, norm_w, eps, o, flags, stream);
 }
@@ -296,14 +300,14 @@ kda_status kda_gated_rmsnorm(const kda_dims* dims, int32_t T, const void* x, con
   KDA_REQUIRE_PTR(norm_w, "norm_w", 16);
   KDA_REQUIRE_PTR(out, "out", 16);
   const long rows = (long)dims->batch * T * dims->heads;
-  const size_t bytes = (size_t)rows * dims->d_v * io_size(dims->io);
+  const size_t bytes = (size_t)rows * dims->d_v * io_size(io_of(dims));
   const uintptr_t xo = reinterpret_cast<uintptr_t>(x), oo = reinterpret_cast<uintptr_t>(out),
                   go = reinterpret_cast<uintptr_t>(gate);
   if (oo != xo && oo < xo + bytes && xo < oo + bytes)
     return fail(KDA_ERR_INVALID, "out overlaps x without being x");
   if (oo < go + bytes && go < oo + bytes)
     return fail(KDA_ERR_INVALID, "out overlaps gate");
-  hipError_t e = kda::launch_gated_rmsnorm(x, gate, norm_w, eps, out, rows, dims->d_v, dims->io,
+  hipError_t e = kda::launch_gated_rmsnorm(x, gate, norm_w, eps, out, rows, dims->d_v, io_of(dims),
                                            stream);
   if (e != hipSuccess) return hip_fail(e, "gated rmsnorm launch");
   return KDA_OK;
@@ -315,7 +319,7 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chun
   const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
   return nchunks *
          kda::prefill_ws_bytes_per_chunk(dims->heads, dims->batch, dims->d_k, dims->d_v, chunk,
-                                         dims->io);
+                                         io_of(dims));
 }
 
 namespace {
@@ -334,10 +338,10 @@ kda_status check_prefill(const kda_state* stt, int32_t T, const void* q, const v
   if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);
   if (chunk != 16 && chunk != 32 && chunk != 64)
     return fail(KDA_ERR_UNSUPPORTED, "chunk = %d: supported chunks are 16, 32, 64", chunk);
-  *per_chunk = kda::prefill_ws_bytes_per_chunk(d->heads, d->batch, d->d_k, d->d_v, chunk, d->io);
+  *per_chunk = kda::prefill_ws_bytes_per_chunk(d->heads, d->batch, d->d_k, d->d_v, chunk, io_of(d));
   *nchunks = ((size_t)T + chunk - 1) / chunk;
   if (T == 0) return KDA_OK;
-  const size_t esz = io_size(d->io);
+  const size_t esz = io_size(io_of(d));
   KDA_REQUIRE_PTR(q, "q", esz);
   KDA_REQUIRE_PTR(k, "k", esz);
   KDA_REQUIRE_PTR(v, "v", esz);
@@ -357,11 +361,11 @@ kda_status run_prefill(kda_state* stt, int32_t T, const void* q, const void* k, 
   const kda_dims* d = &stt->dims;
   kda::PrefillArgs a{stt->S, stt->ring, q, k, v, g, beta, conv_w, o,
                      d->batch, T, d->heads, d->d_k, d->d_v, chunk, flags};
-  hipError_t e = kda::launch_prefill(a, d->io, workspace, workspace_bytes, stream);
+  hipError_t e = kda::launch_prefill(a, io_of(d), workspace, workspace_bytes, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   if (!(flags & KDA_F_SKIP_CONV)) {
     e = kda::launch_ring_advance(q, k, v, stt->ring, d->batch, T, d->heads, d->d_k, d->d_v,
-                                 d->io, stream);
+                                 io_of(d), stream);
     if (e != hipSuccess) return hip_fail(e, "ring advance launch");
   }
   return KDA_OK;
@@ -504,7 +508,7 @@ kda_status kda_chunk_backward(const kda_dims* d, int32_t T, const void* q, const
   if (dS0 && !aligned16(dS0)) return fail(KDA_ERR_INVALID, "dS0 is not 16-byte aligned");
   const size_t need = kda::backward_ws_bytes(d->batch, T, d->heads, d->d_k, d->d_v, chunk);
   if (T > 0) {
-    const size_t esz = io_size(d->io);
+    const size_t esz = io_size(io_of(d));
     // q, k, v, g and dO are read 16 bytes (or 8 for bf16) at a time
     KDA_REQUIRE_PTR(q, "q", 16);
     KDA_REQUIRE_PTR(k, "k", 16);
@@ -527,7 +531,7 @@ kda_status kda_chunk_backward(const kda_dims* d, int32_t T, const void* q, const
   kda::BackwardArgs a{q,  k,  v,     g,   beta,       S0,         dO,         dST,
                       dq, dk, dv,    dg,  dbeta,      dS0,        d->batch,   T,
                       d->heads, d->d_k, d->d_v, chunk, nullptr, nullptr, nullptr};
-  hipError_t e = kda::launch_backward(a, d->io, workspace, stream);
+  hipError_t e = kda::launch_backward(a, io_of(d), workspace, stream);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return KDA_OK;
 }
@@ -551,7 +555,7 @@ kda_status kda_prologue_backward(const kda_dims* d, int32_t T, const void* q, co
   if (T < 0) return fail(KDA_ERR_INVALID, "T = %d is negative", T);
   if ((size_t)d->batch * d->heads * kda::prologue_bwd_segments(T) > 0x7fffffffu)
     return fail(KDA_ERR_UNSUPPORTED, "T = %d: too many (sequence, head, segment) items", T);
-  const size_t esz = io_size(d->io);
+  const size_t esz = io_size(io_of(d));
   KDA_REQUIRE_PTR(conv_w, "conv_w", 16);
   KDA_REQUIRE_PTR(dconv_w, "dconv_w", 16);
   // q, k, v, the ring and the activation gradients are read 16 (fp32) or 8
@@ -583,7 +587,7 @@ kda_status kda_prologue_backward(const kda_dims* d, int32_t T, const void* q, co
                          dk_hat, dv_hat, dq,     dk,     dv,       dconv_w,
                          dring,  static_cast<float*>(workspace), d->batch, T,
                          d->heads, d->d_k, d->d_v, kda::prologue_bwd_segments(T)};
-  e = kda::launch_prologue_backward(a, d->io, stream);
+  e = kda::launch_prologue_backward(a, io_of(d), stream);
   if (e != hipSuccess) return hip_fail(e, "prologue backward launch");
   return KDA_OK;
 }

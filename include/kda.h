@@ -67,7 +67,9 @@ typedef struct {
   int32_t d_k;        /* key width per head: 16, 32, 64 or 128 */
   int32_t d_v;        /* value width per head: 16, 32, 64 or 128 */
   int32_t conv_width; /* must be 4 */
-  kda_dtype io;       /* dtype of q, k, v, o and the ring */
+  int32_t io;         /* a kda_dtype value: dtype of q, k, v, o and the ring
+                         (a plain integer so that any value a caller passes is
+                         read and rejected as an error, not as an enum) */
 } kda_dims;
 
 /* Flags for kda_conv_prologue / kda_decode_step / kda_chunk_prefill. */
