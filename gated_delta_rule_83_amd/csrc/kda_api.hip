@@ -487,6 +487,11 @@ size_t kda_backward_workspace_bytes(const kda_dims* d, int32_t T, int32_t chunk)
   return kda::backward_ws_bytes(d->batch, T, d->heads, d->d_k, d->d_v, chunk);
 }
 
+size_t kda_backward_workspace_min_bytes(const kda_dims* d, int32_t T, int32_t chunk) {
+  if (check_dims(d) != KDA_OK || T < 0 || (chunk != 16 && chunk != 32 && chunk != 64)) return 0;
+  return kda::backward_ws_min_bytes(d->batch, T, d->heads, d->d_k, d->d_v, chunk);
+}
+
 kda_status kda_chunk_backward(const kda_dims* d, int32_t T, const void* q, const void* k,
                               const void* v, const float* g, const float* beta, const float* S0,
                               const void* dO, const float* dST, void* dq, void* dk, void* dv,
@@ -506,7 +511,7 @@ kda_status kda_chunk_backward(const kda_dims* d, int32_t T, const void* q, const
   if (S0 && !aligned16(S0)) return fail(KDA_ERR_INVALID, "S0 is not 16-byte aligned");
   if (dST && !aligned16(dST)) return fail(KDA_ERR_INVALID, "dST is not 16-byte aligned");
   if (dS0 && !aligned16(dS0)) return fail(KDA_ERR_INVALID, "dS0 is not 16-byte aligned");
-  const size_t need = kda::backward_ws_bytes(d->batch, T, d->heads, d->d_k, d->d_v, chunk);
+  const size_t need = kda::backward_ws_min_bytes(d->batch, T, d->heads, d->d_k, d->d_v, chunk);
   if (T > 0) {
     const size_t esz = io_size(io_of(d));
     // q, k, v, g and dO are read 16 bytes (or 8 for bf16) at a time
@@ -530,8 +535,9 @@ kda_status kda_chunk_backward(const kda_dims* d, int32_t T, const void* q, const
   }
   kda::BackwardArgs a{q,  k,  v,     g,   beta,       S0,         dO,         dST,
                       dq, dk, dv,    dg,  dbeta,      dS0,        d->batch,   T,
-                      d->heads, d->d_k, d->d_v, chunk, nullptr, nullptr, nullptr};
-  hipError_t e = kda::launch_backward(a, io_of(d), workspace, stream);
+                      d->heads, d->d_k, d->d_v, chunk, 0, 0, nullptr, nullptr, nullptr,
+                      nullptr};
+  hipError_t e = kda::launch_backward(a, io_of(d), workspace, T > 0 ? workspace_bytes : 0, stream);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return KDA_OK;
 }

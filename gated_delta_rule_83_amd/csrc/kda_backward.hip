@@ -32,6 +32,7 @@
 // accepted: a chunk whose total decay stays within a limit forms its decayed
 // pair terms as MFMA products of e^{Gam}- and e^{-Gam}-scaled rows, any other
 // chunk one exponential of a non-positive difference per pair.
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_common.h"
@@ -77,7 +78,7 @@ struct Item {
 __device__ __forceinline__ Item item_of(const BackwardArgs& a, long it) {
   Item r;
   const int BH = a.B * a.H;
-  r.c = (int)(it / BH);
+  r.c = a.c0 + (int)(it / BH);  // blocks index the launch's chunks from c0
   r.bh = (int)(it % BH);
   r.b = r.bh / a.H;
   r.h = r.bh % a.H;
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
   __shared__ float sU[CM][CT::SPB];
   __shared__ __attribute__((aligned(16))) float sO[CM][CT::SPO];
   __shared__ __attribute__((aligned(16))) float sEn[DK];
-  const int BH = a.B * a.H, nc = (a.T + a.chunk - 1) / a.chunk;
+  const int BH = a.B * a.H, c0 = a.c0, c1 = a.c1;
   int cbk, bh;
   chain_map(blockIdx.x, CT::NB, BH, cbk, bh);
   const int cb0 = cbk * CT::DVB;
@@ -406,19 +407,19 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
                        : 0.f;
   }
   // operands of a chunk: W, then K^d (through one register set), e^{Gam_n}
-  auto blk_of = [&](int c) { return a.scratch + ((long)c * BH + bh) * L::n; };
+  auto blk_of = [&](int c) { return a.scratch + ((long)(c - c0) * BH + bh) * L::n; };
   auto n_of = [&](int c) { return min(a.chunk, a.T - c * a.chunk); };
   Pieces<kBT, CM, DK> pk;
   Pieces<kBT, 1, DK> pe;
-  {
-    const float* b0 = blk_of(0);
-    get_rows(pk, n_of(0), [&](int r, int cx) { return ld4f(b0 + L::oW + r * DK + cx); });
+  if (c0 < c1) {
+    const float* b0 = blk_of(c0);
+    get_rows(pk, n_of(c0), [&](int r, int cx) { return ld4f(b0 + L::oW + r * DK + cx); });
     get_rows(pe, 1, [&](int, int cx) { return ld4f(b0 + L::oEn + cx); });
   }
-  for (int c = 0; c < nc; ++c) {
+  for (int c = c0; c < c1; ++c) {
     const int n = n_of(c), n4 = (n + 3) & ~3;
     float* blk = blk_of(c);
-    float* Sk = a.S0s + ((long)c * BH + bh) * DK * DV;
+    float* Sk = a.S0s + ((long)(c - c0) * BH + bh) * DK * DV;
     __syncthreads();  // the previous chunk is done with sS, sU, sO, sEn
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
     }
     __syncthreads();
     put_rows<CT::SPO>(pk, &sO[0][0]);  // K^d
-    if (c + 1 < nc) {
+    if (c + 1 < c1) {
       const float* bn = blk_of(c + 1);
       get_rows(pk, n_of(c + 1), [&](int r, int cx) { return ld4f(bn + L::oW + r * DK + cx); });
       get_rows(pe, 1, [&](int, int cx) { return ld4f(bn + L::oEn + cx); });
@@ -477,6 +478,17 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
         for (int e = 0; e < 4; ++e) accS[m][e] *= sEn[16 * rt + r4 + e];
         accS[m] = mma_tile(accS[m], n4, [&](int i, int kx) { return sO[kx][16 * rt + i]; },
                            [&](int kx, int j) { return sU[kx][16 * ct + j]; });
+      }
+    }
+  }
+  if (a.S_out) {  // the state leaving chunk c1 - 1: where the next chunk range starts
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {
+      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      if (t < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a.S_out[((long)bh * DK + 16 * rt + r4 + e) * DV + cb0 + 16 * ct + l16] = accS[m][e];
       }
     }
   }
@@ -496,7 +508,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
   __shared__ float sdU[CM][CT::SPB];
   __shared__ __attribute__((aligned(16))) float sO[CM][CT::SPO];
   __shared__ __attribute__((aligned(16))) float sEn[DK];
-  const int BH = a.B * a.H, nc = (a.T + a.chunk - 1) / a.chunk;
+  const int BH = a.B * a.H, c0 = a.c0, c1 = a.c1;
   int cbk, bh;
   chain_map(blockIdx.x, CT::NB, BH, cbk, bh);
   const int cb0 = cbk * DVB, b = bh / a.H, h = bh % a.H;
@@ -518,7 +530,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
   // then K^d, Q~ and W in turn through one set. Rows at or past the chunk's
   // last token are zeros (P is zero right of its diagonal, so its columns
   // past the last token are zero as stored).
-  auto blk_of = [&](int c) { return a.scratch + ((long)c * BH + bh) * L::n; };
+  auto blk_of = [&](int c) { return a.scratch + ((long)(c - c0) * BH + bh) * L::n; };
   auto n_of = [&](int c) { return min(a.chunk, a.T - c * a.chunk); };
   Pieces<kBT, CM, CM> pp;
   Pieces<kBT, CM, DVB> pd;
@@ -532,11 +544,11 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
     get_rows(pd, nn, [&](int r, int cx) { return ld4f(dO + (drow0 + (long)r * a.H) * DV + cb0 + cx); });
     get_rows(pe, 1, [&](int, int cx) { return ld4f(bc + L::oEn + cx); });
   };
-  if (nc > 0) get_first(nc - 1);
-  for (int c = nc - 1; c >= 0; --c) {
+  if (c1 > c0) get_first(c1 - 1);
+  for (int c = c1 - 1; c >= c0; --c) {
     const int n = n_of(c), n4 = (n + 3) & ~3;
     float* blk = blk_of(c);
-    float* dSk = a.dS1s + ((long)c * BH + bh) * DK * DV;
+    float* dSk = a.dS1s + ((long)(c - c0) * BH + bh) * DK * DV;
     auto get_k = [&](long off) {
       get_rows(pk, n, [&](int r, int cx) { return ld4f(blk + off + r * DK + cx); });
     };
@@ -602,7 +614,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
     }
     __syncthreads();
     put_rows<CT::SPO>(pk, &sO[0][0]);  // W
-    if (c > 0) get_first(c - 1);
+    if (c > c0) get_first(c - 1);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {  // - W^T dU
@@ -1005,18 +1017,21 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
   }
 }
 
+// Stages of one launch sequence over the chunk range [a.c0, a.c1).
+enum : unsigned { kStPrep = 1, kStState = 2, kStReverse = 4, kStGrads = 8, kStAll = 15 };
+
 template <int DK, int DV, typename IO>
-hipError_t run_bw(const BackwardArgs& a, hipStream_t st) {
+hipError_t run_bw(const BackwardArgs& a, unsigned stages, hipStream_t st) {
   constexpr int NB = DV / bw_dvb<DV>();
-  const int nc = (a.T + a.chunk - 1) / a.chunk;
-  const long items = (long)nc * a.B * a.H;
+  const long items = (long)(a.c1 - a.c0) * a.B * a.H;
   const unsigned chains = (unsigned)(NB * a.B * a.H);
-  if (items > 0) {
+  if (items > 0 && (stages & kStPrep))
     hipLaunchKernelGGL((bw_prep_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBP), 0, st, a);
+  if (items > 0 && (stages & kStState))
     hipLaunchKernelGGL((bw_state_chain_kernel<DK, DV>), dim3(chains), dim3(kBT), 0, st, a);
-  }
-  hipLaunchKernelGGL((bw_reverse_chain_kernel<DK, DV, IO>), dim3(chains), dim3(kBT), 0, st, a);
-  if (items > 0) {
+  if (stages & kStReverse)
+    hipLaunchKernelGGL((bw_reverse_chain_kernel<DK, DV, IO>), dim3(chains), dim3(kBT), 0, st, a);
+  if (items > 0 && (stages & kStGrads)) {
     hipLaunchKernelGGL((bw_grad_dense_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBT), 0,
                        st, a);
     hipLaunchKernelGGL((bw_grad_solve_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBS), 0,
@@ -1028,17 +1043,28 @@ hipError_t run_bw(const BackwardArgs& a, hipStream_t st) {
 }
 
 template <int DK, int DV>
-hipError_t run_bw_io(const BackwardArgs& a, kda_dtype io, hipStream_t st) {
-  return io == KDA_BF16 ? run_bw<DK, DV, bf16>(a, st) : run_bw<DK, DV, float>(a, st);
+hipError_t run_bw_io(const BackwardArgs& a, kda_dtype io, unsigned stages, hipStream_t st) {
+  return io == KDA_BF16 ? run_bw<DK, DV, bf16>(a, stages, st)
+                        : run_bw<DK, DV, float>(a, stages, st);
 }
 
 template <int DK>
-hipError_t run_bw_dv(const BackwardArgs& a, kda_dtype io, hipStream_t st) {
+hipError_t run_bw_dv(const BackwardArgs& a, kda_dtype io, unsigned stages, hipStream_t st) {
   switch (a.dvw) {
-    case 16: return run_bw_io<DK, 16>(a, io, st);
-    case 32: return run_bw_io<DK, 32>(a, io, st);
-    case 64: return run_bw_io<DK, 64>(a, io, st);
-    case 128: return run_bw_io<DK, 128>(a, io, st);
+    case 16: return run_bw_io<DK, 16>(a, io, stages, st);
+    case 32: return run_bw_io<DK, 32>(a, io, stages, st);
+    case 64: return run_bw_io<DK, 64>(a, io, stages, st);
+    case 128: return run_bw_io<DK, 128>(a, io, stages, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t run_bw_any(const BackwardArgs& a, kda_dtype io, unsigned stages, hipStream_t st) {
+  switch (a.dkw) {
+    case 16: return run_bw_dv<16>(a, io, stages, st);
+    case 32: return run_bw_dv<32>(a, io, stages, st);
+    case 64: return run_bw_dv<64>(a, io, stages, st);
+    case 128: return run_bw_dv<128>(a, io, stages, st);
   }
   return hipErrorInvalidValue;
 }
@@ -1056,29 +1082,101 @@ size_t scratch_floats(int dk, int dv) {
   return 0;
 }
 
+// Workspace bytes per chunk of all sequences and heads (its scratch blocks,
+// entering states and leaving-state gradients) and per state [B][H][dk][dv].
+struct BwSizes {
+  size_t per_chunk, state;
+};
+
+BwSizes bw_sizes(int B, int H, int dk, int dv) {
+  const size_t BH = (size_t)B * H, st = (size_t)dk * dv;
+  return {BH * (scratch_floats(dk, dv) + 2 * st) * sizeof(float), BH * st * sizeof(float)};
+}
+
+// Bytes for ranges of L chunks out of nc: one range's blocks, plus, when
+// there are several ranges, the state entering every range but the first
+// and one carried state gradient.
+size_t range_need(long nc, long L, const BwSizes& z) {
+  if (L >= nc) return (size_t)nc * z.per_chunk;
+  const long nseg = (nc + L - 1) / L;
+  return (size_t)L * z.per_chunk + (size_t)nseg * z.state;
+}
+
+// The longest range that fits ws_bytes (nc when the one-shot layout fits,
+// 0 when nothing does).
+long range_chunks(long nc, size_t ws_bytes, const BwSizes& z) {
+  if (range_need(nc, nc, z) <= ws_bytes) return nc;
+  for (long L = std::min<long>(nc - 1, (long)(ws_bytes / z.per_chunk)); L >= 1; --L)
+    if (range_need(nc, L, z) <= ws_bytes) return L;
+  return 0;
+}
+
 }  // namespace
 
 size_t backward_ws_bytes(int B, int T, int H, int dk, int dv, int chunk) {
-  const size_t nc = ((size_t)T + chunk - 1) / chunk;
-  const size_t items = nc * B * H;
-  return items * scratch_floats(dk, dv) * sizeof(float) +
-         2 * items * (size_t)dk * dv * sizeof(float);
+  const long nc = ((long)T + chunk - 1) / chunk;
+  return range_need(nc, nc, bw_sizes(B, H, dk, dv));
 }
 
-hipError_t launch_backward(BackwardArgs a, kda_dtype io, void* ws, hipStream_t stream) {
-  const size_t nc = ((size_t)a.T + a.chunk - 1) / a.chunk;
-  const size_t items = nc * a.B * a.H;
+size_t backward_ws_min_bytes(int B, int T, int H, int dk, int dv, int chunk) {
+  const long nc = ((long)T + chunk - 1) / chunk;
+  const BwSizes z = bw_sizes(B, H, dk, dv);
+  size_t best = range_need(nc, nc, z);
+  // need(L) >= L * per_chunk, so no L past best / per_chunk can do better
+  for (long L = 1; L < nc && (size_t)L * z.per_chunk < best; ++L)
+    best = std::min(best, range_need(nc, L, z));
+  return best;
+}
+
+// One-shot when the workspace holds every chunk's blocks; otherwise the
+// chunks are taken in ranges of L (the longest that fits): a forward pass
+// over the ranges keeps only the state entering each (prep + state chain),
+// then, from the last range to the first, each range is prepared again, its
+// state chain rerun from the kept state, its reverse chain started from the
+// state gradient the later range handed back, and its per-chunk gradients
+// formed. Every chunk sees the same fp32 values as in the one-shot call.
+hipError_t launch_backward(BackwardArgs a, kda_dtype io, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  const long nc = ((long)a.T + a.chunk - 1) / a.chunk;
+  const BwSizes z = bw_sizes(a.B, a.H, a.dkw, a.dvw);
+  const long L = range_chunks(nc, ws_bytes, z);
+  if (nc > 0 && L < 1) return hipErrorInvalidValue;
+  const size_t BH = (size_t)a.B * a.H, st = (size_t)a.dkw * a.dvw;
   float* w = static_cast<float*>(ws);
   a.scratch = w;
-  a.S0s = w + items * scratch_floats(a.dkw, a.dvw);
-  a.dS1s = a.S0s + items * (size_t)a.dkw * a.dvw;
-  switch (a.dkw) {
-    case 16: return run_bw_dv<16>(a, io, stream);
-    case 32: return run_bw_dv<32>(a, io, stream);
-    case 64: return run_bw_dv<64>(a, io, stream);
-    case 128: return run_bw_dv<128>(a, io, stream);
+  a.S0s = w + (size_t)L * BH * scratch_floats(a.dkw, a.dvw);
+  a.dS1s = a.S0s + (size_t)L * BH * st;
+  a.S_out = nullptr;
+  if (L >= nc) {
+    a.c0 = 0;
+    a.c1 = (int)nc;
+    return run_bw_any(a, io, kStAll, stream);
   }
-  return hipErrorInvalidValue;
+  const long nseg = (nc + L - 1) / L;
+  float* kept = a.dS1s + (size_t)L * BH * st;  // states entering ranges 1 .. nseg - 1
+  float* carry = kept + (size_t)(nseg - 1) * BH * st;
+  auto kept_of = [&](long s) { return kept + (size_t)(s - 1) * BH * st; };
+  auto range = [&](long s) {
+    BackwardArgs x = a;
+    x.c0 = (int)(s * L);
+    x.c1 = (int)std::min(nc, (s + 1) * L);
+    x.S0 = s == 0 ? a.S0 : kept_of(s);
+    return x;
+  };
+  for (long s = 0; s + 1 < nseg; ++s) {
+    BackwardArgs x = range(s);
+    x.S_out = kept_of(s + 1);
+    const hipError_t e = run_bw_any(x, io, kStPrep | kStState, stream);
+    if (e != hipSuccess) return e;
+  }
+  for (long s = nseg - 1; s >= 0; --s) {
+    BackwardArgs x = range(s);
+    x.dST = s == nseg - 1 ? a.dST : carry;
+    x.dS0 = s == 0 ? a.dS0 : carry;  // read and written by the same thread, in place
+    const hipError_t e = run_bw_any(x, io, kStAll, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kda

@@ -134,23 +134,30 @@ struct BackwardArgs {
   const void* v;        // [B][T][H][dv] v^
   const float* g;       // [B][T][H][dk]
   const float* beta;    // [B][T][H]
-  const float* S0;      // [B][H][dk][dv] entering state, or NULL (zero)
+  const float* S0;      // [B][H][dk][dv] state entering chunk c0, or NULL (zero)
   const void* dO;       // [B][T][H][dv] (io dtype)
-  const float* dST;     // [B][H][dk][dv], or NULL (zero)
+  const float* dST;     // [B][H][dk][dv] gradient of the state leaving chunk c1 - 1, or NULL
   void* dq;             // [B][T][H][dk] (io dtype)
   void* dk;
   void* dv;             // [B][T][H][dv] (io dtype)
   float* dg;            // [B][T][H][dk]
   float* dbeta;         // [B][T][H]
-  float* dS0;           // [B][H][dk][dv], or NULL (not written)
+  float* dS0;           // [B][H][dk][dv] gradient of the state entering chunk c0, or NULL
   int B, T, H, dkw, dvw, chunk;  // widths d_k, d_v
-  // workspace regions, set by launch_backward
+  // set by launch_backward for each launch: the chunk range [c0, c1) and
+  // the workspace regions (indexed from chunk c0)
+  int c0, c1;
+  float* S_out;         // [B][H][dk][dv] state leaving chunk c1 - 1, or NULL
   float* scratch;       // per (chunk, sequence, head) blocks
-  float* S0s;           // entering state of every chunk [nc][B][H][dk][dv]
+  float* S0s;           // entering state of every chunk [c1 - c0][B][H][dk][dv]
   float* dS1s;          // gradient reaching every chunk's leaving state
 };
+// Workspace of the one-shot call (every chunk's blocks at once), and the
+// least any chunk-range split needs.
 size_t backward_ws_bytes(int B, int T, int H, int dk, int dv, int chunk);
-hipError_t launch_backward(BackwardArgs a, kda_dtype io, void* ws, hipStream_t stream);
+size_t backward_ws_min_bytes(int B, int T, int H, int dk, int dv, int chunk);
+hipError_t launch_backward(BackwardArgs a, kda_dtype io, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 struct PrologueBwdArgs {
   const void* q;        // [B][T][H][dk] raw projections (io dtype)

@@ -26,6 +26,7 @@ EXPORTED = [
     "kda_decode_step", "kda_prefill_workspace_bytes", "kda_chunk_prefill",
     "kda_chunk_prefill_noalloc",
     "kda_gated_rmsnorm", "kda_decode_step_gated", "kda_backward_workspace_bytes",
+    "kda_backward_workspace_min_bytes",
     "kda_chunk_backward", "kda_prologue_backward_workspace_bytes", "kda_prologue_backward",
     "kda_stream_rmw", "kda_last_error", "kda_version",
 ]
@@ -77,6 +78,7 @@ def lib():
         "kda_decode_step_gated": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
                                                  u32, vp]),
         "kda_backward_workspace_bytes": (sz, [dp, i32, i32]),
+        "kda_backward_workspace_min_bytes": (sz, [dp, i32, i32]),
         "kda_chunk_backward": (ctypes.c_int, [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                               vp, vp, vp, vp, i32, vp, sz, u32, vp]),
         "kda_prologue_backward_workspace_bytes": (sz, [dp, i32]),
@@ -257,12 +259,18 @@ def kda_backward_workspace_bytes(dims, T, chunk=64) -> int:
     return int(lib().kda_backward_workspace_bytes(ctypes.byref(dims), int(T), int(chunk)))
 
 
+def kda_backward_workspace_min_bytes(dims, T, chunk=64) -> int:
+    return int(lib().kda_backward_workspace_min_bytes(ctypes.byref(dims), int(T), int(chunk)))
+
+
 def kda_chunk_backward(dims, T, q, k, v, g, beta, S0, dO, dST, dq, dk, dv, dg, dbeta, dS0,
                        chunk=64, workspace=None, flags=0, stream=None):
     """Gradients of the recurrence for T tokens (include/kda.h). S0, dST and
     dS0 may be None. `workspace` is a device tensor of at least
-    kda_backward_workspace_bytes(dims, T, chunk) bytes; if None, one is taken
-    from torch's allocator for this call."""
+    kda_backward_workspace_min_bytes(dims, T, chunk) bytes (with less than
+    kda_backward_workspace_bytes the chunks are taken in ranges); if None, one
+    of kda_backward_workspace_bytes is taken from torch's allocator for this
+    call."""
     io = io_dtype(dims)
     need = kda_backward_workspace_bytes(dims, T, chunk)
     if workspace is None and need > 0:

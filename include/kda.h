@@ -274,12 +274,24 @@ kda_status kda_decode_step_gated(kda_state* st, const void* q, const void* k,
                                  const float* conv_w, const void* gate, const float* norm_w,
                                  float eps, void* o, uint32_t flags, hipStream_t stream);
 
-/* Device workspace that kda_chunk_backward needs for T tokens and `chunk`
- * (0 if the arguments are invalid): per (chunk, sequence, head) a scratch
- * block of the chunk's intermediate products, plus the entering state and the
- * leaving-state gradient of every chunk, all fp32. About 3.5 GB for B = 1,
- * T = 4096, 96 heads of 128 x 128, chunk 64. */
+/* Device workspace with which kda_chunk_backward takes all T tokens in one
+ * pass (0 if the arguments are invalid): per (chunk, sequence, head) a
+ * scratch block of the chunk's intermediate products, plus the entering
+ * state and the leaving-state gradient of every chunk, all fp32. About
+ * 3.5 GB for B = 1, T = 4096, 96 heads of 128 x 128, chunk 64 (and 451 GB
+ * for 16 sequences of 32768 tokens: see kda_backward_workspace_min_bytes). */
 size_t kda_backward_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chunk);
+
+/* The least workspace kda_chunk_backward accepts for T tokens and `chunk`
+ * (0 if the arguments are invalid). With less than
+ * kda_backward_workspace_bytes the call takes the chunks in ranges of L
+ * (the longest that fits): L chunks' blocks, the fp32 state
+ * [B][H][d_k][d_v] entering every range but the first, and one carried
+ * state gradient, i.e. L * (one chunk's blocks) + ceil(nc / L) * (one
+ * state) bytes for nc = ceil(T / chunk) chunks; this returns the least of
+ * that over L. About 13.4 GB for 16 sequences of 32768 tokens, 96 heads
+ * of 128 x 128, chunk 64 (L = 8). */
+size_t kda_backward_workspace_min_bytes(const kda_dims* dims, int32_t T, int32_t chunk);
 
 /* Gradient of the recurrence (decay, delta read, rank-1 write, readout) for
  * training, chunkwise: for the forward pass that kda_chunk_prefill runs with
@@ -301,7 +313,13 @@ size_t kda_backward_workspace_bytes(const kda_dims* dims, int32_t T, int32_t chu
  *  dS0:   [B][H][d_k][d_v] fp32, or NULL (not written).
  * q, k, v, g, dO, S0, dST and dS0 must be 16-byte aligned (the other
  * pointers the alignment of their element type). workspace: device buffer of
- * kda_backward_workspace_bytes (16-byte aligned, contents on entry ignored).
+ * workspace_bytes >= kda_backward_workspace_min_bytes (16-byte aligned,
+ * contents on entry ignored). With kda_backward_workspace_bytes or more the
+ * chunks are taken in one pass; with less, in ranges: a first pass over the
+ * ranges keeps the state entering each (the forward part is then computed
+ * twice per range but the last), then the ranges are taken from the last to
+ * the first, each handing the gradient of its entering state to the one
+ * before. The results are bitwise those of the one-pass call.
  * flags must be 0. chunk: 16, 32 or 64; T need not be a multiple of it.
  * T = 0 writes dS0 = dST (zero if dST is NULL). All arithmetic is fp32.
  * The forward pass is recomputed inside (the entering state of every chunk
