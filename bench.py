@@ -480,7 +480,62 @@ def backward_bench(kda, workloads, torch, dev, args):
                         "hbm_frac": pbytes / (pmed / 1e3) / 1e9 / HBM_PEAK_GBPS},
            "training_backward_ms": med + pmed,
            "training_backward_tokens_per_s": B * T / ((med + pmed) / 1e3)}
-    del ws, out, pws, pout
+    del ws, out, pws, pout, qh, kh, vh, g, beta, S0, dO, dST, q, k, v
+    torch.cuda.empty_cache()
+    if not args.no_backward_layer:
+        res["layer_16x32768"] = backward_layer_bench(kda, workloads, torch, dev, args)
+    return res
+
+
+def backward_layer_bench(kda, workloads, torch, dev, args):
+    """The backward of one training layer of the stack's shape (16 sequences
+    of 32768 tokens, 96 heads of 128 x 128, bf16 I/O), whose one-pass
+    workspace (451 GB) exceeds the device: the call takes its chunks in
+    ranges within a 24 GiB workspace. Inputs drawn on the device
+    (workloads.draw_layer_activations); one warm-up call, then the median of
+    event-bracketed calls."""
+    B, T, H, dk, dv = 16, 32768, 96, 128, 128
+    ws_bytes = 24 << 30
+    dims = kda.make_dims(B, H, dk, dv, torch.bfloat16)
+    ins = workloads.draw_layer_activations(B, T, H, dk, dv, dev, seed=1500)
+    out = [torch.empty(B, T, H, dk, dtype=torch.bfloat16, device=dev),
+           torch.empty(B, T, H, dk, dtype=torch.bfloat16, device=dev),
+           torch.empty(B, T, H, dv, dtype=torch.bfloat16, device=dev),
+           torch.empty(B, T, H, dk, device=dev), torch.empty(B, T, H, device=dev),
+           torch.empty(B, H, dk, dv, device=dev)]
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def call():
+        kda.kda_chunk_backward(dims, T, *ins, *out, chunk=64, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.backward_layer_reps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    med = ms[len(ms) // 2]
+    assert all(torch.isfinite(t.float()).all().item() for t in out)
+    nc = -(-T // 64)
+    full = kda.kda_backward_workspace_bytes(dims, T, 64)
+    per_chunk, state = full // nc, B * H * dk * dv * 4
+    L = next(n for n in range(min(nc - 1, ws_bytes // per_chunk), 0, -1)
+             if n * per_chunk + (-(-nc // n)) * state <= ws_bytes)
+    flops = backward_flops(B, T, H, dk, dv, 64)
+    res = {"workload": "chunked backward of one layer of the training step: 16 sequences x "
+                       "32768 tokens, 96 heads of 128x128, chunk 64, bf16 I/O",
+           "workspace_bytes": ws_bytes, "one_pass_workspace_bytes": full,
+           "min_workspace_bytes": kda.kda_backward_workspace_min_bytes(dims, T, 64),
+           "chunks_per_range": L, "ranges": -(-nc // L),
+           "ms": med, "ms_min": ms[0], "ms_max": ms[-1], "calls": len(ms),
+           "tokens_per_s": B * T / (med / 1e3),
+           "tflops": flops / (med / 1e3) / 1e12}
+    del ins, out, ws
+    torch.cuda.empty_cache()
     return res
 
 
@@ -504,6 +559,9 @@ def parse():
                    help="skip the chunked backward measurement")
     p.add_argument("--backward-reps", type=int, default=10)
     p.add_argument("--backward-warmup", type=int, default=5)
+    p.add_argument("--no-backward-layer", action="store_true",
+                   help="skip the backward of the 16 x 32768-token layer (ranges in 24 GiB)")
+    p.add_argument("--backward-layer-reps", type=int, default=3)
     p.add_argument("--no-gdn", action="store_true",
                    help="skip the flag variants (KDA_F_SCALAR_G, KDA_F_RAW_GATES)")
     p.add_argument("--record-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),

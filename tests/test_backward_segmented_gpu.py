@@ -114,32 +114,6 @@ def test_segmented_backward_rejects_a_smaller_workspace():
         _call(dims, T, ins, 64, least - 16, dev)
 
 
-def _layer_inputs(B, T, H, dk, dv, dev, seed):
-    """Activations of the training step's shape, drawn on the device one
-    sequence at a time: q^ and k^ unit vectors per head (bf16), v^ ~ N(0, 1)
-    (bf16), g = log sigmoid(N(0, 1)), beta = sigmoid(N(0, 1)), S0 ~ N(0, 1)/4,
-    dO ~ N(0, 1) (bf16), dST ~ N(0, 1)."""
-    gen = torch.Generator(device=dev).manual_seed(seed)
-    bf = torch.bfloat16
-    q = torch.empty(B, T, H, dk, dtype=bf, device=dev)
-    k = torch.empty_like(q)
-    v = torch.empty(B, T, H, dv, dtype=bf, device=dev)
-    g = torch.empty(B, T, H, dk, device=dev)
-    dO = torch.empty(B, T, H, dv, dtype=bf, device=dev)
-    for b in range(B):
-        for dst in (q[b], k[b]):
-            x = torch.randn(T, H, dk, generator=gen, device=dev)
-            dst.copy_(torch.nn.functional.normalize(x, dim=-1))
-        v[b].copy_(torch.randn(T, H, dv, generator=gen, device=dev))
-        g[b].copy_(torch.nn.functional.logsigmoid(torch.randn(T, H, dk, generator=gen,
-                                                              device=dev)))
-        dO[b].copy_(torch.randn(T, H, dv, generator=gen, device=dev))
-    beta = torch.sigmoid(torch.randn(B, T, H, generator=gen, device=dev))
-    S0 = torch.randn(B, H, dk, dv, generator=gen, device=dev) * 0.25
-    dST = torch.randn(B, H, dk, dv, generator=gen, device=dev)
-    return [q, k, v, g, beta, S0, dO, dST]
-
-
 def test_backward_layer_16x32768_in_bounded_workspace():
     dev = device()
     B, T, H, dk, dv = 16, 32768, 96, 128, 128
@@ -153,7 +127,7 @@ def test_backward_layer_16x32768_in_bounded_workspace():
     assert kda.kda_backward_workspace_min_bytes(dims, T, 64) < ws_bytes
     L = _ranges_of(dims, T, 64, ws_bytes)
     print(f"ranges of {L} chunks, {-(-512 // L)} ranges", flush=True)
-    ins = _layer_inputs(B, T, H, dk, dv, dev, seed=1500)
+    ins = workloads.draw_layer_activations(B, T, H, dk, dv, dev, seed=1500)
     out = _outputs(B, T, H, dk, dv, torch.bfloat16, dev)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

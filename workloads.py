@@ -189,3 +189,34 @@ def draw_stack_conv_w(layer: int, H: int, dk: int, dv: int, device) -> torch.Ten
     gen = torch.Generator(device=device).manual_seed(4_000_000 + 100 * layer + 99)
     return 0.5 * torch.randn(H * (2 * dk + dv), 4, generator=gen, dtype=torch.float32,
                              device=device)
+
+
+def draw_layer_activations(B: int, T: int, H: int, dk: int, dv: int, device,
+                           seed: int) -> list:
+    """Inputs of a backward call at the size of a training layer, drawn on the
+    device one sequence at a time (no host copy of the ~150 GB they take at
+    16 x 32768 x 96 heads): q^ and k^ unit vectors per head (bf16), v^ ~
+    N(0, 1) (bf16), g = log sigmoid(N(0, 1)), beta = sigmoid(N(0, 1)),
+    S0 ~ N(0, 1) / 4, dO ~ N(0, 1) (bf16), dST ~ N(0, 1).
+    Returns [q, k, v, g, beta, S0, dO, dST]."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    bf = torch.bfloat16
+    q = torch.empty(B, T, H, dk, dtype=bf, device=device)
+    k = torch.empty_like(q)
+    v = torch.empty(B, T, H, dv, dtype=bf, device=device)
+    g = torch.empty(B, T, H, dk, device=device)
+    dO = torch.empty(B, T, H, dv, dtype=bf, device=device)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
+
+    for b in range(B):
+        for dst in (q[b], k[b]):
+            dst.copy_(torch.nn.functional.normalize(randn(T, H, dk), dim=-1))
+        v[b].copy_(randn(T, H, dv))
+        g[b].copy_(torch.nn.functional.logsigmoid(randn(T, H, dk)))
+        dO[b].copy_(randn(T, H, dv))
+    beta = torch.sigmoid(randn(B, T, H))
+    S0 = randn(B, H, dk, dv) * 0.25
+    dST = randn(B, H, dk, dv)
+    return [q, k, v, g, beta, S0, dO, dST]
