@@ -747,6 +747,158 @@ __global__ __launch_bounds__(kBT, 2) void bw_grad_dense_kernel(BackwardArgs a) {
     }
 }
 
+// The same products for bf16 I/O (d_v >= 32), with bf16 MFMA operands as in
+// the forward (v_mfma_f32_16x16x32_bf16; fp32 accumulation): each 32-column
+// slab of S0, dS1, dO, dU and U is staged in LDS as bf16 rows, and one MFMA
+// per output tile and slab takes 8 consecutive elements per lane from two
+// 16-byte LDS reads. The row sums of dS1 * S0 are taken in fp32 from the
+// values as loaded, before rounding.
+template <int DK, int DV>
+__global__ __launch_bounds__(kBT, 2) void bw_grad_dense_bf16_kernel(BackwardArgs a) {
+  using L = BwL<DK, DV>;
+  constexpr int SL = 32, SLB = SL + 8;  // slab width; bf16 row stride (16-byte rows)
+  constexpr int CTN = DK / 16, CPW = (CTN + 3) / 4, RT = CM / 16;
+  constexpr int Q4 = SL / 4;                  // float4 pieces per slab row
+  constexpr int SP = (DK * Q4 + kBT - 1) / kBT;  // S0 / dS1 pieces per thread
+  constexpr int TP = (CM * Q4 + kBT - 1) / kBT;  // dO / dU / U pieces per thread
+  static_assert(DV % SL == 0 && kBT % Q4 == 0, "dense bf16 tiling");
+  __shared__ __attribute__((aligned(16))) bf16 sS0[DK][SLB], sdS1[DK][SLB];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[CM][SLB], sdU[CM][SLB], sU[CM][SLB];
+  __shared__ float sdD[DK];
+  const Item it = item_of(a, blockIdx.x);
+  const int n = it.n;
+  float* blk = a.scratch + (long)blockIdx.x * L::n;
+  const float* S0 = a.S0s + (long)blockIdx.x * DK * DV;
+  const float* dS1 = a.dS1s + (long)blockIdx.x * DK * DV;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l16 = lane % 16, r4 = 4 * (lane / 16), koff = 8 * (lane / 16);
+  const bf16* dO = static_cast<const bf16*>(a.dO);
+  const long row0 = tok(a, it.b, it.t0, it.h);
+  f32x4 aQ[CPW][RT], aW[CPW][RT], aK[CPW][RT], aP[RT];
+#pragma unroll
+  for (int m = 0; m < CPW; ++m)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) aQ[m][rt] = aW[m][rt] = aK[m][rt] = kZero4;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) aP[rt] = kZero4;
+  float dd[SP];  // row sums of dS1 * S0 for rows (tid + kBT p) / Q4, in lanes with tid % Q4 == 0
+#pragma unroll
+  for (int p = 0; p < SP; ++p) dd[p] = 0.f;
+  auto cvt = [](f32x4 v) { return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]}; };
+  for (int l0 = 0; l0 < DV; l0 += SL) {
+    // every load of the slab issued before the first LDS store
+    f32x4 vs[SP], vd[SP], vo[TP], vdu[TP], vu[TP];
+#pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int idx = tid + kBT * p, r = idx / Q4, c = 4 * (idx % Q4);
+      const bool live = idx < DK * Q4;
+      vs[p] = live ? ld4f(S0 + (long)r * DV + l0 + c) : kZero4;
+      vd[p] = live ? ld4f(dS1 + (long)r * DV + l0 + c) : kZero4;
+    }
+#pragma unroll
+    for (int p = 0; p < TP; ++p) {
+      const int idx = tid + kBT * p, r = idx / Q4, c = 4 * (idx % Q4);
+      const bool live = idx < CM * Q4 && r < n;
+      vo[p] = live ? ld4f(dO + (row0 + (long)r * a.H) * DV + l0 + c) : kZero4;
+      vdu[p] = live ? ld4f(blk + L::odU + r * DV + l0 + c) : kZero4;
+      vu[p] = live ? ld4f(blk + L::oU + r * DV + l0 + c) : kZero4;
+    }
+    __syncthreads();  // the previous slab's products are done with the LDS rows
+#pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int idx = tid + kBT * p, r = idx / Q4, c = 4 * (idx % Q4);
+      float part = vs[p][0] * vd[p][0] + vs[p][1] * vd[p][1] + vs[p][2] * vd[p][2] +
+                   vs[p][3] * vd[p][3];
+#pragma unroll
+      for (int off = 1; off < Q4; off <<= 1) part += __shfl_xor(part, off, kWave);
+      dd[p] += part;
+      if (idx < DK * Q4) {
+        *reinterpret_cast<bf16x4*>(&sS0[r][c]) = cvt(vs[p]);
+        *reinterpret_cast<bf16x4*>(&sdS1[r][c]) = cvt(vd[p]);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < TP; ++p) {
+      const int idx = tid + kBT * p, r = idx / Q4, c = 4 * (idx % Q4);
+      if (idx < CM * Q4) {
+        *reinterpret_cast<bf16x4*>(&sdO[r][c]) = cvt(vo[p]);
+        *reinterpret_cast<bf16x4*>(&sdU[r][c]) = cvt(vdu[p]);
+        *reinterpret_cast<bf16x4*>(&sU[r][c]) = cvt(vu[p]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+      const int ct = wv + 4 * m;
+      if (ct < CTN) {
+        const bf16x8 fs0 = *reinterpret_cast<const bf16x8*>(&sS0[16 * ct + l16][koff]);
+        const bf16x8 fds1 = *reinterpret_cast<const bf16x8*>(&sdS1[16 * ct + l16][koff]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8 fo = *reinterpret_cast<const bf16x8*>(&sdO[16 * rt + l16][koff]);
+          const bf16x8 fdu = *reinterpret_cast<const bf16x8*>(&sdU[16 * rt + l16][koff]);
+          const bf16x8 fu = *reinterpret_cast<const bf16x8*>(&sU[16 * rt + l16][koff]);
+          aQ[m][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fo, fs0, aQ[m][rt], 0, 0, 0);
+          aW[m][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fdu, fs0, aW[m][rt], 0, 0, 0);
+          aK[m][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fu, fds1, aK[m][rt], 0, 0, 0);
+        }
+      }
+    }
+    {
+      const bf16x8 fuj = *reinterpret_cast<const bf16x8*>(&sU[16 * wv + l16][koff]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const bf16x8 fo = *reinterpret_cast<const bf16x8*>(&sdO[16 * rt + l16][koff]);
+        aP[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fo, fuj, aP[rt], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < SP; ++p)
+    if (tid % Q4 == 0 && tid + kBT * p < DK * Q4) sdD[(tid + kBT * p) / Q4] = dd[p];
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < CPW; ++m) {
+    const int ct = wv + 4 * m;
+    if (ct >= CTN) continue;
+    const int cc = 16 * ct + l16;
+    float col = 0.f;  // sum over the rows of K^d * dK^d in this column
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + r4 + e;
+        if (row < n) col += blk[L::oKd + (long)row * DK + cc] * aK[m][rt][e];
+      }
+    col += __shfl_xor(col, 16, kWave);
+    col += __shfl_xor(col, 32, kWave);
+    const float Gn = blk[L::oG + (long)(n - 1) * DK + cc];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + r4 + e;
+        if (row >= n) continue;
+        const long i = (long)row * DK + cc;
+        const float G = blk[L::oG + i], kd = blk[L::oKd + i], qt = blk[L::oQt + i];
+        const float dq = aQ[m][rt][e], dkd = aK[m][rt][e];
+        float dG = qt * dq - kd * dkd;
+        if (row == n - 1) dG += col + blk[L::oEn + cc] * sdD[cc];
+        blk[L::odq + i] = __expf(G) * dq;
+        blk[L::odk + i] = __expf(Gn - G) * dkd;
+        blk[L::odG + i] = dG;
+        blk[L::odW + i] = -aW[m][rt][e];
+      }
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)  // dP = (dO U^T) on j <= r
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, j = 16 * wv + l16;
+      if (row < n) blk[L::odP + row * CM + j] = j <= row ? aP[rt][e] : 0.f;
+    }
+}
+
 // ---- 5. per chunk-head: through W, U' and the inverse; dv and dbeta --------
 // LDS holds X and, in a first phase, dW, dU, K~, V^; in a second phase the
 // same space holds dX and T1 = dX X^T.
@@ -1032,8 +1184,12 @@ hipError_t run_bw(const BackwardArgs& a, unsigned stages, hipStream_t st) {
   if (stages & kStReverse)
     hipLaunchKernelGGL((bw_reverse_chain_kernel<DK, DV, IO>), dim3(chains), dim3(kBT), 0, st, a);
   if (items > 0 && (stages & kStGrads)) {
-    hipLaunchKernelGGL((bw_grad_dense_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBT), 0,
-                       st, a);
+    if constexpr (std::is_same<IO, bf16>::value && DV >= 32)
+      hipLaunchKernelGGL((bw_grad_dense_bf16_kernel<DK, DV>), dim3((unsigned)items), dim3(kBT), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((bw_grad_dense_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBT), 0,
+                         st, a);
     hipLaunchKernelGGL((bw_grad_solve_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBS), 0,
                        st, a);
     hipLaunchKernelGGL((bw_grad_gram_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBP), 0,
