@@ -162,6 +162,21 @@ __device__ __forceinline__ void stage_rows(float* dst, int live, F&& ld4) {
   get_rows(b, live, ld4);
   put_rows<LD>(b, dst);
 }
+
+// put_rows into LDS rows of LD bf16 (LD a multiple of 4: 8-byte pieces),
+// each value rounded to the nearest bf16.
+template <int LD, int NT, int ROWS, int COLS>
+__device__ __forceinline__ void put_rows_bf16(const Pieces<NT, ROWS, COLS>& b, bf16* dst) {
+  using P = Pieces<NT, ROWS, COLS>;
+  static_assert(LD % 4 == 0, "8-byte rows");
+#pragma unroll
+  for (int p = 0; p < P::PER; ++p) {
+    const int i = (int)threadIdx.x + p * NT, r = i / P::Q, c = 4 * (i % P::Q);
+    if (i < P::TOT)
+      *reinterpret_cast<bf16x4*>(dst + r * LD + c) =
+          bf16x4{(bf16)b.v[p][0], (bf16)b.v[p][1], (bf16)b.v[p][2], (bf16)b.v[p][3]};
+  }
+}
 constexpr int kBP = 1024;  // threads of the per-chunk kernels with scalar loops
 
 // Decay factors e^{Gam_r - Gam_j} (j <= r) of a chunk may be formed as the
@@ -1055,6 +1070,172 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
   }
 }
 
+// The same for bf16 I/O with a third of the LDS, so that two workgroups share
+// a CU: dW and K~, then dU and V^, are held as bf16 rows (the operand
+// rounding of the forward), in two phases through one buffer; X, dX and T1
+// stay fp32. The products are the fp32 MFMAs of the kernel above on the
+// rounded values, in the same order.
+template <int DK, int DV>
+__global__ __launch_bounds__(kBS, 2) void bw_grad_solve_bf16_kernel(BackwardArgs a) {
+  using L = BwL<DK, DV>;
+  constexpr int PX = CM + 4, PW = (DK > DV ? DK : DV) + 4, RT = CM / 16, NW = kBS / kWave;
+  constexpr int XPW = RT * RT / NW;  // C x C tiles per wave
+  constexpr int PH1 = 2 * CM * PW * 2, PH2 = 2 * CM * PX * 4;  // bytes
+  __shared__ __attribute__((aligned(16))) float sX[CM][PX];
+  __shared__ __attribute__((aligned(16))) uint8_t sBuf[PH1 > PH2 ? PH1 : PH2];
+  constexpr int SY = 0, SZ = DK / 16, SM = SZ + DV / 16, NSLOT = SM + RT;
+  __shared__ float sbt[CM], sdb[NSLOT][CM];
+  bf16(*sA)[PW] = reinterpret_cast<bf16(*)[PW]>(sBuf);                   // dW, then dU
+  bf16(*sB)[PW] = reinterpret_cast<bf16(*)[PW]>(sBuf + CM * PW * 2);     // K~, then V^
+  float(*sdX)[PX] = reinterpret_cast<float(*)[PX]>(sBuf);
+  float(*sT)[PX] = reinterpret_cast<float(*)[PX]>(sBuf + CM * PX * 4);
+  const Item it = item_of(a, blockIdx.x);
+  const int n = it.n, n4 = (n + 3) & ~3;
+  float* blk = a.scratch + (long)blockIdx.x * L::n;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l16 = lane % 16, r4 = 4 * (lane / 16);
+  const bf16* v = static_cast<const bf16*>(a.v);
+  bf16* dv = static_cast<bf16*>(a.dv);
+  const long row0 = tok(a, it.b, it.t0, it.h);
+  {
+    Pieces<kBS, CM, DK> pw, pk;
+    get_rows(pw, n, [&](int r, int c) { return ld4f(blk + L::odW + r * DK + c); });
+    get_rows(pk, n, [&](int r, int c) { return ld4f(blk + L::oKt + r * DK + c); });
+    stage_rows<kBS, CM, CM, PX>(&sX[0][0], n, [&](int r, int c) { return ld4f(blk + L::oX + r * CM + c); });
+    put_rows_bf16<PW>(pw, &sA[0][0]);
+    put_rows_bf16<PW>(pk, &sB[0][0]);
+  }
+  if (tid < CM) sbt[tid] = tid < n ? a.beta[tok(a, it.b, it.t0 + tid, it.h)] : 0.f;
+  for (int i = tid; i < NSLOT * CM; i += kBS) sdb[i / CM][i % CM] = 0.f;
+  // dU and V^ for the second phase, loaded now and written to LDS after it
+  Pieces<kBS, CM, DV> pu, pv;
+  get_rows(pu, n, [&](int r, int c) { return ld4f(blk + L::odU + r * DV + c); });
+  get_rows(pv, n, [&](int r, int c) { return ld4f(v + (row0 + (long)r * a.H) * DV + c); });
+  __syncthreads();
+  // Y = X^T dW: dk^ += e^Gam beta Y, dGam += K~ beta Y, dbeta += K~ . Y
+  for (int t = wv; t < RT * (DK / 16); t += NW) {
+    const int rt = t % RT, ct = t / RT;
+    if (16 * rt >= n) continue;
+    float pk[4], pg[4], gg[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e;
+      const long o = (long)row * DK + 16 * ct + l16;
+      pk[e] = row < n ? blk[L::odk + o] : 0.f;
+      pg[e] = row < n ? blk[L::odG + o] : 0.f;
+      gg[e] = row < n ? blk[L::oG + o] : 0.f;
+    }
+    const f32x4 y = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
+                             [&](int kx, int j) { return (float)sA[kx][16 * ct + j]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, cc = 16 * ct + l16;
+      float part = 0.f;
+      if (row < n) {
+        const long o = (long)row * DK + cc;
+        const float br = sbt[row], kt = (float)sB[row][cc];
+        blk[L::odk + o] = pk[e] + __expf(gg[e]) * br * y[e];
+        blk[L::odG + o] = pg[e] + kt * br * y[e];
+        part = kt * y[e];
+      }
+      part = sum16(part);
+      if (l16 == 0 && row < n) sdb[SY + ct][row] = part;
+    }
+  }
+  // dX = (dW K~^T + dU V^^T) diag(beta), strictly lower: the dW K~^T part
+  f32x4 aX[XPW];
+#pragma unroll
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
+    aX[m] = kZero4;
+    if (16 * rt < n)
+      aX[m] = mma_tile(aX[m], DK, [&](int i, int kx) { return (float)sA[16 * rt + i][kx]; },
+                       [&](int kx, int j) { return (float)sB[16 * ct + j][kx]; });
+  }
+  __syncthreads();  // dW and K~ are dead from here
+  put_rows_bf16<PW>(pu, &sA[0][0]);
+  put_rows_bf16<PW>(pv, &sB[0][0]);
+  __syncthreads();
+  // Z = X^T dU: dv^ = beta Z, dbeta += V^ . Z
+  for (int t = wv; t < RT * (DV / 16); t += NW) {
+    const int rt = t % RT, ct = t / RT;
+    if (16 * rt >= n) continue;
+    const f32x4 z = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
+                             [&](int kx, int j) { return (float)sA[kx][16 * ct + j]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, l = 16 * ct + l16;
+      float part = 0.f;
+      if (row < n) {
+        dv[tok(a, it.b, it.t0 + row, it.h) * DV + l] = (bf16)(sbt[row] * z[e]);
+        part = (float)sB[row][l] * z[e];
+      }
+      part = sum16(part);
+      if (l16 == 0 && row < n) sdb[SZ + ct][row] = part;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < XPW; ++m) {  // + dU V^^T, then diag(beta) on the strict lower part
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
+    f32x4 acc = aX[m];
+    if (16 * rt < n)
+      acc = mma_tile(acc, DV, [&](int i, int kx) { return (float)sA[16 * rt + i][kx]; },
+                     [&](int kx, int j) { return (float)sB[16 * ct + j][kx]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, col = 16 * ct + l16;
+      acc[e] = col < row ? sbt[col] * acc[e] : 0.f;
+    }
+    aX[m] = acc;
+  }
+  __syncthreads();  // dU and V^ are dead from here
+#pragma unroll
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sdX[16 * rt + r4 + e][16 * ct + l16] = aX[m][e];
+  }
+  __syncthreads();
+  // T1 = dX X^T
+#pragma unroll
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
+    f32x4 acc = kZero4;
+    if (16 * rt < n)
+      acc = mma_tile(acc, n4, [&](int i, int kx) { return sdX[16 * rt + i][kx]; },
+                     [&](int kx, int j) { return sX[16 * ct + j][kx]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[16 * rt + r4 + e][16 * ct + l16] = acc[e];
+  }
+  __syncthreads();
+  // dM = -X^T T1 (strictly lower): dA = beta dM, dbeta += A . dM
+#pragma unroll
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
+    if (16 * rt >= n) continue;
+    const f32x4 acc = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
+                               [&](int kx, int j) { return sT[kx][16 * ct + j]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, j = 16 * ct + l16;
+      float part = 0.f;
+      if (row < n) {
+        const float dm = j < row ? -acc[e] : 0.f;
+        blk[L::odA + row * CM + j] = sbt[row] * dm;
+        part = j < row ? blk[L::oA + row * CM + j] * dm : 0.f;
+      }
+      part = sum16(part);
+      if (l16 == 0 && row < n) sdb[SM + ct][row] = part;
+    }
+  }
+  __syncthreads();
+  if (tid < n) {
+    float db = 0.f;
+    for (int sl = 0; sl < NSLOT; ++sl) db += sdb[sl][tid];
+    a.dbeta[tok(a, it.b, it.t0 + tid, it.h)] = db;
+  }
+}
+
 // ---- 6. per chunk-head: through the decayed Grams; dq, dk, dg --------------
 // Thread (channel c, row group): for each of its rows r the row-side sums
 // over j <= r and the column-side sums over r2 >= r of the pair terms, each
@@ -1190,8 +1371,12 @@ hipError_t run_bw(const BackwardArgs& a, unsigned stages, hipStream_t st) {
     else
       hipLaunchKernelGGL((bw_grad_dense_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBT), 0,
                          st, a);
-    hipLaunchKernelGGL((bw_grad_solve_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBS), 0,
-                       st, a);
+    if constexpr (std::is_same<IO, bf16>::value)
+      hipLaunchKernelGGL((bw_grad_solve_bf16_kernel<DK, DV>), dim3((unsigned)items), dim3(kBS), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((bw_grad_solve_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBS), 0,
+                         st, a);
     hipLaunchKernelGGL((bw_grad_gram_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBP), 0,
                        st, a);
   }
