@@ -299,20 +299,52 @@ __global__ __launch_bounds__(kBP) void bw_prep_kernel(BackwardArgs a) {
       sM[row][j] = 0.f;
     }
   }
+  // rows of M past the chunk's last token were not written: zeros, so that
+  // no product below meets a stale value (0 * NaN)
+  for (int i = n * CM + tid; i < CM * CM; i += kBP) sM[i / CM][i % CM] = 0.f;
   __syncthreads();
-  // X = (I + diag(beta) A)^-1, unit lower triangular, by forward
-  // substitution: waves 0-3 own 16 columns each, four lanes per column split
-  // each row's dot product (rows >= n stay zero). A row's new value is
-  // written by lane group 0 and read by the other groups of the same wave in
-  // the next row (LDS accesses of one wave complete in order).
+  // X = (I + diag(beta) A)^-1 = (I + M)^-1, unit lower triangular, by 16-row
+  // blocks (rows >= n stay zero):
+  // - each diagonal block X_ii = (I + M_ii)^-1 by forward substitution, wave
+  //   i for block i, four lanes per column splitting each row's dot product
+  //   (a row's value is written by lane group 0 and read by the other groups
+  //   of the same wave in the next row: LDS accesses of one wave complete in
+  //   order);
+  // - then the blocks below the diagonal, one block diagonal d = i - j at a
+  //   time: X_ij = -X_ii (M_ij X_jj + M_i,j+1 X_j+1,j + ... + M_i,i-1 X_i-1,j),
+  //   as 16 x 16 fp32 MFMA products, wave j for block (j + d, j).
+  static_assert(CM == 64, "four 16-row blocks");
   if (wv < 4) {
-    const int j = 16 * wv + l16, p = lane / 16;
-    for (int r = 0; r < n; ++r) {
+    const int b0 = 16 * wv, j = b0 + l16, p = lane / 16;
+    for (int r = b0; r < b0 + 16; ++r) {
       float acc = 0.f;
-      for (int m = p; m < r; m += 4) acc += sM[r][m] * sX[m][j];
+      for (int m = b0 + p; m < r; m += 4) acc += sM[r][m] * sX[m][j];
       acc += __shfl_xor(acc, 16, kWave);
       acc += __shfl_xor(acc, 32, kWave);
-      if (p == 0) sX[r][j] = r > j ? -acc : (r == j ? 1.f : 0.f);
+      if (p == 0) sX[r][j] = r >= n ? 0.f : (r > j ? -acc : (r == j ? 1.f : 0.f));
+    }
+  }
+  __shared__ float sY[3][16][17];  // the sums of the current block diagonal
+  for (int d = 1; d < 4; ++d) {
+    __syncthreads();  // the previous block diagonal (or the diagonal blocks) is in sX
+    const int jb = wv, ib = wv + d;
+    if (wv < 4 - d) {
+      f32x4 y = kZero4;
+      for (int kb = jb; kb < ib; ++kb)
+        y = mma_tile(y, 16, [&](int i, int kx) { return sM[16 * ib + i][16 * kb + kx]; },
+                     [&](int kx, int jj) { return sX[16 * kb + kx][16 * jb + jj]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sY[wv][r4 + e][l16] = y[e];
+    }
+    __syncthreads();
+    if (wv < 4 - d) {
+      const f32x4 x = mma_tile(kZero4, 16, [&](int i, int kx) { return sX[16 * ib + i][16 * ib + kx]; },
+                               [&](int kx, int jj) { return sY[wv][kx][jj]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * ib + r4 + e;
+        sX[row][16 * jb + l16] = row < n ? -x[e] : 0.f;
+      }
     }
   }
   __syncthreads();

@@ -7,8 +7,9 @@ alpha -> 0 clears the memory).
 Kinds (the workload's mild decays g = logsigmoid(N(0, 1)) elsewhere):
   g10, g40   every token and channel decays by 10 / 40 (every 16-token block
              decays past 64: the diagonal tiles are formed term by term);
-  g5         -5 per token: blocks decay by 75 over their last 15 tokens, just
-             past the factored form's limit;
+  g5, g6     -5 and -6 per token: blocks decay by 75 and 90 over their last 15
+             tokens, just past the factored form's limit (16 x -6 = -96: where a
+             factor e^{+90} of an unbounded in-block reference would overflow fp32);
   mixed      bands of -40 on half the channels, a 16-token run of -6, one
              token at -inf on one channel, one token at -1e30 on all, mild
              chunks in between (factored and explicit tiles in one call, and
@@ -43,6 +44,8 @@ def _strong(g, kind):
         g.fill_(-40.0)
     elif kind == "g5":
         g.fill_(-5.0)
+    elif kind == "g6":
+        g.fill_(-6.0)
     elif kind == "edge":
         g.fill_(-4.2)
     elif kind == "mixed":
@@ -92,7 +95,7 @@ def _prefill(inp, chunk, io, flags=0):
     return st, o
 
 
-KINDS = ["g10", "g40", "g5", "mixed", "edge"]
+KINDS = ["g10", "g40", "g5", "mixed", "edge", "g6"]
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
