@@ -353,7 +353,7 @@ kda_status check_prefill(const kda_state* stt, int32_t T, const void* q, const v
 }
 
 // The prefill itself, once the workspace is chosen: the chunked kernels,
-// then the ring advance.
+// which also advance the ring.
 kda_status run_prefill(kda_state* stt, int32_t T, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const float* conv_w, void* o,
                        int32_t chunk, void* workspace, size_t workspace_bytes, uint32_t flags,
@@ -363,11 +363,6 @@ kda_status run_prefill(kda_state* stt, int32_t T, const void* q, const void* k, 
                      d->batch, T, d->heads, d->d_k, d->d_v, chunk, flags};
   hipError_t e = kda::launch_prefill(a, io_of(d), workspace, workspace_bytes, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  if (!(flags & KDA_F_SKIP_CONV)) {
-    e = kda::launch_ring_advance(q, k, v, stt->ring, d->batch, T, d->heads, d->d_k, d->d_v,
-                                 io_of(d), stream);
-    if (e != hipSuccess) return hip_fail(e, "ring advance launch");
-  }
   return KDA_OK;
 }
 

@@ -1066,6 +1066,39 @@ __global__ __launch_bounds__(512) void prefill_chain_roles_kernel(PrefillArgs a,
         for (int e = 0; e < 4; ++e)
           Sg[(long)(16 * (sw + 4 * i) + r4 + e) * DV + 16 * ct + l16] = accS[i][ct][e];
   }
+  // The conv ring of this head's channels takes the call's last three raw
+  // tokens (older ring entries shift down when the call has fewer than three),
+  // written by the launch that holds the last chunk, its column blocks
+  // splitting the head's q | k | v channels. The preparation, which reads the
+  // old ring for the first chunk's history, has finished before this launch.
+  if (!(a.flags & KDA_F_SKIP_CONV) && t0 + ncs * C >= T) {
+    constexpr int NCH = 2 * DK + DV, PER = (NCH + nblk - 1) / nblk;
+    const long ctot = (long)H * NCH;
+    MT* rb = static_cast<MT*>(a.ring) + (long)b * 3 * ctot;
+    for (int u = tid; u < PER; u += 512) {
+      const int ch = cbk * PER + u;
+      if (ch >= NCH) break;
+      const MT* x;
+      int d;
+      long c;  // ring channel
+      if (ch < DK) {
+        x = static_cast<const MT*>(a.q); d = DK; c = (long)h * DK + ch;
+      } else if (ch < 2 * DK) {
+        x = static_cast<const MT*>(a.k); d = DK; c = (long)H * DK + (long)h * DK + (ch - DK);
+      } else {
+        x = static_cast<const MT*>(a.v); d = DV; c = 2L * H * DK + (long)h * DV + (ch - 2 * DK);
+      }
+      const int hc = ch < 2 * DK ? (ch % DK) : ch - 2 * DK;
+      MT nw[3];
+#pragma unroll
+      for (int tap = 0; tap < 3; ++tap) {
+        const int s = T - 3 + tap;
+        nw[tap] = s >= 0 ? x[(((long)b * T + s) * H + h) * d + hc] : rb[(long)(3 + s) * ctot + c];
+      }
+#pragma unroll
+      for (int tap = 0; tap < 3; ++tap) rb[(long)tap * ctot + c] = nw[tap];
+    }
+  }
 }
 
 template <int C, int DK, int DV, typename IO, class M>
@@ -1107,6 +1140,11 @@ hipError_t run(const PrefillArgs& a, uint8_t* ws, size_t ws_bytes, hipStream_t s
                          (const uint8_t*)ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // the roles chain advances the ring in its last launch; otherwise a kernel of its own
+  constexpr bool ring_in_chain = sizeof(IO) == 2 && C == 64 && DK % 64 == 0 && DV % 64 == 0;
+  if (!ring_in_chain && !(a.flags & KDA_F_SKIP_CONV))
+    return launch_ring_advance(a.q, a.k, a.v, a.ring, a.B, a.T, a.H, a.dk, a.dv,
+                               sizeof(IO) == 2 ? KDA_BF16 : KDA_F32, st);
   return hipSuccess;
 }
 
