@@ -340,3 +340,26 @@ def test_prologue_backward_validation():
     bad = kda.make_dims(1, 1, 24, 32, kda.KDA_F32)
     assert L.kda_prologue_backward(ctypes.byref(bad), 8, *[_vp(FAKE)] * 14, need, 0, None) == \
         K.KDA_ERR_UNSUPPORTED
+
+
+def test_backward_workspace_sizes():
+    """The one-pass size is per chunk and head; the least size the call
+    accepts takes chunk ranges with kept states and is far smaller at a
+    training layer's length (16 x 32768 tokens, 96 heads of 128 x 128)."""
+    d = kda.make_dims(16, 96, 128, 128, kda.KDA_BF16)
+    full = kda.kda_backward_workspace_bytes(d, 32768, 64)
+    least = kda.kda_backward_workspace_min_bytes(d, 32768, 64)
+    assert full > 400e9 and 10e9 < least < 16e9
+    state = 16 * 96 * 128 * 128 * 4
+    per_chunk = full // 512
+    # the least is the best range length: L chunks' blocks + one state per range
+    best = min(L * per_chunk + -(-512 // L) * state for L in range(1, 512))
+    assert least == min(best, full)
+    # small cases: one chunk needs no kept state, T = 0 nothing
+    d1 = kda.make_dims(1, 2, 32, 32, kda.KDA_F32)
+    assert kda.kda_backward_workspace_min_bytes(d1, 64, 64) == kda.kda_backward_workspace_bytes(d1, 64, 64)
+    assert kda.kda_backward_workspace_min_bytes(d1, 0, 64) == 0
+    # invalid arguments give 0
+    assert kda.kda_backward_workspace_min_bytes(d1, -1, 64) == 0
+    assert kda.kda_backward_workspace_min_bytes(d1, 64, 48) == 0
+    assert kda.kda_backward_workspace_min_bytes(kda.make_dims(1, 2, 24, 32, kda.KDA_F32), 64, 64) == 0
