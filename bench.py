@@ -483,7 +483,19 @@ def backward_bench(kda, workloads, torch, dev, args):
     del ws, out, pws, pout, qh, kh, vh, g, beta, S0, dO, dST, q, k, v
     torch.cuda.empty_cache()
     if not args.no_backward_layer:
-        res["layer_16x32768"] = backward_layer_bench(kda, workloads, torch, dev, args)
+        # about 150 GB of inputs and outputs plus the 24 GiB workspace: run it
+        # only where the device has the room, and never lose the line to it
+        free, _ = torch.cuda.mem_get_info(dev)
+        need = 16 * 32768 * 96 * (128 * 2 * 2 + 128 * 2 + 128 * 4 + 4) * 2 + (24 << 30)
+        if free < need + (8 << 30):
+            res["layer_16x32768"] = {"skipped": f"needs about {need >> 30} GiB of device memory, "
+                                                f"{free >> 30} GiB free"}
+        else:
+            try:
+                res["layer_16x32768"] = backward_layer_bench(kda, workloads, torch, dev, args)
+            except torch.cuda.OutOfMemoryError as e:
+                torch.cuda.empty_cache()
+                res["layer_16x32768"] = {"skipped": f"out of device memory: {e}"[:300]}
     return res
 
 
