@@ -119,8 +119,8 @@ def backward_bytes(B, T, H, dk, dv, io_bytes=2):
     return B * T * H * per_tok + 3 * B * H * dk * dv * 4
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_h96_d128_bf16_traffic.json")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_t4096_h96_d128_bf16_traffic.json")
 CSRC = "gated_delta_rule_83_amd/csrc/"
 # (file, first marker, last marker): the digest covers only the text the
 # kernel is built from; None markers = the whole file
@@ -180,12 +180,12 @@ def counter_means(csv_path, counter):
 
 
 def record_traffic(fetch_csv, write_csv, command):
-    """Writes profiles/decode_traffic.json and profiles/prefill_traffic.json
+    """Writes profiles/decode_b64_h96_d128_bf16_traffic.json and profiles/prefill_t4096_h96_d128_bf16_traffic.json
     from the FETCH_SIZE and WRITE_SIZE counter runs of this benchmark
     (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, each over
     `python bench.py ... --no-stack --no-gdn --no-backward`). The counters
-    are scaled by what they read for kda_stream_rmw over 1 GiB in the same
-    runs (1 GiB read, 1 GiB written per dispatch)."""
+    are scaled by what they read for kda_stream_rmw over 6 GiB in the same
+    runs (the stream-ceiling leg: 6 GiB read, 6 GiB written per dispatch)."""
     fetch, write = counter_means(fetch_csv, "FETCH_SIZE"), counter_means(write_csv, "WRITE_SIZE")
 
     def pick(table, *parts, grid=None):
@@ -195,11 +195,12 @@ def record_traffic(fetch_csv, write_csv, command):
             raise SystemExit(f"expected one kernel matching {parts}, found {[n for n, _ in hits]}")
         return hits[0]
 
-    gib_kib = float(1 << 20)
-    fscale = gib_kib / pick(fetch, "stream_rmw_kernel")[1][0]
-    wscale = gib_kib / pick(write, "stream_rmw_kernel")[1][0]
-    common = {"scale": "FETCH_SIZE x %.4f, WRITE_SIZE x %.4f (kda_stream_rmw over 1 GiB: "
-                       "1 GiB read and 1 GiB written per dispatch)" % (fscale, wscale),
+    calib_bytes = 6 << 30  # one stream_rmw_kernel thread per 8 x 16 bytes
+    calib_kib, calib_grid = float(calib_bytes >> 10), calib_bytes // (16 * 8)
+    fscale = calib_kib / pick(fetch, "stream_rmw_kernel", grid=calib_grid)[1][0]
+    wscale = calib_kib / pick(write, "stream_rmw_kernel", grid=calib_grid)[1][0]
+    common = {"scale": "FETCH_SIZE x %.4f, WRITE_SIZE x %.4f (kda_stream_rmw over 6 GiB: "
+                       "6 GiB read and 6 GiB written per dispatch)" % (fscale, wscale),
               "fetch_scale": fscale, "write_scale": wscale, "command": command}
 
     def traffic(parts, grid):
@@ -226,6 +227,8 @@ def record_traffic(fetch_csv, write_csv, command):
              64 * 96 * 256),
             ("chain", ("prefill_chain_roles_kernel",), 2 * 96 * 512),
             ("ring_advance", ("ring_advance_kernel", "DF16b"), None)):
+        if label == "ring_advance" and not any(all(p in n for p in parts) for n, _ in fetch):
+            continue  # the bf16 chain advances the ring itself
         name, n, f_kib, w_kib, tb = traffic(parts, grid)
         per_kernel[label] = {"kernel": name, "dispatches": n, "fetch_kib_per_dispatch": f_kib,
                              "write_kib_per_dispatch": w_kib, "traffic_bytes": tb}
