@@ -23,7 +23,12 @@ namespace kda {
 namespace {
 
 constexpr int kSeg = 32;       // tokens per workgroup
-constexpr int kPBT = 256;      // threads per workgroup
+// threads per workgroup: eight waves, four workgroups per CU (37 KB of LDS
+// each). Measured on MI355X for the 4096-token, 96-head workload: 504 us,
+// against 570 with 256 threads and 531 with 1024 (the results are the same
+// bit for bit: each token's and channel's arithmetic stays in one wave or
+// thread, in the same order).
+constexpr int kPBT = 512;
 constexpr int kHalo = 3;       // conv history
 
 __device__ __forceinline__ f32x4 ld4x(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
