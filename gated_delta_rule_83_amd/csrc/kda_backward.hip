@@ -404,16 +404,21 @@ constexpr int bw_dvb() {
 // 557 with 32 and 793 with 64; the reverse chain 1007 us with 32 against
 // 1207 with 16 and 1632 with 64.
 constexpr int kStateChainW = 16, kReverseChainW = 32;
+// threads of the reverse chain's workgroups: sixteen waves, one state tile
+// each, so a chunk's latency-bound step is short (measured at T = 4096, 96
+// heads of 128 x 128: 851 us against 946 with eight waves and 1008 with four;
+// the results are the same bit for bit)
+constexpr int kRevNT = 1024;
 
 // Tiling of a chain: a workgroup holds a DK x DVB block of the state (or of
 // its gradient) as 16 x 16 MFMA accumulators, tile t = w + 4 m of wave w; the
 // token-row blocks (U, dU, dO) are CM x DVB.
-template <int DK, int DV, int W>
+template <int DK, int DV, int W, int NW = 4>
 struct ChainTiles {
   static constexpr int DVB = bw_dvb<DV, W>(), NB = DV / DVB, NCT = DVB / 16;
   static constexpr int SPB = DVB + 4, SPO = (DK > CM ? DK : CM) + 4;
-  static constexpr int NST = (DK / 16) * NCT, SPW = (NST + 3) / 4;
-  static constexpr int NUT = (CM / 16) * NCT, UPW = (NUT + 3) / 4;
+  static constexpr int NST = (DK / 16) * NCT, SPW = (NST + NW - 1) / NW;
+  static constexpr int NUT = (CM / 16) * NCT, UPW = (NUT + NW - 1) / NW;
 };
 
 // Workgroup L -> (column block cbk, sequence-head bh). Workgroups are dealt
@@ -551,9 +556,10 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
 // Same grid and tiling as the state chain, chunks from the last to the
 // first; one staging buffer holds P, K^d, Q~ and W in turn.
 template <int DK, int DV, typename IO>
-__global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kRevNT) void bw_reverse_chain_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  using CT = ChainTiles<DK, DV, kReverseChainW>;
+  constexpr int NW = kRevNT / kWave;
+  using CT = ChainTiles<DK, DV, kReverseChainW, NW>;
   constexpr int NCT = CT::NCT, SPW = CT::SPW, UPW = CT::UPW, NST = CT::NST, NUT = CT::NUT;
   constexpr int DVB = CT::DVB;
   __shared__ float sdS[DK][CT::SPB];
@@ -571,7 +577,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
   f32x4 accS[SPW];
 #pragma unroll
   for (int m = 0; m < SPW; ++m) {
-    const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+    const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       accS[m][e] = (t < NST && a.dST)
@@ -585,10 +591,10 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
   // past the last token are zero as stored).
   auto blk_of = [&](int c) { return a.scratch + ((long)(c - c0) * BH + bh) * L::n; };
   auto n_of = [&](int c) { return min(a.chunk, a.T - c * a.chunk); };
-  Pieces<kBT, CM, CM> pp;
-  Pieces<kBT, CM, DVB> pd;
-  Pieces<kBT, 1, DK> pe;
-  Pieces<kBT, CM, DK> pk;
+  Pieces<kRevNT, CM, CM> pp;
+  Pieces<kRevNT, CM, DVB> pd;
+  Pieces<kRevNT, 1, DK> pe;
+  Pieces<kRevNT, CM, DK> pk;
   auto get_first = [&](int c) {  // P, dO, e^{Gam_n} of chunk c
     const float* bc = blk_of(c);
     const int nn = n_of(c);
@@ -608,7 +614,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
     __syncthreads();  // the previous chunk is done with every buffer
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       if (t < NST) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -626,7 +632,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
     f32x4 accU[UPW];
 #pragma unroll
     for (int m = 0; m < UPW; ++m) {  // P^T dO
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       accU[m] = kZero4;
       if (t < NUT)
         accU[m] = mma_tile(kZero4, n4, [&](int i, int kx) { return sO[kx][16 * rt + i]; },
@@ -638,7 +644,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < UPW; ++m) {  // + K^d dS
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       if (t < NUT) {
         accU[m] = mma_tile(accU[m], DK, [&](int i, int kx) { return sO[16 * rt + i][kx]; },
                            [&](int kx, int j) { return sdS[kx][16 * ct + j]; });
@@ -657,7 +663,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {  // dS = Diag(e^{Gam_n}) dS + Q~^T dO
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       if (t < NST) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) accS[m][e] *= sEn[16 * rt + r4 + e];
@@ -671,7 +677,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {  // - W^T dU
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       if (t < NST)
         accS[m] = mma_tile(accS[m], n4, [&](int i, int kx) { return -sO[kx][16 * rt + i]; },
                            [&](int kx, int j) { return sdU[kx][16 * ct + j]; });
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(kBT) void bw_reverse_chain_kernel(BackwardArgs a) {
   if (a.dS0) {
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       if (t < NST) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -1401,7 +1407,8 @@ hipError_t run_bw(const BackwardArgs& a, unsigned stages, hipStream_t st) {
   if (items > 0 && (stages & kStState))
     hipLaunchKernelGGL((bw_state_chain_kernel<DK, DV>), dim3(chains_s), dim3(kBT), 0, st, a);
   if (stages & kStReverse)
-    hipLaunchKernelGGL((bw_reverse_chain_kernel<DK, DV, IO>), dim3(chains_r), dim3(kBT), 0, st, a);
+    hipLaunchKernelGGL((bw_reverse_chain_kernel<DK, DV, IO>), dim3(chains_r), dim3(kRevNT), 0, st,
+                       a);
   if (items > 0 && (stages & kStGrads)) {
     if constexpr (std::is_same<IO, bf16>::value && DV >= 32)
       hipLaunchKernelGGL((bw_grad_dense_bf16_kernel<DK, DV>), dim3((unsigned)items), dim3(kBT), 0,
