@@ -409,6 +409,11 @@ constexpr int kStateChainW = 16, kReverseChainW = 32;
 // heads of 128 x 128: 851 us against 946 with eight waves and 1008 with four;
 // the results are the same bit for bit)
 constexpr int kRevNT = 1024;
+// threads of the state chain's workgroups: four waves (measured at T = 4096,
+// 96 heads of 128 x 128: 509 us against 600 with eight waves and 587 with
+// sixteen; a 16-column block holds only eight 16 x 16 state tiles, so more
+// waves sit idle for most of a step and only add to its barriers' cost)
+constexpr int kStateNT = 256;
 
 // Tiling of a chain: a workgroup holds a DK x DVB block of the state (or of
 // its gradient) as 16 x 16 MFMA accumulators, tile t = w + 4 m of wave w; the
@@ -440,9 +445,10 @@ __device__ __forceinline__ void chain_map(int L, int NB, int BH, int& cbk, int& 
 // One workgroup per (16-column block, head, sequence). Per chunk: keep S,
 // U = U' - W S (over U' in the scratch), S = Diag(e^{Gam_n}) S + K^d^T U.
 template <int DK, int DV>
-__global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kStateNT) void bw_state_chain_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
-  using CT = ChainTiles<DK, DV, kStateChainW>;
+  constexpr int NW = kStateNT / kWave;
+  using CT = ChainTiles<DK, DV, kStateChainW, NW>;
   constexpr int NCT = CT::NCT, SPW = CT::SPW, UPW = CT::UPW, NST = CT::NST, NUT = CT::NUT;
   __shared__ float sS[DK][CT::SPB];
   __shared__ float sU[CM][CT::SPB];
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
   f32x4 accS[SPW];
 #pragma unroll
   for (int m = 0; m < SPW; ++m) {
-    const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+    const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       accS[m][e] = (t < NST && a.S0)
@@ -467,8 +473,8 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
   // operands of a chunk: W, then K^d (through one register set), e^{Gam_n}
   auto blk_of = [&](int c) { return a.scratch + ((long)(c - c0) * BH + bh) * L::n; };
   auto n_of = [&](int c) { return min(a.chunk, a.T - c * a.chunk); };
-  Pieces<kBT, CM, DK> pk;
-  Pieces<kBT, 1, DK> pe;
+  Pieces<kStateNT, CM, DK> pk;
+  Pieces<kStateNT, 1, DK> pe;
   if (c0 < c1) {
     const float* b0 = blk_of(c0);
     get_rows(pk, n_of(c0), [&](int r, int cx) { return ld4f(b0 + L::oW + r * DK + cx); });
@@ -481,7 +487,7 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
     __syncthreads();  // the previous chunk is done with sS, sU, sO, sEn
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       if (t < NST) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -497,7 +503,7 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
     float up[UPW][4];  // U' of this thread's elements, loaded before the products
 #pragma unroll
     for (int m = 0; m < UPW; ++m) {
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * rt + r4 + e, col = 16 * ct + l16;
@@ -507,7 +513,7 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < UPW; ++m) {  // U = U' - W S
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       if (t < NUT) {
         const f32x4 ws = mma_tile(kZero4, DK, [&](int i, int kx) { return sO[16 * rt + i][kx]; },
                                   [&](int kx, int j) { return sS[kx][16 * ct + j]; });
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {  // S = Diag(e^{Gam_n}) S + K^d^T U
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       if (t < NST) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) accS[m][e] *= sEn[16 * rt + r4 + e];
@@ -542,7 +548,7 @@ __global__ __launch_bounds__(kBT) void bw_state_chain_kernel(BackwardArgs a) {
   if (a.S_out) {  // the state leaving chunk c1 - 1: where the next chunk range starts
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
-      const int t = wv + 4 * m, rt = t / NCT, ct = t % NCT;
+      const int t = wv + NW * m, rt = t / NCT, ct = t % NCT;
       if (t < NST) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -1405,7 +1411,7 @@ hipError_t run_bw(const BackwardArgs& a, unsigned stages, hipStream_t st) {
   if (items > 0 && (stages & kStPrep))
     hipLaunchKernelGGL((bw_prep_kernel<DK, DV, IO>), dim3((unsigned)items), dim3(kBP), 0, st, a);
   if (items > 0 && (stages & kStState))
-    hipLaunchKernelGGL((bw_state_chain_kernel<DK, DV>), dim3(chains_s), dim3(kBT), 0, st, a);
+    hipLaunchKernelGGL((bw_state_chain_kernel<DK, DV>), dim3(chains_s), dim3(kStateNT), 0, st, a);
   if (stages & kStReverse)
     hipLaunchKernelGGL((bw_reverse_chain_kernel<DK, DV, IO>), dim3(chains_r), dim3(kRevNT), 0, st,
                        a);
