@@ -850,9 +850,10 @@ __global__ __launch_bounds__(kBT, 2) void bw_grad_dense_bf16_kernel(BackwardArgs
 #pragma unroll
   for (int p = 0; p < SP; ++p) dd[p] = 0.f;
   auto cvt = [](f32x4 v) { return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]}; };
-  for (int l0 = 0; l0 < DV; l0 += SL) {
-    // every load of the slab issued before the first LDS store
-    f32x4 vs[SP], vd[SP], vo[TP], vdu[TP], vu[TP];
+  // A slab's S0 and dS1 pieces are loaded as soon as the previous slab is in
+  // LDS, so they are in flight during that slab's products.
+  f32x4 vs[SP], vd[SP];
+  auto load_state = [&](int l0) {
 #pragma unroll
     for (int p = 0; p < SP; ++p) {
       const int idx = tid + kBT * p, r = idx / Q4, c = 4 * (idx % Q4);
@@ -860,6 +861,10 @@ __global__ __launch_bounds__(kBT, 2) void bw_grad_dense_bf16_kernel(BackwardArgs
       vs[p] = live ? ld4f(S0 + (long)r * DV + l0 + c) : kZero4;
       vd[p] = live ? ld4f(dS1 + (long)r * DV + l0 + c) : kZero4;
     }
+  };
+  load_state(0);
+  for (int l0 = 0; l0 < DV; l0 += SL) {
+    f32x4 vo[TP], vdu[TP], vu[TP];
 #pragma unroll
     for (int p = 0; p < TP; ++p) {
       const int idx = tid + kBT * p, r = idx / Q4, c = 4 * (idx % Q4);
@@ -892,6 +897,7 @@ __global__ __launch_bounds__(kBT, 2) void bw_grad_dense_bf16_kernel(BackwardArgs
       }
     }
     __syncthreads();
+    if (l0 + SL < DV) load_state(l0 + SL);
 #pragma unroll
     for (int m = 0; m < CPW; ++m) {
       const int ct = wv + 4 * m;
