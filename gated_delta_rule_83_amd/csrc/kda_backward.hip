@@ -1398,11 +1398,18 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
   }
   __syncthreads();
   if (tid < DK) {  // dg = reverse in-chunk prefix sum of dGam
+    // every load of the column issued before the first store of dg (which the
+    // compiler cannot tell apart from the scratch), so they are in flight together
+    float v[CM];
+#pragma unroll
+    for (int r = 0; r < CM; ++r) v[r] = r < n ? blk[L::odG + (long)r * DK + tid] : 0.f;
     float s = 0.f;
-    for (int r = n - 1; r >= 0; --r) {
-      s += blk[L::odG + (long)r * DK + tid];
-      a.dg[tok(a, it.b, it.t0 + r, it.h) * DK + tid] = s;
-    }
+#pragma unroll
+    for (int r = CM - 1; r >= 0; --r)
+      if (r < n) {
+        s += v[r];
+        a.dg[tok(a, it.b, it.t0 + r, it.h) * DK + tid] = s;
+      }
   }
 }
 
