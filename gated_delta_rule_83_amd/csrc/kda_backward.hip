@@ -1301,7 +1301,12 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
   using L = BwL<DK, DV>;
   constexpr int PK = DK + 4, PC = CM + 4, RG = kBP / (DK / 2);
   __shared__ __attribute__((aligned(16))) float sK[CM][PK], sQ[CM][PK], sG[CM][PK];
-  __shared__ __attribute__((aligned(16))) float sdA[CM][PC], sdP[CM][PC];
+  // dA and dP, and once the products are done with them, the total dGam
+  __shared__ __attribute__((aligned(16))) float sdAP[2 * CM * PC];
+  static_assert(CM * PK <= 2 * CM * PC, "dGam fits where dA and dP were");
+  float(*sdA)[PC] = reinterpret_cast<float(*)[PC]>(sdAP);
+  float(*sdP)[PC] = reinterpret_cast<float(*)[PC]>(sdAP + CM * PC);
+  float(*sdG)[PK] = reinterpret_cast<float(*)[PK]>(sdAP);
   const Item it = item_of(a, blockIdx.x);
   const int n = it.n;
   float* blk = a.scratch + (long)blockIdx.x * L::n;
@@ -1329,10 +1334,13 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
     // tiles, the exponentials formed per operand element.
     const int lane = tid % kWave, wv = tid / kWave, l16 = lane % 16, r4 = 4 * (lane / 16);
     const int n4 = (n + 3) & ~3;
-    constexpr int NW = kBP / kWave, NT16 = (CM / 16) * (DK / 16);
-    for (int t = wv; t < NT16; t += NW) {
-      const int rt = t / (DK / 16), ct = t % (DK / 16);
-      if (16 * rt >= n) continue;
+    constexpr int NW = kBP / kWave, NT16 = (CM / 16) * (DK / 16), TPW = (NT16 + NW - 1) / NW;
+    f32x4 rsv[TPW], rpv[TPW], ctv[TPW];
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int t = wv + NW * m, rt = t / (DK / 16), ct = t % (DK / 16);
+      rsv[m] = rpv[m] = ctv[m] = kZero4;
+      if (t >= NT16 || 16 * rt >= n) continue;
       const int cb = 16 * ct;
       auto kminus = [&](int kx, int j) { return sK[kx][cb + j] * __expf(-sG[kx][cb + j]); };
       const f32x4 rs = mma_tile(kZero4, n4, [&](int i, int kx) { return sdA[16 * rt + i][kx]; },
@@ -1343,6 +1351,17 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
                            [&](int kx, int j) { return sK[kx][cb + j] * __expf(sG[kx][cb + j]); });
       ct4 = mma_tile(ct4, n4, [&](int i, int kx) { return sdP[kx][16 * rt + i]; },
                      [&](int kx, int j) { return sQ[kx][cb + j] * __expf(sG[kx][cb + j]); });
+      rsv[m] = rs;
+      rpv[m] = rp;
+      ctv[m] = ct4;
+    }
+    __syncthreads();  // dA and dP are dead from here
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int t = wv + NW * m, rt = t / (DK / 16), ct = t % (DK / 16);
+      if (t >= NT16 || 16 * rt >= n) continue;
+      const int cb = 16 * ct;
+      const f32x4 rs = rsv[m], rp = rpv[m], ct4 = ctv[m];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + r4 + e, c = cb + l16;
@@ -1354,13 +1373,18 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
         const long o = tok(a, it.b, it.t0 + r, it.h) * DK + c;
         dq[o] = from_f32<IO>(blk[L::odq + i] + SP);
         dk[o] = from_f32<IO>(blk[L::odk + i] + SA + TT);
-        blk[L::odG + i] += kr * SA + qr * SP - kr * TT;
+        sdG[r][c] = blk[L::odG + i] + (kr * SA + qr * SP - kr * TT);
       }
     }
   } else {
   // two channels per thread (8-byte LDS reads); rows r0, r0 + RG, ...
+  constexpr int RPT = (CM + RG - 1) / RG;  // rows per thread
   const int c0 = 2 * (tid % (DK / 2));
-  for (int r = tid / (DK / 2); r < n; r += RG) {
+  f32x2 SAv[RPT], SPv[RPT], TTv[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int r = tid / (DK / 2) + RG * m;
+    if (r >= n) continue;
     const f32x2 Gr = *reinterpret_cast<const f32x2*>(&sG[r][c0]);
     const f32x2 kr = *reinterpret_cast<const f32x2*>(&sK[r][c0]);
     const f32x2 qr = *reinterpret_cast<const f32x2*>(&sQ[r][c0]);
@@ -1386,30 +1410,35 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) TT[e] += (da * k2[e] + dp * q2[e]) * __expf(g2[e] - Gr[e]);
     }
+    SAv[m] = SA;
+    SPv[m] = SP;
+    TTv[m] = TT;
+  }
+  __syncthreads();  // dA and dP are dead from here
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int r = tid / (DK / 2) + RG * m;
+    if (r >= n) continue;
+    const f32x2 kr = *reinterpret_cast<const f32x2*>(&sK[r][c0]);
+    const f32x2 qr = *reinterpret_cast<const f32x2*>(&sQ[r][c0]);
+    const f32x2 SA = SAv[m], SP = SPv[m], TT = TTv[m];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const long i = (long)r * DK + c0 + e;
       const long o = tok(a, it.b, it.t0 + r, it.h) * DK + c0 + e;
       dq[o] = from_f32<IO>(blk[L::odq + i] + SP[e]);
       dk[o] = from_f32<IO>(blk[L::odk + i] + SA[e] + TT[e]);
-      blk[L::odG + i] += kr[e] * SA[e] + qr[e] * SP[e] - kr[e] * TT[e];
+      sdG[r][c0 + e] = blk[L::odG + i] + (kr[e] * SA[e] + qr[e] * SP[e] - kr[e] * TT[e]);
     }
   }
   }
   __syncthreads();
   if (tid < DK) {  // dg = reverse in-chunk prefix sum of dGam
-    // every load of the column issued before the first store of dg (which the
-    // compiler cannot tell apart from the scratch), so they are in flight together
-    float v[CM];
-#pragma unroll
-    for (int r = 0; r < CM; ++r) v[r] = r < n ? blk[L::odG + (long)r * DK + tid] : 0.f;
     float s = 0.f;
-#pragma unroll
-    for (int r = CM - 1; r >= 0; --r)
-      if (r < n) {
-        s += v[r];
-        a.dg[tok(a, it.b, it.t0 + r, it.h) * DK + tid] = s;
-      }
+    for (int r = n - 1; r >= 0; --r) {
+      s += sdG[r][tid];
+      a.dg[tok(a, it.b, it.t0 + r, it.h) * DK + tid] = s;
+    }
   }
 }
 
