@@ -933,17 +933,30 @@ __global__ __launch_bounds__(kBT, 2) void bw_grad_dense_bf16_kernel(BackwardArgs
     const int ct = wv + 4 * m;
     if (ct >= CTN) continue;
     const int cc = 16 * ct + l16;
+    // the tile's operands loaded before its first store, all in flight together
+    float vG[RT][4], vkd[RT][4], vqt[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + r4 + e;
+        const long i = (long)row * DK + cc;
+        vG[rt][e] = row < n ? blk[L::oG + i] : 0.f;
+        vkd[rt][e] = row < n ? blk[L::oKd + i] : 0.f;
+        vqt[rt][e] = row < n ? blk[L::oQt + i] : 0.f;
+      }
+    const float Gn = blk[L::oG + (long)(n - 1) * DK + cc];
+    const float En = blk[L::oEn + cc];
     float col = 0.f;  // sum over the rows of K^d * dK^d in this column
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * rt + r4 + e;
-        if (row < n) col += blk[L::oKd + (long)row * DK + cc] * aK[m][rt][e];
+        if (row < n) col += vkd[rt][e] * aK[m][rt][e];
       }
     col += __shfl_xor(col, 16, kWave);
     col += __shfl_xor(col, 32, kWave);
-    const float Gn = blk[L::oG + (long)(n - 1) * DK + cc];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -951,10 +964,10 @@ __global__ __launch_bounds__(kBT, 2) void bw_grad_dense_bf16_kernel(BackwardArgs
         const int row = 16 * rt + r4 + e;
         if (row >= n) continue;
         const long i = (long)row * DK + cc;
-        const float G = blk[L::oG + i], kd = blk[L::oKd + i], qt = blk[L::oQt + i];
+        const float G = vG[rt][e], kd = vkd[rt][e], qt = vqt[rt][e];
         const float dq = aQ[m][rt][e], dkd = aK[m][rt][e];
         float dG = qt * dq - kd * dkd;
-        if (row == n - 1) dG += col + blk[L::oEn + cc] * sdD[cc];
+        if (row == n - 1) dG += col + En * sdD[cc];
         blk[L::odq + i] = __expf(G) * dq;
         blk[L::odk + i] = __expf(Gn - G) * dkd;
         blk[L::odG + i] = dG;
@@ -1355,6 +1368,21 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
       rpv[m] = rp;
       ctv[m] = ct4;
     }
+    // the dense parts of dq, dk and dGam loaded before the first store
+    float vq[TPW][4], vk[TPW][4], vg[TPW][4];
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int t = wv + NW * m, rt = t / (DK / 16), ct = t % (DK / 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + r4 + e;
+        const bool live = t < NT16 && r < n;
+        const long i = (long)r * DK + 16 * ct + l16;
+        vq[m][e] = live ? blk[L::odq + i] : 0.f;
+        vk[m][e] = live ? blk[L::odk + i] : 0.f;
+        vg[m][e] = live ? blk[L::odG + i] : 0.f;
+      }
+    }
     __syncthreads();  // dA and dP are dead from here
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
@@ -1369,11 +1397,10 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
         const float G = sG[r][c], eg = __expf(G);
         const float SA = eg * rs[e], SP = eg * rp[e], TT = ct4[e] * __expf(-G);
         const float kr = sK[r][c], qr = sQ[r][c];
-        const long i = (long)r * DK + c;
         const long o = tok(a, it.b, it.t0 + r, it.h) * DK + c;
-        dq[o] = from_f32<IO>(blk[L::odq + i] + SP);
-        dk[o] = from_f32<IO>(blk[L::odk + i] + SA + TT);
-        sdG[r][c] = blk[L::odG + i] + (kr * SA + qr * SP - kr * TT);
+        dq[o] = from_f32<IO>(vq[m][e] + SP);
+        dk[o] = from_f32<IO>(vk[m][e] + SA + TT);
+        sdG[r][c] = vg[m][e] + (kr * SA + qr * SP - kr * TT);
       }
     }
   } else {
