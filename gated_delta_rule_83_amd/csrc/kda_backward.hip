@@ -775,17 +775,30 @@ __global__ __launch_bounds__(kBT, 2) void bw_grad_dense_kernel(BackwardArgs a) {
     const int ct = wv + 4 * m;
     if (ct >= CTN) continue;
     const int cc = 16 * ct + l16;
+    // the tile's operands loaded before its first store, all in flight together
+    float vG[RT][4], vkd[RT][4], vqt[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + r4 + e;
+        const long i = (long)row * DK + cc;
+        vG[rt][e] = row < n ? blk[L::oG + i] : 0.f;
+        vkd[rt][e] = row < n ? blk[L::oKd + i] : 0.f;
+        vqt[rt][e] = row < n ? blk[L::oQt + i] : 0.f;
+      }
+    const float Gn = blk[L::oG + (long)(n - 1) * DK + cc];
+    const float En = blk[L::oEn + cc];
     float col = 0.f;  // sum over the rows of K^d * dK^d in this column
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * rt + r4 + e;
-        if (row < n) col += blk[L::oKd + (long)row * DK + cc] * aK[m][rt][e];
+        if (row < n) col += vkd[rt][e] * aK[m][rt][e];
       }
     col += __shfl_xor(col, 16, kWave);
     col += __shfl_xor(col, 32, kWave);
-    const float Gn = blk[L::oG + (long)(n - 1) * DK + cc];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -793,10 +806,10 @@ __global__ __launch_bounds__(kBT, 2) void bw_grad_dense_kernel(BackwardArgs a) {
         const int row = 16 * rt + r4 + e;
         if (row >= n) continue;
         const long i = (long)row * DK + cc;
-        const float G = blk[L::oG + i], kd = blk[L::oKd + i], qt = blk[L::oQt + i];
+        const float G = vG[rt][e], kd = vkd[rt][e], qt = vqt[rt][e];
         const float dq = aQ[m][rt][e], dkd = aK[m][rt][e];
         float dG = qt * dq - kd * dkd;
-        if (row == n - 1) dG += col + blk[L::oEn + cc] * sdD[cc];
+        if (row == n - 1) dG += col + En * sdD[cc];
         blk[L::odq + i] = __expf(G) * dq;
         blk[L::odk + i] = __expf(Gn - G) * dkd;
         blk[L::odG + i] = dG;
@@ -1099,6 +1112,17 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
     for (int e = 0; e < 4; ++e) sdX[16 * rt + r4 + e][16 * ct + l16] = aX[m][e];
   }
   __syncthreads();
+  // A for dbeta below, loaded before the first store of dA
+  float vA[XPW][4];
+#pragma unroll
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, j = 16 * ct + l16;
+      vA[m][e] = row < n && j < row ? blk[L::oA + row * CM + j] : 0.f;
+    }
+  }
   // T1 = dX X^T
 #pragma unroll
   for (int m = 0; m < XPW; ++m) {
@@ -1125,7 +1149,7 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
       if (row < n) {
         const float dm = j < row ? -acc[e] : 0.f;
         blk[L::odA + row * CM + j] = sbt[row] * dm;
-        part = j < row ? blk[L::oA + row * CM + j] * dm : 0.f;
+        part = j < row ? vA[m][e] * dm : 0.f;
       }
       part = sum16(part);
       if (l16 == 0 && row < n) sdb[SM + ct][row] = part;
@@ -1265,6 +1289,17 @@ __global__ __launch_bounds__(kBS, 2) void bw_grad_solve_bf16_kernel(BackwardArgs
     for (int e = 0; e < 4; ++e) sdX[16 * rt + r4 + e][16 * ct + l16] = aX[m][e];
   }
   __syncthreads();
+  // A for dbeta below, loaded before the first store of dA
+  float vA[XPW][4];
+#pragma unroll
+  for (int m = 0; m < XPW; ++m) {
+    const int u = wv + NW * m, rt = u / RT, ct = u % RT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + r4 + e, j = 16 * ct + l16;
+      vA[m][e] = row < n && j < row ? blk[L::oA + row * CM + j] : 0.f;
+    }
+  }
   // T1 = dX X^T
 #pragma unroll
   for (int m = 0; m < XPW; ++m) {
@@ -1291,7 +1326,7 @@ __global__ __launch_bounds__(kBS, 2) void bw_grad_solve_bf16_kernel(BackwardArgs
       if (row < n) {
         const float dm = j < row ? -acc[e] : 0.f;
         blk[L::odA + row * CM + j] = sbt[row] * dm;
-        part = j < row ? blk[L::oA + row * CM + j] * dm : 0.f;
+        part = j < row ? vA[m][e] * dm : 0.f;
       }
       part = sum16(part);
       if (l16 == 0 && row < n) sdb[SM + ct][row] = part;
@@ -1441,6 +1476,16 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
     SPv[m] = SP;
     TTv[m] = TT;
   }
+  // the dense parts of dq, dk and dGam loaded before the first store
+  f32x2 vq[RPT], vk[RPT], vg[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int r = tid / (DK / 2) + RG * m;
+    const long i = (long)r * DK + c0;
+    vq[m] = r < n ? *reinterpret_cast<const f32x2*>(blk + L::odq + i) : f32x2{0.f, 0.f};
+    vk[m] = r < n ? *reinterpret_cast<const f32x2*>(blk + L::odk + i) : f32x2{0.f, 0.f};
+    vg[m] = r < n ? *reinterpret_cast<const f32x2*>(blk + L::odG + i) : f32x2{0.f, 0.f};
+  }
   __syncthreads();  // dA and dP are dead from here
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
@@ -1451,11 +1496,10 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
     const f32x2 SA = SAv[m], SP = SPv[m], TT = TTv[m];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const long i = (long)r * DK + c0 + e;
       const long o = tok(a, it.b, it.t0 + r, it.h) * DK + c0 + e;
-      dq[o] = from_f32<IO>(blk[L::odq + i] + SP[e]);
-      dk[o] = from_f32<IO>(blk[L::odk + i] + SA[e] + TT[e]);
-      sdG[r][c0 + e] = blk[L::odG + i] + (kr[e] * SA[e] + qr[e] * SP[e] - kr[e] * TT[e]);
+      dq[o] = from_f32<IO>(vq[m][e] + SP[e]);
+      dk[o] = from_f32<IO>(vk[m][e] + SA[e] + TT[e]);
+      sdG[r][c0 + e] = vg[m][e] + (kr[e] * SA[e] + qr[e] * SP[e] - kr[e] * TT[e]);
     }
   }
   }
