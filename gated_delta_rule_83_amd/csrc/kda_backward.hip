@@ -220,11 +220,20 @@ __global__ __launch_bounds__(kBP) void bw_prep_kernel(BackwardArgs a) {
   const IO* k = static_cast<const IO*>(a.k);
   const IO* v = static_cast<const IO*>(a.v);
   const long row0 = tok(a, it.b, it.t0, it.h), rs = (long)a.H;  // token row r: row0 + r * rs
-  stage_rows<kBP, CM, DK, PKV>(&sK[0][0], n, [&](int r, int c) { return ld4f(k + (row0 + r * rs) * DK + c); });
-  stage_rows<kBP, CM, DK, PK>(&sQ[0][0], n, [&](int r, int c) { return ld4f(q + (row0 + r * rs) * DK + c); });
-  stage_rows<kBP, CM, DK, PK>(&sG[0][0], n, [&](int r, int c) { return ld4f(a.g + (row0 + r * rs) * DK + c); });
+  // every input load issued before the first LDS store; V^ stays in registers
+  // until its rows of LDS are free
+  Pieces<kBP, CM, DK> pk, pq, pg;
+  Pieces<kBP, CM, DV> pv;
+  get_rows(pk, n, [&](int r, int c) { return ld4f(k + (row0 + r * rs) * DK + c); });
+  get_rows(pq, n, [&](int r, int c) { return ld4f(q + (row0 + r * rs) * DK + c); });
+  get_rows(pg, n, [&](int r, int c) { return ld4f(a.g + (row0 + r * rs) * DK + c); });
+  get_rows(pv, n, [&](int r, int c) { return ld4f(v + (row0 + r * rs) * DV + c); });
+  const float bt = tid < n ? a.beta[row0 + tid * rs] : 0.f;
   for (int i = tid; i < CM * CM; i += kBP) sX[i / CM][i % CM] = 0.f;
-  if (tid < CM) sb[tid] = tid < n ? a.beta[row0 + tid * rs] : 0.f;
+  put_rows<PKV>(pk, &sK[0][0]);
+  put_rows<PK>(pq, &sQ[0][0]);
+  put_rows<PK>(pg, &sG[0][0]);
+  if (tid < CM) sb[tid] = bt;
   __syncthreads();
   if (tid < DK) {
     float s = 0.f;
@@ -362,9 +371,14 @@ __global__ __launch_bounds__(kBP) void bw_prep_kernel(BackwardArgs a) {
   if (tid < DK) blk[L::oEn + tid] = __expf(sG[n - 1][tid]);
   __syncthreads();
   // beta V^ over the (now unused) k rows
-  stage_rows<kBP, CM, DV, PKV>(&sK[0][0], n, [&](int r, int c) {
-    return sb[r] * ld4f(v + (row0 + r * rs) * DV + c);
-  });
+  {
+    using P = Pieces<kBP, CM, DV>;
+#pragma unroll
+    for (int p = 0; p < P::PER; ++p) {
+      const int i = tid + p * kBP, r = i / P::Q, c = 4 * (i % P::Q);
+      if (i < P::TOT) *reinterpret_cast<f32x4*>(&sK[r][c]) = r < n ? sb[r] * pv.v[p] : kZero4;
+    }
+  }
   // W = X (beta K~): 16 x 16 tiles over the waves
   constexpr int TW = (CM / 16) * (DK / 16);
   for (int t = wv; t < TW; t += NW) {
@@ -1364,15 +1378,20 @@ __global__ __launch_bounds__(kBP) void bw_grad_gram_kernel(BackwardArgs a) {
   IO* dq = static_cast<IO*>(a.dq);
   IO* dk = static_cast<IO*>(a.dk);
   const long row0 = tok(a, it.b, it.t0, it.h);
-  stage_rows<kBP, CM, DK, PK>(&sK[0][0], n, [&](int r, int c) {
-    return ld4f(k + (row0 + (long)r * a.H) * DK + c);
-  });
-  stage_rows<kBP, CM, DK, PK>(&sQ[0][0], n, [&](int r, int c) {
-    return ld4f(q + (row0 + (long)r * a.H) * DK + c);
-  });
-  stage_rows<kBP, CM, DK, PK>(&sG[0][0], n, [&](int r, int c) { return ld4f(blk + L::oG + r * DK + c); });
-  stage_rows<kBP, CM, CM, PC>(&sdA[0][0], n, [&](int r, int c) { return ld4f(blk + L::odA + r * CM + c); });
-  stage_rows<kBP, CM, CM, PC>(&sdP[0][0], n, [&](int r, int c) { return ld4f(blk + L::odP + r * CM + c); });
+  {  // every load issued before the first LDS store
+    Pieces<kBP, CM, DK> pk, pq, pg;
+    Pieces<kBP, CM, CM> pa, pp;
+    get_rows(pk, n, [&](int r, int c) { return ld4f(k + (row0 + (long)r * a.H) * DK + c); });
+    get_rows(pq, n, [&](int r, int c) { return ld4f(q + (row0 + (long)r * a.H) * DK + c); });
+    get_rows(pg, n, [&](int r, int c) { return ld4f(blk + L::oG + r * DK + c); });
+    get_rows(pa, n, [&](int r, int c) { return ld4f(blk + L::odA + r * CM + c); });
+    get_rows(pp, n, [&](int r, int c) { return ld4f(blk + L::odP + r * CM + c); });
+    put_rows<PK>(pk, &sK[0][0]);
+    put_rows<PK>(pq, &sQ[0][0]);
+    put_rows<PK>(pg, &sG[0][0]);
+    put_rows<PC>(pa, &sdA[0][0]);
+    put_rows<PC>(pp, &sdP[0][0]);
+  }
   __shared__ int sflag;
   __syncthreads();
   if (chunk_factorable<kBP, DK, PK>(sG, n, &sflag)) {
