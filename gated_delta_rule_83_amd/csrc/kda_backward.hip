@@ -1050,34 +1050,50 @@ __global__ __launch_bounds__(kBS) void bw_grad_solve_kernel(BackwardArgs a) {
   for (int i = tid; i < NSLOT * CM; i += kBS) sdb[i / CM][i % CM] = 0.f;
   __syncthreads();
   // Y = X^T dW: dk^ += e^Gam beta Y, dGam += K~ beta Y, dbeta += K~ . Y
-  for (int t = wv; t < RT * (DK / 16); t += NW) {
+  // Each tile's dk^, dGam partials and Gam are loaded one tile ahead, before
+  // the stores of the tile before it.
+  constexpr int TY = RT * (DK / 16);
+  auto load_y = [&](int t, float* pk, float* pg, float* gg) {
     const int rt = t % RT, ct = t / RT;
-    if (16 * rt >= n) continue;
-    // this tile's dk^, dGam partials and Gam, loaded before the products
-    float pk[4], pg[4], gg[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * rt + r4 + e;
+      const bool live = t < TY && row < n;
       const long o = (long)row * DK + 16 * ct + l16;
-      pk[e] = row < n ? blk[L::odk + o] : 0.f;
-      pg[e] = row < n ? blk[L::odG + o] : 0.f;
-      gg[e] = row < n ? blk[L::oG + o] : 0.f;
+      pk[e] = live ? blk[L::odk + o] : 0.f;
+      pg[e] = live ? blk[L::odG + o] : 0.f;
+      gg[e] = live ? blk[L::oG + o] : 0.f;
     }
-    const f32x4 y = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
-                             [&](int kx, int j) { return sdW[kx][16 * ct + j]; });
+  };
+  float pk[4], pg[4], gg[4];
+  load_y(wv, pk, pg, gg);
+  for (int t = wv; t < TY; t += NW) {
+    const int rt = t % RT, ct = t / RT;
+    float nk[4], ng[4], ngg[4];
+    load_y(t + NW, nk, ng, ngg);
+    if (16 * rt < n) {
+      const f32x4 y = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
+                               [&](int kx, int j) { return sdW[kx][16 * ct + j]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + r4 + e, cc = 16 * ct + l16;
+        float part = 0.f;
+        if (row < n) {
+          const long o = (long)row * DK + cc;
+          const float br = sbt[row], kt = sKt[row][cc];
+          blk[L::odk + o] = pk[e] + __expf(gg[e]) * br * y[e];
+          blk[L::odG + o] = pg[e] + kt * br * y[e];
+          part = kt * y[e];
+        }
+        part = sum16(part);
+        if (l16 == 0 && row < n) sdb[SY + ct][row] = part;
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * rt + r4 + e, cc = 16 * ct + l16;
-      float part = 0.f;
-      if (row < n) {
-        const long o = (long)row * DK + cc;
-        const float br = sbt[row], kt = sKt[row][cc];
-        blk[L::odk + o] = pk[e] + __expf(gg[e]) * br * y[e];
-        blk[L::odG + o] = pg[e] + kt * br * y[e];
-        part = kt * y[e];
-      }
-      part = sum16(part);
-      if (l16 == 0 && row < n) sdb[SY + ct][row] = part;
+      pk[e] = nk[e];
+      pg[e] = ng[e];
+      gg[e] = ngg[e];
     }
   }
   // Z = X^T dU: dv^ = beta Z, dbeta += V^ . Z
@@ -1220,33 +1236,50 @@ __global__ __launch_bounds__(kBS, 2) void bw_grad_solve_bf16_kernel(BackwardArgs
   get_rows(pv, n, [&](int r, int c) { return ld4f(v + (row0 + (long)r * a.H) * DV + c); });
   __syncthreads();
   // Y = X^T dW: dk^ += e^Gam beta Y, dGam += K~ beta Y, dbeta += K~ . Y
-  for (int t = wv; t < RT * (DK / 16); t += NW) {
+  // Each tile's dk^, dGam partials and Gam are loaded one tile ahead, before
+  // the stores of the tile before it.
+  constexpr int TY = RT * (DK / 16);
+  auto load_y = [&](int t, float* pk, float* pg, float* gg) {
     const int rt = t % RT, ct = t / RT;
-    if (16 * rt >= n) continue;
-    float pk[4], pg[4], gg[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * rt + r4 + e;
+      const bool live = t < TY && row < n;
       const long o = (long)row * DK + 16 * ct + l16;
-      pk[e] = row < n ? blk[L::odk + o] : 0.f;
-      pg[e] = row < n ? blk[L::odG + o] : 0.f;
-      gg[e] = row < n ? blk[L::oG + o] : 0.f;
+      pk[e] = live ? blk[L::odk + o] : 0.f;
+      pg[e] = live ? blk[L::odG + o] : 0.f;
+      gg[e] = live ? blk[L::oG + o] : 0.f;
     }
-    const f32x4 y = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
-                             [&](int kx, int j) { return (float)sA[kx][16 * ct + j]; });
+  };
+  float pk[4], pg[4], gg[4];
+  load_y(wv, pk, pg, gg);
+  for (int t = wv; t < TY; t += NW) {
+    const int rt = t % RT, ct = t / RT;
+    float nk[4], ng[4], ngg[4];
+    load_y(t + NW, nk, ng, ngg);
+    if (16 * rt < n) {
+      const f32x4 y = mma_tile(kZero4, n4, [&](int i, int kx) { return sX[kx][16 * rt + i]; },
+                               [&](int kx, int j) { return (float)sA[kx][16 * ct + j]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + r4 + e, cc = 16 * ct + l16;
+        float part = 0.f;
+        if (row < n) {
+          const long o = (long)row * DK + cc;
+          const float br = sbt[row], kt = (float)sB[row][cc];
+          blk[L::odk + o] = pk[e] + __expf(gg[e]) * br * y[e];
+          blk[L::odG + o] = pg[e] + kt * br * y[e];
+          part = kt * y[e];
+        }
+        part = sum16(part);
+        if (l16 == 0 && row < n) sdb[SY + ct][row] = part;
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * rt + r4 + e, cc = 16 * ct + l16;
-      float part = 0.f;
-      if (row < n) {
-        const long o = (long)row * DK + cc;
-        const float br = sbt[row], kt = (float)sB[row][cc];
-        blk[L::odk + o] = pk[e] + __expf(gg[e]) * br * y[e];
-        blk[L::odG + o] = pg[e] + kt * br * y[e];
-        part = kt * y[e];
-      }
-      part = sum16(part);
-      if (l16 == 0 && row < n) sdb[SY + ct][row] = part;
+      pk[e] = nk[e];
+      pg[e] = ng[e];
+      gg[e] = ngg[e];
     }
   }
   // dX = (dW K~^T + dU V^^T) diag(beta), strictly lower: the dW K~^T part
